@@ -1,0 +1,210 @@
+"""CPU oracle for the DSA layer group under the IndexShare schedule.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path never
+does.  It shares no code with the GPU library: it reads raw input bytes
+(bf16 bit patterns, e4m3fn codes, fp32) and computes everything in float64
+with plain NumPy, following the definitions on the pages:
+
+* "IndexShare" (LLM Architecture Gallery), section "Why The Indexer Becomes
+  Expensive": a lightweight indexer scores the preceding tokens of a query and
+  keeps the top-k positions; the main attention then runs on that subset only.
+* "GLM-5.2 and IndexShare for Long-Context Sparse Attention", section "Where
+  the DSA indexer becomes expensive": the indexer keeps the top 2,048 earlier
+  tokens for each query position.
+* "IndexShare" (LLM Architecture Gallery), section "How IndexShare Works": a
+  full layer runs the indexer, does the top-k and stores the selected
+  positions; a shared layer skips both and reuses the most recent full layer's
+  positions; only the integer positions cross layers.
+* "IndexCache: Killing the Indexer's O(NL^2) Bottleneck" notes, section 2:
+  F layers compute fresh top-k, S layers reuse the nearest preceding F layer's
+  result, and the first layer is always F.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+* indexer score: score(t, s) = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :]),
+  one key vector per token shared by all indexer heads (the pages only say
+  "few heads, low-rank, FP8");
+* a query at absolute position p may select any s with 0 <= s <= p (itself
+  included), and s < kv_len;
+* order: larger score first, equal scores -> lower position first; the row is
+  emitted as ascending positions, padded with -1 to length k;
+* fp8 keys are e4m3fn codes times a per-row fp32 scale;
+* attention over the selected rows: o = softmax(sm_scale * Q K^T) V with K the
+  whole latent row and V its first d_v dims; slots holding -1 (or any value
+  outside [0, kv_len)) are ignored; a row with no valid slot gives o = 0 and
+  lse = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16", "decode_e4m3fn", "key_matrix", "indexer_scores", "select_topk",
+    "indexer_topk", "attention_row", "sparse_attention", "group_forward",
+]
+
+
+# ---------------------------------------------------------------- decoding --
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64.  A bf16 value is the upper half
+    of an IEEE binary32 word, so widening is a 16-bit shift."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """OCP FP8 E4M3FN codes (uint8) -> float64.
+
+    1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+    holds subnormals m * 2^-9; code 0x7F/0xFF is NaN; there is no infinity.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = m * 2.0 ** -9
+    v = np.where(e == 0, sub, normal)
+    v = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, v)
+    return sign * v
+
+
+def key_matrix(keys, key_dtype: str, scale=None) -> np.ndarray:
+    """Stored indexer keys [..., n, d] -> float64 values (codes times the row
+    scale for fp8)."""
+    if key_dtype == "bf16":
+        return decode_bf16(keys)
+    if key_dtype == "fp8":
+        v = decode_e4m3fn(keys)
+        return v * np.asarray(scale, dtype=np.float64)[..., None]
+    raise ValueError(f"unknown key dtype {key_dtype!r}")
+
+
+# ----------------------------------------------------------------- indexer --
+def indexer_scores(q_row: np.ndarray, w_row: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """score[s] = sum_h w[h] * max(0, q[h, :] . keys[s, :]) in float64.
+
+    q_row [H, d], w_row [H], keys [n, d] (already decoded) -> [n].
+    """
+    x = keys @ q_row.T                       # [n, H]: one dot product per head
+    return np.maximum(x, 0.0) @ w_row        # weighted sum of the ReLU'd heads
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """The first min(k, n) positions under (score desc, position asc),
+    returned in ascending position order and padded with -1 to length k.
+
+    A stable sort of -score keeps ascending position among equal scores
+    (+0.0 and -0.0 compare equal)."""
+    n = scores.shape[0]
+    order = np.argsort(-scores, kind="stable")
+    sel = np.sort(order[: min(k, n)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[: sel.shape[0]] = sel
+    return out
+
+
+def indexer_topk(q, w, keys, key_dtype, scale, q_start: int, kv_len: int, k: int,
+                 rows=None) -> np.ndarray:
+    """Full-layer indexer + top-k for every (sequence, query row).
+
+    q: bf16 bits [B, n_q, H, d]; w: fp32 [B, n_q, H]; keys: [B, cap, d] bf16
+    bits or e4m3fn codes; scale: [B, cap] fp32 (fp8 only).  ``rows`` limits
+    the work to the listed query rows (the result then has len(rows) rows).
+    Returns int32 [B, len(rows), k].
+    """
+    q = np.asarray(q)
+    B, n_q = q.shape[0], q.shape[1]
+    rows = list(range(n_q)) if rows is None else list(rows)
+    out = np.full((B, len(rows), k), -1, dtype=np.int32)
+    for b in range(B):
+        p_max = min(q_start + max(rows), kv_len - 1)
+        sc = None if scale is None else np.asarray(scale)[b, : p_max + 1]
+        kmat = key_matrix(np.asarray(keys)[b, : p_max + 1], key_dtype, sc)
+        for i, t in enumerate(rows):
+            p = q_start + t
+            n = min(p, kv_len - 1) + 1
+            s = indexer_scores(decode_bf16(q[b, t]), np.asarray(w[b, t], np.float64),
+                               kmat[:n])
+            out[b, i] = select_topk(s, k)
+    return out
+
+
+# --------------------------------------------------------------- attention --
+def attention_row(q_row: np.ndarray, kv: np.ndarray, sel: np.ndarray, sm_scale: float,
+                  d_v: int):
+    """Exact softmax attention of one query row over the latent rows ``sel``.
+
+    q_row [Hq, D] float64; kv [n, D] float64 (all rows); sel: valid row ids.
+    Returns (o [Hq, d_v], lse [Hq]) in float64.
+    """
+    hq = q_row.shape[0]
+    if sel.size == 0:
+        return np.zeros((hq, d_v)), np.full(hq, -np.inf)
+    rows = kv[sel]                                   # [m, D]
+    z = sm_scale * (q_row @ rows.T)                  # [Hq, m]
+    mx = z.max(axis=1, keepdims=True)
+    p = np.exp(z - mx)
+    den = p.sum(axis=1)
+    o = (p @ rows[:, :d_v]) / den[:, None]
+    return o, mx[:, 0] + np.log(den)
+
+
+def sparse_attention(Q, KV, idx, kv_len: int, sm_scale: float, d_v: int, rows=None,
+                     idx_rows=None):
+    """Sparse attention of every query row over its selected positions.
+
+    Q: bf16 bits [B, n_q, Hq, D]; KV: bf16 bits [B, cap, D]; idx: int32
+    [B, n_idx, k].  ``rows`` picks the query rows; ``idx_rows`` gives, for each
+    of them, its row in ``idx`` (default: the same index).  Slots outside
+    [0, kv_len) are ignored.  Returns (O [B, R, Hq, d_v], lse [B, R, Hq]).
+    """
+    Q = np.asarray(Q)
+    B, n_q, hq, _ = Q.shape
+    rows = list(range(n_q)) if rows is None else list(rows)
+    idx_rows = rows if idx_rows is None else list(idx_rows)
+    O = np.zeros((B, len(rows), hq, d_v))
+    L = np.zeros((B, len(rows), hq))
+    for b in range(B):
+        for i, (t, it) in enumerate(zip(rows, idx_rows)):
+            r = np.asarray(idx[b, it]).astype(np.int64)
+            sel = r[(r >= 0) & (r < kv_len)]
+            kv = decode_bf16(np.asarray(KV)[b, sel])    # decode only the rows used
+            O[b, i], L[b, i] = attention_row(decode_bf16(Q[b, t]), kv,
+                                             np.arange(sel.size), sm_scale, d_v)
+    return O, L
+
+
+# ---------------------------------------------------------------- schedule --
+def group_forward(roles: str, indexer_layers, attn_layers, q_start: int, kv_len: int,
+                  k: int, sm_scale: float, d_v: int, rows=None):
+    """Walk one IndexShare layer group.
+
+    roles: one letter per layer, "F" (runs indexer + top-k and stores the
+    positions) or "S" (reuses the most recent F layer's positions untouched).
+    indexer_layers[l] = (q, w, keys, key_dtype, scale) — read for F layers
+    only; attn_layers[l] = (Q, KV).  Returns a dict with per-layer outputs
+    "O"/"lse", the list "idx" of index buffers (one per F layer), "used" (for
+    each layer, which F buffer it attended over) and "n_indexer_runs".
+    """
+    if not roles or roles[0] != "F":
+        raise ValueError("the first layer of a group must be a full (F) layer")
+    cur = None
+    idx_list, used, outs, lses = [], [], [], []
+    runs = 0
+    for l, role in enumerate(roles):
+        if role == "F":
+            q, w, keys, kd, sc = indexer_layers[l]
+            cur = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows)
+            idx_list.append(cur)
+            runs += 1
+        elif role != "S":
+            raise ValueError(f"unknown role {role!r}")
+        used.append(len(idx_list) - 1)
+        Q, KV = attn_layers[l]
+        n_r = cur.shape[1]
+        o, lse = sparse_attention(Q, KV, cur, kv_len, sm_scale, d_v, rows=rows,
+                                  idx_rows=range(n_r))
+        outs.append(o)
+        lses.append(lse)
+    return {"O": outs, "lse": lses, "idx": idx_list, "used": used, "n_indexer_runs": runs}

@@ -1,0 +1,96 @@
+"""Plant plausible mistakes in the CPU oracle and check that the pins catch
+each one (the pins are only worth something if they fail on a wrong oracle).
+CPU only; every mutation is undone by monkeypatch."""
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as O
+import test_oracle_pins as P
+
+
+def _no_relu(q_row, w_row, keys):
+    return (keys @ q_row.T) @ w_row
+
+
+def _abs_weights(q_row, w_row, keys):
+    return np.maximum(keys @ q_row.T, 0.0) @ np.abs(w_row)
+
+
+def _transposed_q(q_row, w_row, keys):
+    # the hand-worked example is square (H = d = 2), so q^T has q's shape
+    return np.maximum(keys @ q_row, 0.0) @ w_row
+
+
+def _ties_to_higher_position(scores, k):
+    n = scores.shape[0]
+    order = np.lexsort((-np.arange(n), -scores))       # equal scores: higher position first
+    sel = np.sort(order[: min(k, n)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[: sel.shape[0]] = sel
+    return out
+
+
+def _score_order_output(scores, k):
+    n = scores.shape[0]
+    order = np.argsort(-scores, kind="stable")[: min(k, n)]
+    out = np.full(k, -1, dtype=np.int32)
+    out[: order.shape[0]] = order
+    return out
+
+
+def _e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    v = np.where(e == 0, m * 2.0 ** -10, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    v = np.where((e == 0xF) & ((c & 7) == 7), np.nan, v)
+    return sign * v
+
+
+def _attn_wrong_v(q_row, kv, sel, sm_scale, d_v):
+    rows = kv[sel]
+    z = sm_scale * (q_row @ rows.T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    den = p.sum(axis=1)
+    return (p @ rows[:, -d_v:]) / den[:, None], z.max(axis=1) + np.log(den)
+
+
+def _attn_no_scale(q_row, kv, sel, sm_scale, d_v):
+    return ATTN(q_row, kv, sel, 1.0, d_v)
+
+
+ATTN = O.attention_row
+INDEXER = O.indexer_topk
+
+HAND = {c["p"] * 100 + c["k"]: c for c in P.gold()["indexer"]["cases"]}
+
+MUTATIONS = [
+    ("drop_relu", "indexer_scores", _no_relu, lambda: P.test_hand_worked_indexer_topk(HAND[403])),
+    ("abs_weights", "indexer_scores", _abs_weights, lambda: P.test_hand_worked_indexer_topk(HAND[402])),
+    ("transposed_q", "indexer_scores", _transposed_q, P.test_hand_worked_indexer_scores),
+    ("ties_high_pos", "select_topk", _ties_to_higher_position, P.test_select_topk_brute_force_tiny),
+    ("score_order", "select_topk", _score_order_output, lambda: P.test_hand_worked_indexer_topk(HAND[402])),
+    ("e4m3_bias", "decode_e4m3fn", _e4m3_bias8, P.test_e4m3fn_decode_matches_torch_for_all_256_codes),
+    ("wrong_v_slice", "attention_row", _attn_wrong_v, P.test_hand_worked_attention),
+    ("no_sm_scale", "attention_row", _attn_no_scale, P.test_attention_with_full_prefix_equals_dense_causal_sdpa),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn,check", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, name, attr, fn, check):
+    check()                                   # passes on the real oracle
+    monkeypatch.setattr(O, attr, fn)
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_pins_catch_self_excluded_causality(monkeypatch):
+    """A query that may not select its own position changes the hand-worked
+    p=4, k=5 row (position 4 would be missing)."""
+    def excl(q, w, keys, key_dtype, scale, q_start, kv_len, k, rows=None):
+        out = INDEXER(q, w, keys, key_dtype, scale, q_start, kv_len, k, rows)
+        return np.where(out == q_start, -1, out)
+    monkeypatch.setattr(O, "indexer_topk", excl)
+    with pytest.raises(AssertionError):
+        P.test_hand_worked_indexer_topk(HAND[405])

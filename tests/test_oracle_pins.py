@@ -1,0 +1,340 @@
+"""Pins for the CPU oracle: checked against hand-worked examples, library
+routines, brute force on tiny inputs and closed forms -- never against itself.
+CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import dsa_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float values (exactly representable in bf16) -> bf16 bit patterns."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    assert torch.equal(t.float(), torch.as_tensor(np.asarray(x, dtype=np.float32))), \
+        "fixture value not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------- decoders ----
+def test_e4m3fn_decode_matches_torch_for_all_256_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().double().numpy()
+    got = O.decode_e4m3fn(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2                     # 0x7F and 0xFF only: no infinities
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = O.decode_bf16(bits)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~ok)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+# ----------------------------------------------------- hand-worked cases ----
+def _hand_inputs(g):
+    ix = g["indexer"]
+    q = bf16_bits(ix["q"])[None, None]                      # [1, 1, H, d]
+    w = np.asarray(ix["w"], np.float32)[None, None]
+    keys = bf16_bits(ix["keys"])[None]                      # [1, 5, d]
+    return q, w, keys
+
+
+def test_hand_worked_indexer_scores():
+    g = gold()
+    q, w, keys = _hand_inputs(g)
+    s = O.indexer_scores(O.decode_bf16(q[0, 0]), w[0, 0].astype(np.float64),
+                         O.key_matrix(keys[0], "bf16"))
+    np.testing.assert_array_equal(s, g["indexer"]["scores_p4"])
+
+
+@pytest.mark.parametrize("case", gold()["indexer"]["cases"], ids=lambda c: f"p{c['p']}k{c['k']}")
+def test_hand_worked_indexer_topk(case):
+    q, w, keys = _hand_inputs(gold())
+    idx = O.indexer_topk(q, w, keys, "bf16", None, q_start=case["p"], kv_len=5, k=case["k"])
+    assert idx.tolist() == [[case["idx"]]]
+
+
+def test_hand_worked_attention():
+    a = gold()["attention"]
+    Q = bf16_bits(a["q"])[None, None]
+    KV = bf16_bits(a["kv"])[None]
+    idx = np.asarray(a["idx"], np.int32)[None, None]
+    o, lse = O.sparse_attention(Q, KV, idx, a["kv_len"], math.log(2.0), a["d_v"])
+    np.testing.assert_allclose(o[0, 0], a["o"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(np.exp(lse[0, 0]), a["lse_exp"], rtol=1e-14)
+
+
+# ------------------------------------------------------------- brute force --
+def _brute_topk(scores, k):
+    """Enumerate every subset of size min(k, n); the answer is the unique one
+    in which each member beats each non-member (higher score, or equal score
+    and lower position)."""
+    n = len(scores)
+    m = min(k, n)
+    found = []
+    for sub in itertools.combinations(range(n), m):
+        inside = set(sub)
+        if all((scores[i] > scores[j]) or (scores[i] == scores[j] and i < j)
+               for i in inside for j in range(n) if j not in inside):
+            found.append(sub)
+    assert len(found) == 1
+    return list(found[0]) + [-1] * (k - m)
+
+
+def test_select_topk_brute_force_tiny():
+    rng = np.random.default_rng(1)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 10))
+        scores = rng.integers(-2, 3, size=n).astype(np.float64)   # many ties
+        if trial % 3 == 0:
+            scores = scores * -0.0 + scores                       # keep -0.0/+0.0 mixes
+            scores[scores == 0] = np.where(rng.random(np.sum(scores == 0)) < 0.5, -0.0, 0.0)
+        assert O.select_topk(scores, k).tolist() == _brute_topk(list(scores), k)
+
+
+def test_indexer_topk_brute_force_tiny_end_to_end():
+    """Whole indexer on tiny integer inputs against scores summed by explicit
+    loops and the subset-enumeration selection."""
+    rng = np.random.default_rng(2)
+    for _ in range(20):
+        H, d, n = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(2, 8))
+        qv = rng.integers(-3, 4, size=(H, d)).astype(np.float32)
+        kv = rng.integers(-3, 4, size=(n, d)).astype(np.float32)
+        wv = rng.choice([-2.0, -1.0, 1.0, 2.0, 4.0], size=H).astype(np.float32)
+        k = int(rng.integers(1, n + 2))
+        p = n - 1
+        ref = []
+        for s in range(n):
+            tot = 0.0
+            for h in range(H):
+                dot = 0.0
+                for j in range(d):
+                    dot += float(qv[h, j]) * float(kv[s, j])
+                tot += float(wv[h]) * (dot if dot > 0 else 0.0)
+            ref.append(tot)
+        got = O.indexer_topk(bf16_bits(qv)[None, None], wv[None, None], bf16_bits(kv)[None],
+                             "bf16", None, q_start=p, kv_len=n, k=k)
+        assert got[0, 0].tolist() == _brute_topk(ref, k)
+
+
+# ------------------------------------------------------------ closed forms --
+def _ix(q, w, keys, q_start, kv_len, k, kd="bf16", scale=None):
+    return O.indexer_topk(q, w, keys, kd, scale, q_start, kv_len, k)
+
+
+def test_k_at_least_candidates_selects_whole_prefix():
+    rng = np.random.default_rng(3)
+    n, H, d = 40, 3, 8
+    q = bf16_bits(rng.integers(-8, 9, (1, n, H, d)))
+    w = rng.choice([1.0, 2.0, 4.0], (1, n, H)).astype(np.float32)
+    keys = bf16_bits(rng.integers(-8, 9, (1, n, d)))
+    idx = _ix(q, w, keys, 0, n, k=n)
+    for t in range(n):
+        assert idx[0, t].tolist() == list(range(t + 1)) + [-1] * (n - t - 1)
+
+
+def test_zero_query_keeps_lowest_positions():
+    n, H, d, k = 50, 2, 4, 7
+    q = bf16_bits(np.zeros((1, 1, H, d)))
+    w = np.ones((1, 1, H), np.float32)
+    keys = bf16_bits(np.random.default_rng(4).integers(-8, 9, (1, n, d)))
+    assert _ix(q, w, keys, n - 1, n, k)[0, 0].tolist() == list(range(k))
+
+
+def test_increasing_scores_keep_latest_positions():
+    n, k = 200, 16
+    keys = bf16_bits(np.arange(n, dtype=np.float32)[None, :, None])   # key[s] = s
+    q = bf16_bits(np.ones((1, 3, 1, 1)))
+    w = np.ones((1, 3, 1), np.float32)
+    idx = _ix(q, w, keys, n - 3, n, k)
+    for i in range(3):
+        p = n - 3 + i
+        assert idx[0, i].tolist() == list(range(p - k + 1, p + 1))
+
+
+def test_decreasing_scores_keep_earliest_positions():
+    n, k = 200, 16
+    keys = bf16_bits(np.arange(n, dtype=np.float32)[None, :, None])
+    q = bf16_bits(np.ones((1, 1, 1, 1)))
+    w = -np.ones((1, 1, 1), np.float32)                 # score = -s
+    assert _ix(q, w, keys, n - 1, n, k)[0, 0].tolist() == list(range(k))
+
+
+def test_single_head_nonnegative_reduces_to_matmul():
+    rng = np.random.default_rng(5)
+    qv = rng.integers(0, 9, (1, 16)).astype(np.float32)
+    kv = rng.integers(0, 9, (30, 16)).astype(np.float32)
+    s = O.indexer_scores(O.decode_bf16(bf16_bits(qv)), np.ones(1), O.key_matrix(bf16_bits(kv), "bf16"))
+    np.testing.assert_array_equal(s, (kv.astype(np.float64) @ qv[0].astype(np.float64)))
+
+
+def test_positive_homogeneity_leaves_selection_unchanged():
+    rng = np.random.default_rng(6)
+    n, H, d, k = 120, 4, 8, 10
+    q = rng.integers(-8, 9, (1, 8, H, d)).astype(np.float32)
+    w = rng.choice([1.0, 2.0, 4.0], (1, 8, H)).astype(np.float32)
+    keys = bf16_bits(rng.integers(-8, 9, (1, n, d)))
+    base = _ix(bf16_bits(q), w, keys, n - 8, n, k)
+    assert np.array_equal(base, _ix(bf16_bits(4 * q), w, keys, n - 8, n, k))
+    assert np.array_equal(base, _ix(bf16_bits(q), 8 * w, keys, n - 8, n, k))
+
+
+def test_fp8_keys_with_scale_match_equal_bf16_values():
+    """The same key values stored as e4m3fn codes * scale or as bf16 give the
+    same selection; the row scale multiplies the key."""
+    rng = np.random.default_rng(7)
+    n, H, d, k = 64, 4, 16, 9
+    ints = rng.integers(-8, 9, (1, n, d)).astype(np.float32)
+    codes = torch.from_numpy(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scale = np.full((1, n), 0.125, np.float32)
+    q = bf16_bits(rng.integers(-8, 9, (1, 4, H, d)))
+    w = rng.choice([1.0, 2.0, 4.0], (1, 4, H)).astype(np.float32)
+    a = _ix(q, w, codes, n - 4, n, k, kd="fp8", scale=scale)
+    b = _ix(q, w, bf16_bits(ints / 8.0), n - 4, n, k)
+    assert np.array_equal(a, b)
+    km = O.key_matrix(codes[0], "fp8", scale[0])
+    np.testing.assert_array_equal(km, ints[0] / 8.0)
+
+
+# -------------------------------------------------------------- attention --
+def _rand_bf16(rng, shape, scale=1.0):
+    return torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)) \
+        .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_attention_with_full_prefix_equals_dense_causal_sdpa():
+    """k >= candidate count: sparse attention over the whole prefix must equal
+    dense causal attention (torch's scaled_dot_product_attention, float64)."""
+    rng = np.random.default_rng(8)
+    L, Hq, D, Dv = 12, 3, 8, 5
+    Q = _rand_bf16(rng, (1, L, Hq, D))
+    KV = _rand_bf16(rng, (1, L, D))
+    idx = np.full((1, L, L), -1, np.int32)
+    for t in range(L):
+        idx[0, t, : t + 1] = np.arange(t + 1)
+    sm = 1.0 / math.sqrt(D)
+    o, lse = O.sparse_attention(Q, KV, idx, L, sm, Dv)
+    q = torch.from_numpy(O.decode_bf16(Q[0])).permute(1, 0, 2)[None]          # [1,Hq,L,D]
+    kvt = torch.from_numpy(O.decode_bf16(KV[0]))
+    kk = kvt[None, None].expand(1, Hq, L, D)
+    vv = kvt[None, None, :, :Dv].expand(1, Hq, L, Dv)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True, scale=sm)
+    np.testing.assert_allclose(o[0], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    # lse against a log-sum-exp over the causal logits
+    logits = (q @ kk.transpose(-1, -2)) * sm
+    mask = torch.triu(torch.ones(L, L, dtype=torch.bool), 1)
+    ref_lse = torch.logsumexp(logits.masked_fill(mask, -math.inf), dim=-1)   # [1,Hq,L]
+    np.testing.assert_allclose(lse[0], ref_lse[0].T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_single_slot_returns_value_row():
+    rng = np.random.default_rng(9)
+    Q = _rand_bf16(rng, (1, 1, 4, 16))
+    KV = _rand_bf16(rng, (1, 10, 16))
+    idx = np.full((1, 1, 6), -1, np.int32)
+    idx[0, 0, 3] = 7
+    o, _ = O.sparse_attention(Q, KV, idx, 10, 0.3, 12)
+    for h in range(4):
+        np.testing.assert_array_equal(o[0, 0, h], O.decode_bf16(KV[0, 7, :12]))
+
+
+def test_attention_zero_query_is_mean_of_selected_values():
+    rng = np.random.default_rng(10)
+    Q = bf16_bits(np.zeros((1, 1, 2, 8)))
+    KV = _rand_bf16(rng, (1, 20, 8))
+    sel = [2, 5, 11, 19]
+    idx = np.asarray([[sel + [-1, -1]]], np.int32)
+    o, lse = O.sparse_attention(Q, KV, idx, 20, 1.0, 6)
+    ref = O.decode_bf16(KV[0, sel, :6]).mean(axis=0)
+    np.testing.assert_allclose(o[0, 0, 0], ref, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], math.log(4.0), rtol=0, atol=1e-15)
+
+
+def test_attention_ignores_out_of_range_slots_and_slot_order():
+    rng = np.random.default_rng(11)
+    Q = _rand_bf16(rng, (1, 1, 2, 8))
+    KV = _rand_bf16(rng, (1, 20, 8))
+    a = np.asarray([[[1, 4, 9, -1, -1]]], np.int32)
+    b = np.asarray([[[9, -1, 1, 25, 4]]], np.int32)      # 25 >= kv_len: ignored
+    oa, la = O.sparse_attention(Q, KV, a, 20, 0.5, 8)
+    ob, lb = O.sparse_attention(Q, KV, b, 20, 0.5, 8)
+    np.testing.assert_allclose(oa, ob, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-14)
+    none = np.full((1, 1, 3), -1, np.int32)
+    on, ln = O.sparse_attention(Q, KV, none, 20, 0.5, 8)
+    assert np.all(on == 0) and np.all(np.isneginf(ln))
+
+
+# --------------------------------------------------------------- schedule --
+def _group_inputs(rng, roles, n=24, H=2, d=4, Hq=2, D=8, same_indexer=False):
+    ixl, atl = [], []
+    shared = None
+    for _ in roles:
+        if same_indexer and shared is not None:
+            ixl.append(shared)
+        else:
+            q = bf16_bits(rng.integers(-8, 9, (1, n, H, d)))
+            w = rng.choice([1.0, 2.0, 4.0], (1, n, H)).astype(np.float32)
+            keys = bf16_bits(rng.integers(-8, 9, (1, n, d)))
+            shared = (q, w, keys, "bf16", None)
+            ixl.append(shared)
+        atl.append((_rand_bf16(rng, (1, n, Hq, D)), _rand_bf16(rng, (1, n, D))))
+    return ixl, atl
+
+
+def test_schedule_fsss_runs_indexer_once_and_shares_positions():
+    rng = np.random.default_rng(12)
+    ixl, atl = _group_inputs(rng, "FSSS")
+    r = O.group_forward("FSSS", ixl, atl, 0, 24, 5, 0.35, 6)
+    assert r["n_indexer_runs"] == 1 and r["used"] == [0, 0, 0, 0] and len(r["idx"]) == 1
+    for l in range(4):     # every layer attends over exactly the F layer's positions
+        o, _ = O.sparse_attention(atl[l][0], atl[l][1], r["idx"][0], 24, 0.35, 6)
+        np.testing.assert_array_equal(o, r["O"][l])
+    assert not np.array_equal(r["O"][0], r["O"][1])   # own Q/KV per layer
+
+
+def test_schedule_two_groups_and_all_full_equivalence():
+    rng = np.random.default_rng(13)
+    ixl, atl = _group_inputs(rng, "FSSSFSSS")
+    r = O.group_forward("FSSSFSSS", ixl, atl, 0, 24, 5, 0.35, 6)
+    assert r["n_indexer_runs"] == 2 and r["used"] == [0] * 4 + [1] * 4
+    # all-F with identical indexer inputs per group reproduces F+3S
+    ix_same = [ixl[0]] * 4 + [ixl[4]] * 4
+    rf = O.group_forward("FFFFFFFF", ix_same, atl, 0, 24, 5, 0.35, 6)
+    assert rf["n_indexer_runs"] == 8
+    for l in range(8):
+        np.testing.assert_array_equal(rf["O"][l], r["O"][l])
+
+
+def test_schedule_rejects_leading_shared_layer():
+    rng = np.random.default_rng(14)
+    ixl, atl = _group_inputs(rng, "SFSS")
+    with pytest.raises(ValueError):
+        O.group_forward("SFSS", ixl, atl, 0, 24, 5, 0.35, 6)
+
+
+def test_oracle_exports():
+    for name in oracle.__all__:
+        assert callable(getattr(oracle, name))
