@@ -1,0 +1,175 @@
+/*
+ * ix.h -- C ABI of the MI355X (gfx950) DSA layer-group library "libix".
+ *
+ * The method (DeepSeek Sparse Attention under GLM-5.2's IndexShare schedule):
+ *   - "IndexShare" (LLM Architecture Gallery), section "Why The Indexer
+ *     Becomes Expensive": a lightweight indexer scores the tokens preceding a
+ *     query and keeps the top-k positions; the main attention then runs over
+ *     that subset only.
+ *   - "GLM-5.2 and IndexShare for Long-Context Sparse Attention", section
+ *     "Where the DSA indexer becomes expensive": k = 2,048.
+ *   - "IndexShare", section "How IndexShare Works": a full (F) layer runs the
+ *     indexer and the top-k and stores the selected positions; a shared (S)
+ *     layer skips both and reuses the most recent F layer's positions; only
+ *     those integer positions are shared.
+ *   - "IndexCache: Killing the Indexer's O(NL^2) Bottleneck" notes, section 2:
+ *     the first layer of a pattern is always F.
+ *
+ * Conventions for every entry point
+ *   - Tensors are row-major, last dimension innermost.  "B" is the number of
+ *     independent sequences, "n_q" query rows per sequence, "cap" the row
+ *     stride of the per-sequence key / latent-KV caches.
+ *   - Query row t of a sequence sits at absolute position p = q_start + t and
+ *     may select any key position s with 0 <= s <= p (itself included).
+ *     q_start + n_q <= kv_len <= kv_cap is required.
+ *   - All pointers except the problem/descriptor structs are DEVICE pointers
+ *     (HBM of the current HIP device) and must be 16-byte aligned.  The
+ *     caller allocates and owns every buffer, including the workspace; the
+ *     library allocates no device memory and keeps no pointer after a call
+ *     returns.  Buffers must stay alive until the work on `stream` completes.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: they enqueue kernels and return.
+ *   - Every argument is validated before anything is enqueued: a non-IX_OK
+ *     return means nothing was launched.  IX_E_HIP reports a failed launch;
+ *     ix_last_error() then holds the HIP error text.  No C++ exception
+ *     crosses the ABI.  Calls on one stream are ordered; the library holds no
+ *     global mutable state besides the last-error string, so different
+ *     streams/threads may call concurrently.
+ */
+#ifndef IX_H_
+#define IX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IX_ABI_VERSION 1
+
+typedef enum ix_status {
+  IX_OK = 0,
+  IX_E_NULL = 1,       /* a required pointer is NULL                         */
+  IX_E_SHAPE = 2,      /* unsupported or inconsistent size, or misalignment  */
+  IX_E_DTYPE = 3,      /* unknown key dtype                                   */
+  IX_E_ROLES = 4,      /* n_layers outside [1, 64], or layer 0 is not F       */
+  IX_E_WORKSPACE = 5,  /* ws_bytes smaller than ix_workspace_bytes()          */
+  IX_E_HIP = 6         /* a HIP launch failed                                 */
+} ix_status;
+
+typedef enum ix_dtype {
+  IX_DTYPE_BF16 = 1,        /* bfloat16 values                                 */
+  IX_DTYPE_FP8_E4M3FN = 2   /* OCP FP8 E4M3FN codes times a per-row fp32 scale */
+} ix_dtype;
+
+typedef enum ix_indexer_path {
+  IX_PATH_AUTO = 0,         /* library picks: fused when there are many rows   */
+  IX_PATH_FUSED = 1,        /* scores streamed straight into the top-k, never stored */
+  IX_PATH_MATERIALIZED = 2  /* one fp32 score row per query in the workspace, then top-k */
+} ix_indexer_path;
+
+typedef enum ix_op {
+  IX_OP_INDEXER_TOPK = 1,   /* op_desc: const ix_indexer_in*  */
+  IX_OP_SPARSE_ATTN = 2,    /* op_desc: const ix_attn_in*     */
+  IX_OP_GROUP_FORWARD = 3,  /* op_desc: const ix_group_desc*  */
+  IX_OP_TOPK_SCORES = 4     /* op_desc: NULL                  */
+} ix_op;
+
+/* Sizes shared by every layer of a call. */
+typedef struct ix_problem {
+  int32_t batch;    /* B >= 1                                                  */
+  int32_t n_q;      /* query rows per sequence, >= 1                           */
+  int64_t q_start;  /* absolute position of query row 0, >= 0                  */
+  int64_t kv_len;   /* valid key rows per sequence, q_start + n_q <= kv_len    */
+  int64_t kv_cap;   /* allocated rows per sequence (row stride), >= kv_len     */
+  int32_t k;        /* positions kept per query row, 1 <= k <= 2048            */
+  int32_t reserved; /* must be 0                                               */
+} ix_problem;
+
+/* Inputs of one full layer's indexer.
+ * score(t, s) = sum_h w[t,h] * max(0, q[t,h,:] . key[s,:]), where key[s,:] is
+ * the bf16 row, or the e4m3fn codes of row s times k_scale[s].  The pages name
+ * the indexer only as "few heads, low-rank, FP8" (IndexCache notes, section
+ * 1); this weighted-ReLU form is the library's stated reading. */
+typedef struct ix_indexer_in {
+  int32_t heads;    /* H, 1..64                                                */
+  int32_t dim;      /* d, a multiple of 16 in 16..128                          */
+  int32_t k_dtype;  /* ix_dtype of `k`                                         */
+  int32_t path;     /* ix_indexer_path                                         */
+  const void* q;    /* bf16 [B][n_q][H][d]                                     */
+  const float* w;   /* fp32 [B][n_q][H]                                        */
+  const void* k;    /* [B][kv_cap][d]: bf16, or uint8 e4m3fn codes             */
+  const float* k_scale; /* fp32 [B][kv_cap] for FP8 keys; must be NULL for bf16 */
+} ix_indexer_in;
+
+/* Inputs/outputs of one layer's sparse attention over selected latent rows.
+ * o[t,h,:] = sum_j softmax_j(sm_scale * q[t,h,:] . kv[idx_j,:]) * kv[idx_j,:d_v]
+ * over the slots j of row t whose idx lies in [0, kv_len) (others ignored). */
+typedef struct ix_attn_in {
+  int32_t q_heads;  /* Hq, 1..16                                               */
+  int32_t d_qk;     /* D: latent row width (key = whole row); 128 or 576       */
+  int32_t d_v;      /* Dv: value = first Dv dims; 96/128 for D=128, 512 for D=576 */
+  float sm_scale;   /* softmax scale; <= 0 selects 1/sqrt(D)                  */
+  int32_t kv_splits;/* slot-range splits per row (0 = library choice), <= 64   */
+  int32_t reserved; /* must be 0                                               */
+  const void* q;    /* bf16 [B][n_q][Hq][D]                                    */
+  const void* kv;   /* bf16 [B][kv_cap][D]                                     */
+  void* out;        /* bf16 [B][n_q][Hq][Dv]                                   */
+  float* lse;       /* optional fp32 [B][n_q][Hq]: natural-log sum of exp(logits); -inf for an empty row */
+} ix_attn_in;
+
+/* A layer group, for ix_workspace_bytes(IX_OP_GROUP_FORWARD). */
+typedef struct ix_group_desc {
+  int32_t n_layers;
+  int32_t reserved;
+  uint64_t f_mask;
+  const ix_indexer_in* ixr;   /* host array [n_layers] */
+  const ix_attn_in* attn;     /* host array [n_layers] */
+} ix_group_desc;
+
+int32_t ix_abi_version(void);
+const char* ix_status_str(int32_t status);
+/* Text of the last IX_E_HIP failure on the calling thread ("" if none). */
+const char* ix_last_error(void);
+
+/* Workspace bytes `op` needs for `prob` and its descriptor (0 if none).
+ * Returns 0 also when the arguments are invalid; the entry point then reports
+ * the precise status. */
+size_t ix_workspace_bytes(const ix_problem* prob, int32_t op, const void* op_desc);
+
+/* Full-layer indexer and top-k (one F layer).
+ * Writes idx int32 [B][n_q][k]: for each query row, the min(k, p+1) positions
+ * with the largest scores (equal scores: lower position wins), in ascending
+ * position order, then -1 up to k.  The fp32 score matrix is never stored on
+ * the fused path (scores stream straight into a per-row candidate set). */
+int32_t ix_indexer_topk(const ix_problem* prob, const ix_indexer_in* in, int32_t* idx,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention of one layer over an index buffer idx int32 [B][n_q][k]
+ * (typically written by ix_indexer_topk).  Entries outside [0, kv_len) are
+ * ignored; latent rows outside [0, kv_len) are never read. */
+int32_t ix_sparse_attn(const ix_problem* prob, const ix_attn_in* in, const int32_t* idx,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* One IndexShare layer group, layers run in order on `stream`.
+ * Bit l of f_mask set => layer l is full (F): it runs ix_indexer_topk with
+ * ixr[l] into the next slot of idx, then attends; clear => shared (S): it
+ * attends over the most recent F layer's slot, byte for byte unchanged.
+ * Bit 0 must be set and 1 <= n_layers <= 64.  ixr entries of S layers are
+ * ignored (may be zeroed).  idx: int32 [popcount(f_mask & ((1<<n)-1))][B][n_q][k]. */
+int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_mask,
+                         const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Top-k over caller-provided fp32 score rows: scores[(b*n_q + t)*ld + s] for
+ * s <= p = q_start + t (entries beyond p are ignored).  Same selection rule
+ * and output layout as ix_indexer_topk.  ld >= kv_len. */
+int32_t ix_topk_scores(const ix_problem* prob, const float* scores, int64_t ld, int32_t* idx,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IX_H_ */

@@ -1,0 +1,276 @@
+"""MI355X-native DSA layer group under the IndexShare schedule.
+
+Thin Python binding over the C ABI in ``include/ix.h`` (``libix.so``, built
+from ``csrc/`` for gfx950).  The functions below only marshal torch tensors
+into pointers and sizes; every step of the indexer, the top-k and the sparse
+attention runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+The method, as the pages describe it ("IndexShare", LLM Architecture Gallery,
+sections "Why The Indexer Becomes Expensive" and "How IndexShare Works"): a
+full layer runs a lightweight indexer over every preceding token, keeps the
+top-k positions (k = 2,048 in GLM-5.2) and stores them; the next shared layers
+skip the indexer and attend over those same positions with their own queries
+and latent KV.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+
+import torch
+
+__all__ = [
+    "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
+    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "lib_path", "load",
+    "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
+
+IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
+IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
+IX_PATH_AUTO, IX_PATH_FUSED, IX_PATH_MATERIALIZED = 0, 1, 2
+IX_OP_INDEXER_TOPK, IX_OP_SPARSE_ATTN, IX_OP_GROUP_FORWARD, IX_OP_TOPK_SCORES = 1, 2, 3, 4
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("n_q", c_int32), ("q_start", c_int64), ("kv_len", c_int64),
+                ("kv_cap", c_int64), ("k", c_int32), ("reserved", c_int32)]
+
+
+class IndexerIn(ctypes.Structure):
+    _fields_ = [("heads", c_int32), ("dim", c_int32), ("k_dtype", c_int32), ("path", c_int32),
+                ("q", c_void_p), ("w", c_void_p), ("k", c_void_p), ("k_scale", c_void_p)]
+
+
+class AttnIn(ctypes.Structure):
+    _fields_ = [("q_heads", c_int32), ("d_qk", c_int32), ("d_v", c_int32), ("sm_scale", c_float),
+                ("kv_splits", c_int32), ("reserved", c_int32), ("q", c_void_p), ("kv", c_void_p),
+                ("out", c_void_p), ("lse", c_void_p)]
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("reserved", c_int32), ("f_mask", c_uint64),
+                ("ixr", POINTER(IndexerIn)), ("attn", POINTER(AttnIn))]
+
+
+class IxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        detail = ""
+        if status == IX_E_HIP and _lib is not None:
+            detail = ": " + _lib.ix_last_error().decode()
+        super().__init__(f"{what}: {ix_status_str(status)}{detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load libix.so (once).  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_sparse_ix_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.ix_abi_version.restype = c_int32
+    lib.ix_abi_version.argtypes = []
+    lib.ix_status_str.restype = ctypes.c_char_p
+    lib.ix_status_str.argtypes = [c_int32]
+    lib.ix_last_error.restype = ctypes.c_char_p
+    lib.ix_last_error.argtypes = []
+    lib.ix_workspace_bytes.restype = c_size_t
+    lib.ix_workspace_bytes.argtypes = [POINTER(Problem), c_int32, c_void_p]
+    lib.ix_indexer_topk.restype = c_int32
+    lib.ix_indexer_topk.argtypes = [POINTER(Problem), POINTER(IndexerIn), c_void_p, c_void_p,
+                                    c_size_t, c_void_p]
+    lib.ix_sparse_attn.restype = c_int32
+    lib.ix_sparse_attn.argtypes = [POINTER(Problem), POINTER(AttnIn), c_void_p, c_void_p, c_size_t,
+                                   c_void_p]
+    lib.ix_group_forward.restype = c_int32
+    lib.ix_group_forward.argtypes = [POINTER(Problem), c_int32, c_uint64, POINTER(IndexerIn),
+                                     POINTER(AttnIn), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ix_topk_scores.restype = c_int32
+    lib.ix_topk_scores.argtypes = [POINTER(Problem), c_void_p, c_int64, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]
+    _lib = lib
+    return lib
+
+
+def ix_abi_version() -> int:
+    return load().ix_abi_version()
+
+
+def ix_status_str(status: int) -> str:
+    return load().ix_status_str(status).decode()
+
+
+# ---------------------------------------------------------------- helpers --
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t, name):
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None, 0
+    key = torch.device(device).index
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf, nbytes
+
+
+def _problem(batch, n_q, q_start, kv_len, kv_cap, k):
+    return Problem(batch, n_q, int(q_start), int(kv_len), int(kv_cap), int(k), 0)
+
+
+def _key_dtype(keys):
+    if keys.dtype == torch.bfloat16:
+        return IX_DTYPE_BF16
+    if keys.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return IX_DTYPE_FP8_E4M3FN
+    raise ValueError(f"indexer keys must be bf16 or e4m3fn codes, got {keys.dtype}")
+
+
+def _indexer_in(q, w, keys, k_scale, path):
+    _dev(q, "q"), _dev(w, "w"), _dev(keys, "keys")
+    _need(q.dtype == torch.bfloat16 and q.dim() == 4, "indexer q must be bf16 [B, n_q, H, d]")
+    _need(w.dtype == torch.float32 and tuple(w.shape) == tuple(q.shape[:3]), "w must be fp32 [B, n_q, H]")
+    kd = _key_dtype(keys)
+    _need(keys.dim() == 3 and keys.shape[0] == q.shape[0] and keys.shape[2] == q.shape[3],
+          "keys must be [B, cap, d]")
+    if kd == IX_DTYPE_FP8_E4M3FN:
+        _need(k_scale is not None, "fp8 keys need k_scale [B, cap]")
+        _dev(k_scale, "k_scale")
+        _need(k_scale.dtype == torch.float32 and tuple(k_scale.shape) == tuple(keys.shape[:2]),
+              "k_scale must be fp32 [B, cap]")
+    else:
+        _need(k_scale is None, "bf16 keys take no k_scale")
+    return IndexerIn(q.shape[2], q.shape[3], kd, path, _ptr(q), _ptr(w), _ptr(keys), _ptr(k_scale))
+
+
+def _attn_in(q, kv, out, lse, sm_scale, kv_splits):
+    _dev(q, "q"), _dev(kv, "kv"), _dev(out, "out")
+    _need(q.dtype == torch.bfloat16 and q.dim() == 4, "attention q must be bf16 [B, n_q, Hq, D]")
+    _need(kv.dtype == torch.bfloat16 and kv.dim() == 3 and kv.shape[2] == q.shape[3],
+          "kv must be bf16 [B, cap, D]")
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape[:3]) == tuple(q.shape[:3]),
+          "out must be bf16 [B, n_q, Hq, Dv]")
+    if lse is not None:
+        _dev(lse, "lse")
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == tuple(q.shape[:3]),
+              "lse must be fp32 [B, n_q, Hq]")
+    return AttnIn(q.shape[2], q.shape[3], out.shape[3], float(sm_scale), int(kv_splits), 0,
+                  _ptr(q), _ptr(kv), _ptr(out), _ptr(lse))
+
+
+def _check(status, what):
+    if status != IX_OK:
+        raise IxError(status, what)
+
+
+# ------------------------------------------------------------- entry points --
+def ix_workspace_bytes(prob: Problem, op: int, desc) -> int:
+    ref = None if desc is None else ctypes.byref(desc)
+    return load().ix_workspace_bytes(ctypes.byref(prob), op, ref)
+
+
+def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=0, kv_len=None, path=IX_PATH_AUTO,
+                    stream=None):
+    """Full-layer indexer + top-k into ``idx`` int32 [B, n_q, k] (see ix.h)."""
+    lib = load()
+    _dev(idx, "idx")
+    _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(q.shape[:2]), "idx must be int32 [B, n_q, k]")
+    cap = keys.shape[1]
+    prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2])
+    desc = _indexer_in(q, w, keys, k_scale, path)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, desc), q.device)
+    _check(lib.ix_indexer_topk(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
+                               _stream(stream)), "ix_indexer_topk")
+
+
+def ix_sparse_attn(q, kv, idx, out, *, lse=None, q_start=0, kv_len=None, sm_scale=0.0, kv_splits=0,
+                   stream=None):
+    """Sparse attention of one layer over ``idx`` into ``out`` (see ix.h)."""
+    lib = load()
+    _dev(idx, "idx")
+    _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(q.shape[:2]), "idx must be int32 [B, n_q, k]")
+    cap = kv.shape[1]
+    prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2])
+    desc = _attn_in(q, kv, out, lse, sm_scale, kv_splits)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_SPARSE_ATTN, desc), q.device)
+    _check(lib.ix_sparse_attn(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
+                              _stream(stream)), "ix_sparse_attn")
+
+
+def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=0, kv_len=None,
+                     sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, stream=None):
+    """One IndexShare layer group (see ix.h).
+
+    indexer_layers[l]: dict(q=, w=, keys=, k_scale=) for full layers (None for
+    shared ones); attn_layers[l]: dict(q=, kv=, out=, lse=).  Bit l of f_mask
+    marks layer l full.  idx: int32 [n_full, B, n_q, k]."""
+    lib = load()
+    n = len(attn_layers)
+    _need(len(indexer_layers) == n, "one indexer entry per layer (None for shared layers)")
+    _dev(idx, "idx")
+    _need(idx.dtype == torch.int32 and idx.dim() == 4, "idx must be int32 [n_full, B, n_q, k]")
+    a0 = attn_layers[0]
+    B, n_q = a0["q"].shape[0], a0["q"].shape[1]
+    cap = a0["kv"].shape[1]
+    prob = _problem(B, n_q, q_start, cap if kv_len is None else kv_len, cap, idx.shape[3])
+    ixr = (IndexerIn * n)()
+    att = (AttnIn * n)()
+    for l in range(n):
+        if (f_mask >> l) & 1:
+            e = indexer_layers[l]
+            _need(e is not None, f"layer {l} is full but has no indexer inputs")
+            _need(e["keys"].shape[1] == cap, "indexer keys and latent KV need the same capacity")
+            ixr[l] = _indexer_in(e["q"], e["w"], e["keys"], e.get("k_scale"), path)
+        a = attn_layers[l]
+        _need(a["q"].shape[:2] == a0["q"].shape[:2] and a["kv"].shape[1] == cap, "layers must share sizes")
+        att[l] = _attn_in(a["q"], a["kv"], a["out"], a.get("lse"), sm_scale, kv_splits)
+    gd = GroupDesc(n, 0, f_mask, ixr, att)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_GROUP_FORWARD, gd), a0["q"].device)
+    _check(lib.ix_group_forward(ctypes.byref(prob), n, f_mask, ixr, att, _ptr(idx), _ptr(ws), nb,
+                                _stream(stream)), "ix_group_forward")
+
+
+def ix_topk_scores(scores, idx, *, q_start=0, kv_len=None, stream=None):
+    """Top-k over fp32 score rows ``scores`` [B, n_q, ld] into idx [B, n_q, k]."""
+    lib = load()
+    _dev(scores, "scores"), _dev(idx, "idx")
+    _need(scores.dtype == torch.float32 and scores.dim() == 3, "scores must be fp32 [B, n_q, ld]")
+    _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(scores.shape[:2]), "idx must be int32 [B, n_q, k]")
+    ld = scores.shape[2]
+    prob = _problem(scores.shape[0], scores.shape[1], q_start, ld if kv_len is None else kv_len,
+                    ld if kv_len is None else kv_len, idx.shape[2])
+    _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), None, 0,
+                              _stream(stream)), "ix_topk_scores")

@@ -1,0 +1,82 @@
+// Device-side helpers shared by the libix kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ix {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Completes this wave's outstanding LDS operations and stops the compiler
+// from moving memory accesses across this point; used where lanes of one
+// wave exchange data through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ int wave_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Total order on fp32 scores as unsigned keys: a larger score gives a larger
+// key; -0.0 is folded onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Four OCP e4m3fn codes (one dword) -> four bf16 values (two dwords).  Every
+// e4m3fn value is exactly representable in bf16, so this is exact.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t codes) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// Wave-wide inclusive suffix sum (lane l gets the sum over lanes >= l).
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t o = __shfl_down(v, d);
+    if (l + d < kWave) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+}  // namespace ix

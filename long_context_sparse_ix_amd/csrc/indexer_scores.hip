@@ -1,0 +1,149 @@
+// Indexer scores written out as fp32 rows (few-row workloads such as decode).
+//
+// Same score as the fused kernel ("IndexShare", LLM Architecture Gallery,
+// section "Why The Indexer Becomes Expensive"):
+//     score(p, s) = sum_h w[h] * max(0, q[h,:] . key[s,:]),  s <= p,
+// but for workloads with only a handful of query rows (decode: one row per
+// sequence) there is nothing to share across rows, so the key range of every
+// row is split over many waves instead and each wave streams its own keys
+// straight from HBM into MFMA B operands (no LDS).  fp8 e4m3fn keys are
+// widened to bf16 in registers (exact) and the per-key scale is applied to the
+// finished score.  The rows are then reduced by the per-row top-k kernel.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ix {
+
+namespace {
+
+constexpr int kTileKeys = 64;
+constexpr int kTilesPerWave = 16;           // 1024 keys per wave
+constexpr int kWavesPerWG = 4;
+
+template <int HT, int KS, bool FP8>
+__global__ __launch_bounds__(kWavesPerWG * kWave) void indexer_scores_kernel(ScoreArgs a) {
+  constexpr int d = KS * 16;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int m = l & 31, hf = l >> 5;
+  const int row = blockIdx.y;                 // b * n_q + t
+  const int b = row / a.n_q, t = row % a.n_q;
+  const int64_t p = a.q_start + t;
+  const int64_t s_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kTilesPerWave * kTileKeys;
+  if (s_begin > p) return;
+
+  bf16x8 qf[HT][KS];
+  float wr[HT][16];
+  {
+    const uint16_t* qrow = a.q + (int64_t)row * a.H * d;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 32 + m;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ht][ks] = h < a.H ? *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks)
+                             : bf16x8{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hh = ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        wr[ht][r] = hh < a.H ? a.w[(int64_t)row * a.H + hh] : 0.0f;
+      }
+    }
+  }
+  const float* scale_b = FP8 ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
+  float* out = a.scores + (int64_t)row * a.ld;
+
+  for (int j = 0; j < kTilesPerWave; ++j) {
+    const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
+    if (s0 > p) break;
+    f32x16 acc[2][HT];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[nt][ht] = f32x16{};
+    bf16x8 bfr[2][KS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      int64_t s = s0 + nt * 32 + m;
+      if (s > p) s = p;                       // stays inside the cache; masked below
+      if constexpr (FP8) {
+        const uint8_t* kr = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.key_bstride + s * d + hf * (d / 2);
+        if constexpr (KS % 2 == 0) {
+#pragma unroll
+          for (int c = 0; c < KS / 2; ++c) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(kr + 16 * c);
+            const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+            const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
+            bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+            bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < KS; ++c) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(kr + 8 * c);
+            const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+            bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+          }
+        }
+      } else {
+        const uint16_t* kr = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.key_bstride + s * d + hf * (d / 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = *reinterpret_cast<const bf16x8*>(kr + 8 * ks);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks], acc[nt][ht], 0, 0, 0);
+    float part[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float s = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), s);
+      part[nt] = s;
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                     __float_as_uint(part[1]), false, false);
+    float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int64_t s = s0 + l;
+    if (s <= p) {
+      if constexpr (FP8) score *= scale_b[s];
+      out[s] = score;
+    }
+  }
+}
+
+template <int HT, int KS, bool FP8>
+hipError_t launch_scores_t(const ScoreArgs& a, int B, int64_t kv_len, hipStream_t st) {
+  const int64_t keys_per_wg = (int64_t)kWavesPerWG * kTilesPerWave * kTileKeys;
+  const int64_t max_keys = a.q_start + a.n_q;   // last row sees this many keys
+  (void)kv_len;
+  dim3 grid((unsigned)((max_keys + keys_per_wg - 1) / keys_per_wg), (unsigned)(B * a.n_q));
+  hipLaunchKernelGGL((indexer_scores_kernel<HT, KS, FP8>), grid, dim3(kWavesPerWG * kWave), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
+                                 hipStream_t s) {
+  const int HT = a.H > 32 ? 2 : 1;
+  const int KS = d / 16;
+#define IX_SC_CASE(ht, ks)                                                   \
+  if (HT == ht && KS == ks)                                                  \
+    return fp8 ? launch_scores_t<ht, ks, true>(a, B, kv_len, s)              \
+               : launch_scores_t<ht, ks, false>(a, B, kv_len, s);
+  IX_SC_CASE(1, 1) IX_SC_CASE(1, 2) IX_SC_CASE(1, 3) IX_SC_CASE(1, 4)
+  IX_SC_CASE(1, 5) IX_SC_CASE(1, 6) IX_SC_CASE(1, 7) IX_SC_CASE(1, 8)
+  IX_SC_CASE(2, 1) IX_SC_CASE(2, 2) IX_SC_CASE(2, 3) IX_SC_CASE(2, 4)
+  IX_SC_CASE(2, 5) IX_SC_CASE(2, 6) IX_SC_CASE(2, 7) IX_SC_CASE(2, 8)
+#undef IX_SC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ix

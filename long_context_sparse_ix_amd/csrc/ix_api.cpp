@@ -1,0 +1,340 @@
+// C ABI of libix: argument validation, workspace sizing, path choice and the
+// IndexShare layer-group driver.  All checks run before the first enqueue.
+//
+// Group schedule ("IndexShare", LLM Architecture Gallery, section "How
+// IndexShare Works"; "IndexCache: Killing the Indexer's O(NL^2) Bottleneck"
+// notes, section 2): a full layer runs the indexer and top-k and stores the
+// positions; a shared layer skips both and attends over the most recent full
+// layer's positions; the first layer of a pattern is full.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "ix.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kMaxK = 2048;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_problem(const ix_problem* p) {
+  if (!p) return IX_E_NULL;
+  if (p->batch < 1 || p->n_q < 1 || p->q_start < 0 || p->k < 1 || p->k > kMaxK ||
+      p->reserved != 0)
+    return IX_E_SHAPE;
+  if (p->kv_len < p->q_start + p->n_q || p->kv_cap < p->kv_len) return IX_E_SHAPE;
+  if (p->kv_len > (int64_t)INT32_MAX) return IX_E_SHAPE;   // positions are int32
+  return IX_OK;
+}
+
+int32_t check_indexer(const ix_problem* p, const ix_indexer_in* in) {
+  if (!in) return IX_E_NULL;
+  if (in->k_dtype != IX_DTYPE_BF16 && in->k_dtype != IX_DTYPE_FP8_E4M3FN) return IX_E_DTYPE;
+  if (!in->q || !in->w || !in->k) return IX_E_NULL;
+  if (in->k_dtype == IX_DTYPE_FP8_E4M3FN && !in->k_scale) return IX_E_NULL;
+  if (in->k_dtype == IX_DTYPE_BF16 && in->k_scale) return IX_E_SHAPE;
+  if (in->heads < 1 || in->heads > 64 || in->dim < 16 || in->dim > 128 || in->dim % 16 != 0)
+    return IX_E_SHAPE;
+  if (in->path < IX_PATH_AUTO || in->path > IX_PATH_MATERIALIZED) return IX_E_SHAPE;
+  if (!aligned16(in->q) || !aligned16(in->w) || !aligned16(in->k) ||
+      (in->k_scale && !aligned16(in->k_scale)))
+    return IX_E_SHAPE;
+  (void)p;
+  return IX_OK;
+}
+
+int32_t check_attn(const ix_attn_in* in) {
+  if (!in) return IX_E_NULL;
+  if (!in->q || !in->kv || !in->out) return IX_E_NULL;
+  if (in->q_heads < 1 || in->q_heads > 16 || !ix::attn_shape_supported(in->d_qk, in->d_v))
+    return IX_E_SHAPE;
+  if (in->kv_splits < 0 || in->kv_splits > 64 || in->reserved != 0) return IX_E_SHAPE;
+  if (!std::isfinite(in->sm_scale)) return IX_E_SHAPE;
+  if (!aligned16(in->q) || !aligned16(in->kv) || !aligned16(in->out) ||
+      (in->lse && !aligned16(in->lse)))
+    return IX_E_SHAPE;
+  return IX_OK;
+}
+
+bool use_fused(const ix_problem* p, const ix_indexer_in* in) {
+  if (in->path == IX_PATH_FUSED) return true;
+  if (in->path == IX_PATH_MATERIALIZED) return false;
+  const int64_t rows = (int64_t)p->batch * p->n_q;
+  const int64_t score_bytes = rows * p->kv_len * 4;
+  return rows >= 128 || score_bytes > ((int64_t)1 << 30);
+}
+
+size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
+  if (use_fused(p, in)) {
+    if (in->k_dtype == IX_DTYPE_FP8_E4M3FN)   // bf16 copy of the keys a query can reach
+      return round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
+    return 0;
+  }
+  return round_up((size_t)p->batch * p->n_q * (size_t)p->kv_len * 4);
+}
+
+int attn_splits(const ix_problem* p, const ix_attn_in* in) {
+  if (in->kv_splits > 0) return in->kv_splits;
+  const int64_t rows = (int64_t)p->batch * p->n_q;
+  if (rows >= 2048) return 1;
+  int64_t s = (2048 + rows - 1) / rows;
+  const int64_t by_slots = p->k / 128 > 1 ? p->k / 128 : 1;   // >= 128 slots per split
+  if (s > by_slots) s = by_slots;
+  if (s > 64) s = 64;
+  return (int)(s < 1 ? 1 : s);
+}
+
+int splits_effective(const ix_problem* p, const ix_attn_in* in) {
+  int s = attn_splits(p, in);
+  // never more splits than 16-slot steps
+  const int steps = (p->k + 15) / 16;
+  return s > steps ? steps : s;
+}
+
+size_t attn_ws(const ix_problem* p, const ix_attn_in* in) {
+  const int s = splits_effective(p, in);
+  if (s <= 1) return 0;
+  const size_t items = (size_t)p->batch * p->n_q * s * 16;
+  return round_up(items * in->d_v * 4) + round_up(items * 2 * 4);
+}
+
+int32_t hip_fail(hipError_t e) {
+  g_last_error = hipGetErrorString(e);
+  return IX_E_HIP;
+}
+
+int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, void* ws,
+                    hipStream_t s) {
+  const bool fp8 = in->k_dtype == IX_DTYPE_FP8_E4M3FN;
+  if (use_fused(p, in)) {
+    ix::FusedArgs a{};
+    a.q = static_cast<const uint16_t*>(in->q);
+    a.w = in->w;
+    a.idx = idx;
+    a.q_start = p->q_start;
+    a.n_q = p->n_q;
+    a.H = in->heads;
+    a.k = p->k;
+    a.C = ix::fused_candidates(p->k);
+    if (fp8) {
+      uint16_t* kb = static_cast<uint16_t*>(ws);
+      hipError_t e = ix::launch_upcast_fp8(static_cast<const uint8_t*>(in->k), p->kv_cap * in->dim,
+                                           kb, p->kv_len * in->dim, p->batch, p->kv_len, in->dim, s);
+      if (e != hipSuccess) return hip_fail(e);
+      a.keys = kb;
+      a.key_bstride = p->kv_len * in->dim;
+      a.scale = in->k_scale;
+      a.scale_bstride = p->kv_cap;
+    } else {
+      a.keys = static_cast<const uint16_t*>(in->k);
+      a.key_bstride = p->kv_cap * in->dim;
+      a.scale = nullptr;
+      a.scale_bstride = 0;
+    }
+    hipError_t e = ix::launch_fused_indexer(a, p->batch, in->dim, s);
+    return e == hipSuccess ? IX_OK : hip_fail(e);
+  }
+  ix::ScoreArgs a{};
+  a.q = static_cast<const uint16_t*>(in->q);
+  a.w = in->w;
+  a.keys = in->k;
+  a.scale = in->k_scale;
+  a.scores = static_cast<float*>(ws);
+  a.key_bstride = p->kv_cap * in->dim;
+  a.scale_bstride = p->kv_cap;
+  a.ld = p->kv_len;
+  a.q_start = p->q_start;
+  a.n_q = p->n_q;
+  a.H = in->heads;
+  hipError_t e = ix::launch_indexer_scores(a, p->batch, in->dim, fp8, p->kv_len, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k, s);
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
+int32_t run_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, void* ws,
+                 hipStream_t s) {
+  ix::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(in->q);
+  a.kv = static_cast<const uint16_t*>(in->kv);
+  a.idx = idx;
+  a.out = static_cast<uint16_t*>(in->out);
+  a.lse = in->lse;
+  a.kv_bstride = p->kv_cap * in->d_qk;
+  a.kv_len = p->kv_len;
+  a.rows = p->batch * p->n_q;
+  a.n_q = p->n_q;
+  a.Hq = in->q_heads;
+  a.k = p->k;
+  a.splits = splits_effective(p, in);
+  const int steps = (p->k + 15) / 16;
+  a.slots_per_split = ((steps + a.splits - 1) / a.splits) * 16;
+  // recompute so that no split is empty
+  a.splits = (p->k + a.slots_per_split - 1) / a.slots_per_split;
+  const float sm = in->sm_scale > 0.0f ? in->sm_scale : 1.0f / std::sqrt((float)in->d_qk);
+  a.scale_log2 = sm * 1.4426950408889634f;
+  if (a.splits > 1) {
+    const size_t items = (size_t)a.rows * a.splits * 16;
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(items * in->d_v * 4));
+  }
+  hipError_t e = ix::launch_sparse_attn(a, in->d_qk, in->d_v, s);
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
+int32_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return IX_OK;
+  if (ws_bytes < need) return IX_E_WORKSPACE;
+  if (!ws) return IX_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return IX_E_SHAPE;
+  return IX_OK;
+}
+
+size_t group_ws(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix_indexer_in* ixr,
+                const ix_attn_in* attn) {
+  size_t need = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((f_mask >> l) & 1u) {
+      const size_t w = indexer_ws(p, &ixr[l]);
+      if (w > need) need = w;
+    }
+    const size_t w = attn_ws(p, &attn[l]);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
+int32_t check_group(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
+                    const ix_indexer_in* ixr, const ix_attn_in* attn) {
+  if (n_layers < 1 || n_layers > 64) return IX_E_ROLES;
+  if (!(f_mask & 1u)) return IX_E_ROLES;
+  if (n_layers < 64 && (f_mask >> n_layers) != 0) return IX_E_ROLES;
+  if (!ixr || !attn) return IX_E_NULL;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((f_mask >> l) & 1u) {
+      int32_t st = check_indexer(p, &ixr[l]);
+      if (st != IX_OK) return st;
+    }
+    int32_t st = check_attn(&attn[l]);
+    if (st != IX_OK) return st;
+  }
+  return IX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ix_abi_version(void) { return IX_ABI_VERSION; }
+
+const char* ix_status_str(int32_t st) {
+  switch (st) {
+    case IX_OK: return "IX_OK";
+    case IX_E_NULL: return "IX_E_NULL: a required pointer is NULL";
+    case IX_E_SHAPE: return "IX_E_SHAPE: unsupported or inconsistent size, or misaligned pointer";
+    case IX_E_DTYPE: return "IX_E_DTYPE: unknown key dtype";
+    case IX_E_ROLES: return "IX_E_ROLES: bad layer count or role mask (layer 0 must be full)";
+    case IX_E_WORKSPACE: return "IX_E_WORKSPACE: workspace too small";
+    case IX_E_HIP: return "IX_E_HIP: a HIP launch failed";
+    default: return "unknown ix_status";
+  }
+}
+
+const char* ix_last_error(void) { return g_last_error.c_str(); }
+
+size_t ix_workspace_bytes(const ix_problem* p, int32_t op, const void* desc) {
+  if (check_problem(p) != IX_OK) return 0;
+  switch (op) {
+    case IX_OP_INDEXER_TOPK: {
+      auto in = static_cast<const ix_indexer_in*>(desc);
+      return check_indexer(p, in) == IX_OK ? indexer_ws(p, in) : 0;
+    }
+    case IX_OP_SPARSE_ATTN: {
+      auto in = static_cast<const ix_attn_in*>(desc);
+      return check_attn(in) == IX_OK ? attn_ws(p, in) : 0;
+    }
+    case IX_OP_GROUP_FORWARD: {
+      auto g = static_cast<const ix_group_desc*>(desc);
+      if (!g || check_group(p, g->n_layers, g->f_mask, g->ixr, g->attn) != IX_OK) return 0;
+      return group_ws(p, g->n_layers, g->f_mask, g->ixr, g->attn);
+    }
+    case IX_OP_TOPK_SCORES:
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+int32_t ix_indexer_topk(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st == IX_OK) st = check_indexer(p, in);
+  if (st != IX_OK) return st;
+  if (!idx) return IX_E_NULL;
+  if (!aligned16(idx)) return IX_E_SHAPE;
+  st = check_ws(indexer_ws(p, in), ws, ws_bytes);
+  if (st != IX_OK) return st;
+  return run_indexer(p, in, idx, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t ix_sparse_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st == IX_OK) st = check_attn(in);
+  if (st != IX_OK) return st;
+  if (!idx) return IX_E_NULL;
+  if (!aligned16(idx)) return IX_E_SHAPE;
+  st = check_ws(attn_ws(p, in), ws, ws_bytes);
+  if (st != IX_OK) return st;
+  return run_attn(p, in, idx, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t ix_group_forward(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
+                         const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st == IX_OK) st = check_group(p, n_layers, f_mask, ixr, attn);
+  if (st != IX_OK) return st;
+  if (!idx) return IX_E_NULL;
+  if (!aligned16(idx)) return IX_E_SHAPE;
+  st = check_ws(group_ws(p, n_layers, f_mask, ixr, attn), ws, ws_bytes);
+  if (st != IX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t slot = (size_t)p->batch * p->n_q * p->k;
+  int32_t* cur = nullptr;
+  int f = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((f_mask >> l) & 1u) {          // full layer: fresh positions into its own slot
+      cur = idx + slot * f++;
+      st = run_indexer(p, &ixr[l], cur, ws, s);
+      if (st != IX_OK) return st;
+    }
+    st = run_attn(p, &attn[l], cur, ws, s);   // shared layers reuse `cur` untouched
+    if (st != IX_OK) return st;
+  }
+  return IX_OK;
+}
+
+int32_t ix_topk_scores(const ix_problem* p, const float* scores, int64_t ld, int32_t* idx,
+                       void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int32_t st = check_problem(p);
+  if (st != IX_OK) return st;
+  if (!scores || !idx) return IX_E_NULL;
+  if (ld < p->kv_len || !aligned16(scores) || !aligned16(idx)) return IX_E_SHAPE;
+  hipError_t e = ix::launch_topk_rows(scores, ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
+}  // extern "C"

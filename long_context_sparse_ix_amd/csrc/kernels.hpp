@@ -1,0 +1,67 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ix {
+
+// Fused indexer score + streaming top-k (prefill and chunked prefill).
+struct FusedArgs {
+  const uint16_t* q;      // bf16 [B][n_q][H][d]
+  const float* w;         // [B][n_q][H]
+  const uint16_t* keys;   // bf16 rows, row stride d, sequence stride key_bstride
+  const float* scale;     // per-key fp32 scale, or nullptr
+  int32_t* idx;           // [B][n_q][k]
+  int64_t key_bstride;    // elements
+  int64_t scale_bstride;  // elements
+  int64_t q_start;
+  int n_q, H, k, C;       // C: candidate slots per row (>= k + 64)
+};
+size_t fused_lds_bytes(int d, int C);
+int fused_candidates(int k);
+hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s);
+
+// e4m3fn codes -> bf16 (exact), rows [0, rows) of every sequence.
+hipError_t launch_upcast_fp8(const uint8_t* src, int64_t src_bstride, uint16_t* dst,
+                             int64_t dst_bstride, int B, int64_t rows, int d, hipStream_t s);
+
+// Materialised indexer scores: scores[(b*n_q+t)*ld + s] for s <= q_start+t.
+struct ScoreArgs {
+  const uint16_t* q;
+  const float* w;
+  const void* keys;       // bf16 or e4m3fn codes, row stride d, sequence stride key_bstride
+  const float* scale;     // fp8 only
+  float* scores;
+  int64_t key_bstride;    // elements
+  int64_t scale_bstride;
+  int64_t ld;
+  int64_t q_start;
+  int n_q, H;
+};
+hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
+                                 hipStream_t s);
+
+// Per-row top-k over materialised fp32 score rows.
+hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
+                            int64_t q_start, int k, hipStream_t s);
+
+// Sparse gather attention.
+struct AttnArgs {
+  const uint16_t* q;      // [B][n_q][Hq][D]
+  const uint16_t* kv;     // [B][cap][D]
+  const int32_t* idx;     // [B][n_q][k]
+  uint16_t* out;          // [B][n_q][Hq][Dv]
+  float* lse;             // [B][n_q][Hq] or nullptr
+  float* part_o;          // splits > 1: [rows][splits][16][Dv]
+  float* part_ml;         // splits > 1: [rows][splits][16][2]
+  int64_t kv_bstride;     // elements
+  int64_t kv_len;
+  int rows, n_q, Hq, k, splits, slots_per_split;
+  float scale_log2;       // sm_scale * log2(e)
+};
+bool attn_shape_supported(int d_qk, int d_v);
+hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s);
+
+}  // namespace ix

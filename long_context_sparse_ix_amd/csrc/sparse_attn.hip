@@ -1,0 +1,252 @@
+// Sparse gather attention over selected latent rows (gfx950).
+//
+// What it computes ("IndexShare", LLM Architecture Gallery, section "Why The
+// Indexer Becomes Expensive": the main attention runs only over the selected
+// subset; "GLM-5.2 and IndexShare for Long-Context Sparse Attention", section
+// "What IndexShare reuses": every layer, shared or not, computes its own
+// attention weights and value combinations over the shared positions):
+//     o[t,h,:] = sum_j softmax_j(sm_scale * q[t,h,:] . kv[idx_j,:]) * kv[idx_j, :Dv]
+// over the slots j of row t whose idx lies in [0, kv_len).  The latent row is
+// the key; its first Dv dims are the value.
+//
+// Layout of the work
+//   * one wave = one (query row, slot range); all Hq <= 16 heads of the row
+//     share every gathered latent row, so each gathered byte feeds 16 heads;
+//   * 16 slots per step: lane (key n16 = l%16, quarter g = l/16) loads its
+//     quarter of latent row idx[n16] straight from HBM into the MFMA A operand
+//     (16 B per load, prefetched one step ahead, index words two steps ahead);
+//   * S^T = KV . Q^T with v_mfma_f32_16x16x32_bf16 (M = keys, N = heads, the
+//     query slice stays in VGPRs), so lane l ends with 4 logits of head l%16
+//     -- exactly the B-operand layout of the P.V product below;
+//   * the value part of the 16 rows is parked in a wave-private LDS tile and
+//     read back transposed (one key column per lane) as the A operand of
+//     O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16);
+//   * online softmax in base 2, rescaling the accumulators only when some
+//     head's running max grows;
+//   * with several slot-range splits per row (few-row decode), partial
+//     (o, m, l) go to the workspace and a combine kernel merges them.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ix {
+
+namespace {
+
+constexpr int kWavesPerWG = 4;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int MT>
+struct VTile {
+  static constexpr int Dv = 16 * MT;
+  // row stride in dwords chosen == 16 (mod 64): the 4 rows a transposed read
+  // touches land in disjoint bank groups
+  static constexpr int stride_dw = Dv / 2 + ((16 - (Dv / 2) % 64) + 64) % 64;
+  static constexpr int stride = 2 * stride_dw;      // bf16 elements
+  static constexpr int bytes = 16 * stride_dw * 4;
+};
+
+template <int KS, int MT>
+__global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(AttnArgs a) {
+  constexpr int D = 32 * KS, QD = 8 * KS, Dv = 16 * MT;
+  using V = VTile<MT>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int n16 = l & 15, g = l >> 4;
+  const int item = blockIdx.x * kWavesPerWG + wave;
+  if (item >= a.rows * a.splits) return;
+  const int r = item / a.splits, sp = item % a.splits;
+  const int b = r / a.n_q;
+  uint16_t* vl = reinterpret_cast<uint16_t*>(smem + wave * V::bytes);
+
+  // Query slice as the B operand: head n16, elements [g*QD + 8ks, +8).
+  const bool hq_ok = n16 < a.Hq;
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + g * QD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * ks) : bf16x8{};
+  }
+
+  const int j0 = sp * a.slots_per_split;
+  const int j1 = min(a.k, j0 + a.slots_per_split);
+  const int32_t* irow = a.idx + (int64_t)r * a.k;
+  const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride + g * QD;
+
+  f32x4 oacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  auto slot_row = [&](int c0) -> int {
+    const int slot = c0 + n16;
+    return slot < j1 ? irow[slot] : -1;
+  };
+  auto fetch = [&](int rid, bf16x8* kf) -> bool {
+    const bool valid = rid >= 0 && (int64_t)rid < a.kv_len;
+    if (valid) {
+      const uint16_t* src = kvb + (int64_t)rid * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = bf16x8{};
+    }
+    return valid;
+  };
+
+  bf16x8 kf_next[KS];
+  int rid_after = (j0 + 16 < j1) ? slot_row(j0 + 16) : -1;
+  bool valid_next = fetch(j0 < j1 ? slot_row(j0) : -1, kf_next);
+
+  for (int c0 = j0; c0 < j1; c0 += 16) {
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kf_next[ks];
+    const bool valid = valid_next;
+    // prefetch: latent rows of the next step, index words of the one after
+    const int rid_next = rid_after;
+    rid_after = (c0 + 32 < j1) ? slot_row(c0 + 32) : -1;
+    valid_next = fetch(c0 + 16 < j1 ? rid_next : -1, kf_next);
+
+    const uint32_t vm = (uint32_t)__ballot(valid) & 0xFFFFu;   // lanes 0..15 own slots 0..15
+    if (vm == 0u) continue;
+
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+    // park the value part of row n16 for the transposed read
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      if (g * QD + 8 * ks < Dv) *reinterpret_cast<bf16x8*>(vl + n16 * V::stride + g * QD + 8 * ks) = kf[ks];
+
+    float z[4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = ((vm >> (4 * g + i)) & 1u) ? sacc[i] * a.scale_log2 : -INFINITY;
+      cmax = fmaxf(cmax, z[i]);
+    }
+    cmax = wave_max_xor(cmax, 16);
+    cmax = wave_max_xor(cmax, 32);
+    const float m_new = fmaxf(m_run, cmax);
+    if (__ballot(m_new > m_run)) {
+      const float alpha = m_new > m_run ? exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
+      m_run = m_new;
+    }
+    float pv[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = m_run == -INFINITY ? 0.0f : exp2f(z[i] - m_run);
+      psum += pv[i];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
+    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
+
+    wave_lds_sync();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* col = vl + 16 * mt + n16 + 4 * g * V::stride;
+      i16x4 av;
+      av[0] = (short)col[0];
+      av[1] = (short)col[V::stride];
+      av[2] = (short)col[2 * V::stride];
+      av[3] = (short)col[3 * V::stride];
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, oacc[mt], 0, 0, 0);
+    }
+    wave_lds_sync();
+  }
+
+  // oacc[mt][i] = O^T[dv = 16mt + 4g + i][head n16]
+  if (a.splits == 1) {
+    if (hq_ok) {
+      const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+      uint16_t* orow = a.out + ((int64_t)r * a.Hq + n16) * Dv + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x2 v = {pack_bf16x2(oacc[mt][0] * inv, oacc[mt][1] * inv),
+                         pack_bf16x2(oacc[mt][2] * inv, oacc[mt][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 16 * mt) = v;
+      }
+      if (a.lse && g == 0)
+        a.lse[(int64_t)r * a.Hq + n16] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    }
+  } else {
+    const int64_t pi = ((int64_t)r * a.splits + sp) * 16 + n16;
+    float* po = a.part_o + pi * Dv + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(po + 16 * mt) = oacc[mt];
+    if (g == 0) {
+      a.part_ml[pi * 2] = m_run;
+      a.part_ml[pi * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Merge the split partials of one (row, head): base-2 log-sum-exp weights.
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int Dv) {
+  const int item = blockIdx.x;              // r * Hq + h
+  const int r = item / a.Hq, h = item % a.Hq;
+  const int S = a.splits;
+  const float* ml = a.part_ml + ((int64_t)r * S * 16 + h) * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(int64_t)s * 32]);
+  float L = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float ms = ml[(int64_t)s * 32];
+    if (ms != -INFINITY) L += ml[(int64_t)s * 32 + 1] * exp2f(ms - M);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * Dv;
+  for (int dv = threadIdx.x; dv < Dv; dv += blockDim.x) {
+    float acc = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = ml[(int64_t)s * 32];
+      if (ms == -INFINITY) continue;
+      acc += a.part_o[(((int64_t)r * S + s) * 16 + h) * Dv + dv] * exp2f(ms - M);
+    }
+    orow[dv] = (uint16_t)bf16_rne(acc * inv);
+  }
+  if (threadIdx.x == 0 && a.lse)
+    a.lse[(int64_t)r * a.Hq + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int KS, int MT>
+hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)kWavesPerWG * VTile<MT>::bytes;
+  const void* fn = reinterpret_cast<const void*>(&sparse_attn_kernel<KS, MT>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)a.rows * a.splits;
+  dim3 grid((unsigned)((items + kWavesPerWG - 1) / kWavesPerWG));
+  hipLaunchKernelGGL((sparse_attn_kernel<KS, MT>), grid, dim3(kWavesPerWG * kWave), lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.rows * a.Hq)), dim3(128), 0, s, a, 16 * MT);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_shape_supported(int d_qk, int d_v) {
+  return (d_qk == 576 && d_v == 512) || (d_qk == 128 && (d_v == 96 || d_v == 128)) ||
+         (d_qk == 64 && d_v == 64);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s) {
+  if (d_qk == 576 && d_v == 512) return launch_attn_t<18, 32>(a, s);
+  if (d_qk == 128 && d_v == 96) return launch_attn_t<4, 6>(a, s);
+  if (d_qk == 128 && d_v == 128) return launch_attn_t<4, 8>(a, s);
+  if (d_qk == 64 && d_v == 64) return launch_attn_t<2, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ix
