@@ -1,0 +1,343 @@
+"""Benchmark of the DSA layer group under the IndexShare schedule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config l128k|l16k|tiny|chunk1m|decode]
+
+A step is one pass of the whole hot path over one synthetic batch: for the
+default (headline) workload that is L = 131072 query rows through 8 layers
+arranged as two full+shared+shared+shared groups -- the indexer + streaming
+top-k on the 2 full layers and sparse attention on all 8.  Inputs are
+generated on the device before timing starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBPS = 8000.0
+
+CONFIGS = {"tiny": "tiny_l1k_exact", "l16k": "prefill_l16k", "l128k": "prefill_l128k_2groups",
+           "decode": "decode_b32_ctx200k", "chunk1m": "chunked_prefill_1m_8k"}
+
+
+def causal_pairs(w, n_rows=None):
+    """sum over query rows of the candidate count p+1 (keys each row scores)."""
+    n = w.n_q if n_rows is None else n_rows
+    a = w.q_start + 1
+    return w.batch * (n * a + n * (n - 1) // 2)
+
+
+def gathered_rows(w):
+    """sum over query rows of min(k, p+1): latent rows each row attends over."""
+    tot = 0
+    k = w.k
+    lo, hi = w.q_start + 1, w.q_start + w.n_q          # candidate counts of first/last row
+    if hi <= k:
+        tot = (lo + hi) * w.n_q // 2
+    elif lo >= k:
+        tot = k * w.n_q
+    else:
+        m = k - lo + 1                                   # rows with count <= k
+        tot = (lo + k) * m // 2 + k * (w.n_q - m)
+    return w.batch * tot
+
+
+class Inputs:
+    """Device inputs for every layer of the workload (generated, then kept resident)."""
+
+    def __init__(self, w, synth, torch, all_full: bool, step: int = 0):
+        self.w = w
+        dev = "cuda"
+        n = w.n_layers
+        self.ix = []
+        for l in range(n):
+            if w.roles[l] == "F" or all_full:
+                q, wt = synth.indexer_queries(w, dev, l, step)
+                keys, scale = synth.indexer_keys(w, dev, l)
+                self.ix.append(dict(q=q, w=wt, keys=keys, k_scale=scale))
+            else:
+                self.ix.append(None)
+        self.attn = []
+        for l in range(n):
+            self.attn.append(dict(q=synth.attn_queries(w, dev, l, step), kv=synth.latent_kv(w, dev, l),
+                                  out=torch.empty((w.batch, w.n_q, w.q_heads, w.d_v), dtype=torch.bfloat16,
+                                                  device=dev)))
+        self.idx_fs = torch.empty((w.roles.count("F"), w.batch, w.n_q, w.k), dtype=torch.int32, device=dev)
+        self.idx_ff = torch.empty((n, w.batch, w.n_q, w.k), dtype=torch.int32, device=dev) if all_full else None
+
+
+def event_time(torch, fn, reps):
+    """Average ms of fn() over reps runs, timed with events on the current
+    stream (the stream every library call enqueues on)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(w, inp, torch, rows, np_threads):
+    """Time the CPU oracle on the sampled rows of this workload and
+    extrapolate to the whole step with the per-row cost model (indexer and
+    top-k ~ candidates per row, attention ~ min(k, candidates))."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dsa_oracle as O
+
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    host = {}
+    for l in range(w.n_layers):
+        a = inp.attn[l]
+        host[l] = dict(Q=bits(a["q"][:, rows]), KV=bits(a["kv"]))
+        if w.roles[l] == "F":
+            e = inp.ix[l]
+            kb = bits(e["keys"]) if e["keys"].dtype == torch.bfloat16 else e["keys"].view(torch.uint8).cpu().numpy()
+            host[l].update(q=bits(e["q"][:, rows]), w=e["w"][:, rows].cpu().numpy(), keys=kb,
+                           kd="bf16" if e["keys"].dtype == torch.bfloat16 else "fp8",
+                           scale=None if e["k_scale"] is None else e["k_scale"].cpu().numpy())
+    sm = 1.0 / math.sqrt(w.d_qk)
+    t_ix = t_at = 0.0
+    idx_oracle, outs = [], []
+    cur = None
+    with threadpool_limits(limits=np_threads):
+        for l in range(w.n_layers):
+            h = host[l]
+            if w.roles[l] == "F":
+                t0 = time.perf_counter()
+                # rows are passed with their absolute positions via q_start + t
+                res = np.stack([O.indexer_topk(h["q"][:, i:i + 1], h["w"][:, i:i + 1], h["keys"], h["kd"],
+                                               h["scale"], w.q_start + t, w.kv_len, w.k)[:, 0]
+                                for i, t in enumerate(rows)], axis=1)
+                t_ix += time.perf_counter() - t0
+                idx_oracle.append(res)
+                cur = inp.idx_fs[len(idx_oracle) - 1][:, rows].cpu().numpy()   # attention is checked given the GPU's indices
+            t0 = time.perf_counter()
+            o, _ = O.sparse_attention(h["Q"], h["KV"], cur, w.kv_len, sm, w.d_v)
+            t_at += time.perf_counter() - t0
+            outs.append(o)
+    n_f = w.roles.count("F")
+    samp_pairs = sum(w.q_start + t + 1 for t in rows) * w.batch
+    samp_rows = sum(min(w.k, w.q_start + t + 1) for t in rows) * w.batch
+    full_ix = t_ix * causal_pairs(w) / samp_pairs
+    full_at = t_at * gathered_rows(w) / samp_rows
+    return dict(t_ix=t_ix, t_at=t_at, full_s=full_ix + full_at, idx=idx_oracle, O=outs,
+                n_f=n_f, samp_rows=len(rows))
+
+
+def sampled_parity(w, inp, rows, cb, torch):
+    """GPU vs oracle on the sampled rows: index-set overlap per full layer and
+    max-abs error of every layer's output given the GPU's indices."""
+    import numpy as np
+
+    ovl = []
+    for f, ref in enumerate(cb["idx"]):
+        got = inp.idx_fs[f][:, rows].cpu().numpy()
+        inter = tot = 0
+        for g, r in zip(got.reshape(-1, w.k), ref.reshape(-1, w.k)):
+            sr = set(r[r >= 0].tolist())
+            inter += len(set(g[g >= 0].tolist()) & sr)
+            tot += len(sr)
+        ovl.append(inter / max(tot, 1))
+    err = max(float(np.abs(inp.attn[l]["out"][:, rows].float().cpu().numpy() - cb["O"][l]).max())
+              for l in range(w.n_layers))
+    return {"rows": len(rows), "idx_overlap_min": min(ovl), "attn_max_abs_err": err,
+            "ok": min(ovl) >= 0.999 and err <= 2e-2}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="l128k", choices=sorted(CONFIGS))
+    ap.add_argument("--kernel-reps", type=int, default=3)
+    ap.add_argument("--sample-rows", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-full", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "the DSA group path runs on exactly one GPU; it has no multi-GPU "
+                          "mode, so --gpus must be 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ix_synth as synth
+    import long_context_sparse_ix_amd as ix
+
+    if not os.path.exists(ix.LIB_PATH):
+        from long_context_sparse_ix_amd import build
+        build.build()
+    ix.load()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[CONFIGS[args.config]]
+    if w.decode_steps:
+        return bench_decode(args, w, torch, synth, ix)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log(f"workload {w.name}: generating inputs")
+    inp = Inputs(w, synth, torch, all_full=not args.no_all_full)
+    torch.cuda.synchronize()
+    fs_mask = w.f_mask
+
+    def run_group(mask, idx):
+        ix.ix_group_forward(inp.ix, inp.attn, mask, idx, q_start=w.q_start, kv_len=w.kv_len)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        run_group(fs_mask, inp.idx_fs)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        run_group(fs_mask, inp.idx_fs)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    n_groups = w.n_layers // 4
+    tok_per_group = w.batch * w.n_q / (ms_step / n_groups / 1e3)
+
+    log("per-kernel timing")
+    e = inp.ix[0]
+    idx0 = inp.idx_fs[0]
+    ix_ms = event_time(torch, lambda: ix.ix_indexer_topk(e["q"], e["w"], e["keys"], idx0, k_scale=e["k_scale"],
+                                                         q_start=w.q_start, kv_len=w.kv_len), args.kernel_reps)
+    a = inp.attn[1]
+    at_ms = event_time(torch, lambda: ix.ix_sparse_attn(a["q"], a["kv"], idx0, a["out"], q_start=w.q_start,
+                                                        kv_len=w.kv_len), args.kernel_reps)
+    ix_flop = causal_pairs(w) * 2 * w.ix_heads * w.ix_dim
+    ix_tflops = ix_flop / (ix_ms / 1e3) / 1e12
+    g_rows = gathered_rows(w)
+    at_bytes = g_rows * w.d_qk * 2
+    at_gbps = at_bytes / (at_ms / 1e3) / 1e9
+    at_flop = g_rows * w.q_heads * 2 * (w.d_qk + w.d_v)
+
+    allf_ms = None
+    if not args.no_all_full:
+        log("all-full baseline")
+        allf_mask = (1 << w.n_layers) - 1
+        allf_ms = event_time(torch, lambda: run_group(allf_mask, inp.idx_ff), 1)
+        # all-F baseline re-ran the F layers' slots; restore the F+3S indices
+        run_group(fs_mask, inp.idx_fs)
+        torch.cuda.synchronize()
+
+    rows = synth.sample_rows(w, args.sample_rows)
+    result_cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle on {len(rows)} sampled rows")
+        cores = min(16, len(os.sched_getaffinity(0)))
+        cb = cpu_baseline(w, inp, torch, rows, cores)
+        n_tokens = w.batch * w.n_q
+        cpu_tok = n_tokens / (cb["full_s"] / n_groups)
+        result_cpu = {"value": cpu_tok, "unit": "tokens/s per group", "cores": cores, "kind": "oracle",
+                      "sample": f"{len(rows)} query rows of {w.n_q} (all {w.n_layers} layers; indexer on "
+                                f"{cb['n_f']} full layers) timed {cb['t_ix'] + cb['t_at']:.1f}s, extrapolated "
+                                f"by rows' candidate counts (indexer) and min(k, candidates) (attention)"}
+        parity = sampled_parity(w, inp, rows, cb, torch)
+
+    out = {
+        "metric": "prefill tokens/s per 4-layer F,S,S,S group at L=128K; indexer TFLOP/s; HBM %"
+        if w.name == synth.L128K.name else f"prefill tokens/s per 4-layer F,S,S,S group ({w.name})",
+        "value": tok_per_group, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, on device)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.kv_len, "query_rows": w.n_q,
+                   "q_start": w.q_start, "roles": w.roles, "k": w.k,
+                   "indexer": f"{w.ix_heads} heads x {w.ix_dim}, {w.key_dtype} keys",
+                   "attention": f"{w.q_heads} heads over 1 latent head {w.d_qk} (V = first {w.d_v})"},
+        "roofline": {"bound": "hbm", "achieved": at_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": at_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "sparse_attn_kernel (gathered latent bytes per launch / launch time)"},
+        "indexer": {"ms": ix_ms, "tflops": ix_tflops, "frac_bf16_peak": ix_tflops / PEAK_BF16_TFLOPS,
+                    "frac_fp8_peak": ix_tflops / PEAK_FP8_TFLOPS, "flop": ix_flop,
+                    "note": "fused score + streaming top-k, incl. fp8->bf16 key upcast"},
+        "attention": {"ms_per_layer": at_ms, "tokens_per_s": w.batch * w.n_q / (at_ms / 1e3),
+                      "gathered_GBps": at_gbps, "frac_hbm_peak": at_gbps / PEAK_HBM_GBPS,
+                      "tflops": at_flop / (at_ms / 1e3) / 1e12},
+        "group": {"ms_fsss": ms_step / n_groups, "ms_all_full": None if allf_ms is None else allf_ms / n_groups,
+                  "speedup_vs_all_full": None if allf_ms is None else allf_ms / ms_step},
+        "cpu_baseline": result_cpu,
+        "parity": parity,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bench_decode(args, w, torch, synth, ix):
+    """Decode: each step appends one token to each of B sequences and runs one
+    full+3 shared layer group for the new query rows."""
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log(f"workload {w.name}: generating caches")
+    dev = "cuda"
+    keys, scale = synth.indexer_keys(w, dev, 0)
+    kvs = [synth.latent_kv(w, dev, l) for l in range(4)]
+    total = args.warmup + args.steps
+    steps = []
+    for j in range(total):
+        q, wt = synth.indexer_queries(w, dev, 0, j)
+        att = [dict(q=synth.attn_queries(w, dev, l, j), kv=kvs[l],
+                    out=torch.empty((w.batch, 1, w.q_heads, w.d_v), dtype=torch.bfloat16, device=dev))
+               for l in range(4)]
+        steps.append(([dict(q=q, w=wt, keys=keys, k_scale=scale), None, None, None], att))
+    idx = torch.empty((1, w.batch, 1, w.k), dtype=torch.int32, device=dev)
+
+    def run(j, mask=1):
+        ixl, att = steps[j]
+        if mask != 1:
+            ixl = [ixl[0]] * 4
+        ix.ix_group_forward(ixl, att, mask, idx if mask == 1 else idx_ff, q_start=w.q_start + j,
+                            kv_len=w.kv_len + j)
+
+    idx_ff = torch.empty((4, w.batch, 1, w.k), dtype=torch.int32, device=dev)
+    for j in range(args.warmup):
+        run(j)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for j in range(args.warmup, total):
+        run(j)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    allf = event_time(torch, lambda: run(args.warmup, mask=0xF), 2)
+    key_bytes = w.batch * (w.kv_len + args.warmup) * (w.ix_dim + 4)
+    out = {"metric": "decode tokens/s (B=32, 200K context, one F,S,S,S group per step)",
+           "value": w.batch / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, on device)",
+           "config": {"workload": w.name, "batch": w.batch, "context": w.kv_len, "k": w.k},
+           "group": {"ms_fsss": ms, "ms_all_full": allf, "speedup_vs_all_full": allf / ms},
+           "indexer_key_GBps_lower_bound": key_bytes / (ms / 1e3) / 1e9}
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
