@@ -14,20 +14,27 @@
 //   * one workgroup = 4 waves = 4 consecutive query rows (one row per wave);
 //     row blocks are issued longest-first so the causal triangle drains evenly;
 //   * keys stream through LDS in 64-key bf16 tiles (double-buffered, one
-//     barrier per tile) shared by the 4 rows;
-//   * each wave keeps its row's 64 heads x d query slice in VGPRs as the MFMA
-//     A operand (M = heads) and reads key tiles as the B operand (N = keys):
-//     v_mfma_f32_32x32x16_bf16, output lane l holds key l%32 and 16 heads;
-//   * epilogue: ReLU, head weight, sum over the lane's heads, then one
-//     permlane32 swap + add finishes the head sum and leaves lane l holding the
-//     score of key (tile start + l);
+//     barrier per tile) shared by the 4 rows; the next tile's global loads are
+//     in flight while the current one is consumed;
+//   * each wave keeps its row's heads x d query slice in VGPRs as the MFMA A
+//     operand (M = heads) and reads key tiles as the B operand (N = keys):
+//     v_mfma_f32_32x32x16_bf16, output lane l holds key l%32 and 16 heads.
+//     All B operands of a tile are read from LDS before its first MFMA;
+//   * software pipeline: while tile i's MFMAs run, the VALU finishes tile
+//     i-1 (ReLU, head weight, sum over the lane's heads; one permlane32 swap +
+//     add completes the head sum and leaves lane l with the score of key
+//     tile_start + l), so the epilogue hides under the matrix pipe;
 //   * streaming top-k per row: a strict "score > tau" filter appends survivors
-//     to a wave-private LDS candidate buffer (kept in ascending position
-//     order); when it nears capacity a wave-level radix select finds the
-//     exact k-th best (score desc, position asc), a stable compaction keeps
-//     exactly k, and tau becomes the k-th score.  Because keys arrive in
-//     ascending position, a later key tying tau always loses the tie, so the
-//     strict filter is exact.
+//     to a wave-private LDS candidate buffer kept in ascending position order.
+//     When any row of the workgroup nears capacity, every row compacts at the
+//     same barrier (one stall per workgroup, not one per row): one histogram
+//     pass over the buffer's key range finds a bin edge T with at least k
+//     entries >= T, entries below T are dropped and tau becomes T.  Because
+//     keys arrive in ascending position, a later key tying tau always loses the
+//     tie, so the strict filter is exact.  If a bin is too crowded (many equal
+//     scores) the exact select below is used instead;
+//   * at the end an exact radix select (score desc, position asc) picks the k
+//     winners and a stable pass writes their positions in ascending order.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -44,37 +51,79 @@ struct Thresh {
   int need;     // how many entries with key == v belong to the top k
 };
 
-// Exact k-th best among cs[0..cnt) (wave-private LDS, cnt >= k >= 1) by a
-// 4-pass, 8-bit radix select on the order keys.
-__device__ Thresh wave_select_kth(const float* cs, int cnt, int k, uint32_t* hist) {
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+  return v;
+}
+
+// Smallest and largest order key in cs[0..cnt).
+__device__ __forceinline__ void wave_key_range(const float* cs, int cnt, uint32_t& lo, uint32_t& hi) {
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+  for (int i = lane_id(); i < cnt; i += kWave) {
+    const uint32_t key = order_key(cs[i]);
+    a = min(a, key);
+    b = max(b, key);
+  }
+  lo = wave_min_u32(a);
+  hi = wave_max_u32(b);
+}
+
+// Histogram of rel = key - lo over 256 bins (bin = (rel >> shift) & 255 for
+// entries whose rel matches `prefix` above the digit) and the bin holding the
+// kk-th largest entry.  Returns the bin; `above` = entries in higher bins,
+// `in_bin` = entries in the bin.
+__device__ int wave_hist_pick(const float* cs, int cnt, uint32_t lo, int shift, uint32_t pmask,
+                              uint32_t prefix, int kk, uint32_t* hist, int& above, int& in_bin) {
   const int l = lane_id();
+  *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
+  wave_lds_sync();
+  for (int i = l; i < cnt; i += kWave) {
+    const uint32_t rel = order_key(cs[i]) - lo;
+    if ((rel & pmask) == prefix) atomicAdd(&hist[(rel >> shift) & 255u], 1u);
+  }
+  wave_lds_sync();
+  const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
+  const uint32_t tot = h.x + h.y + h.z + h.w;
+  const int a3 = (int)(wave_suffix_sum(tot) - tot);   // entries in higher lanes' bins
+  const int a2 = a3 + (int)h.w, a1 = a2 + (int)h.z, a0 = a1 + (int)h.y;
+  int bin = -1, ab = 0, cb = 0;
+  if (a3 < kk && kk <= a2) { bin = 4 * l + 3; ab = a3; cb = (int)h.w; }
+  else if (a2 < kk && kk <= a1) { bin = 4 * l + 2; ab = a2; cb = (int)h.z; }
+  else if (a1 < kk && kk <= a0) { bin = 4 * l + 1; ab = a1; cb = (int)h.y; }
+  else if (a0 < kk && kk <= a0 + (int)h.x) { bin = 4 * l; ab = a0; cb = (int)h.x; }
+  const uint64_t m = __ballot(bin >= 0);
+  const int src = __ffsll((unsigned long long)m) - 1;
+  above = __shfl(ab, src);
+  in_bin = __shfl(cb, src);
+  return __shfl(bin, src);
+}
+
+__device__ __forceinline__ int range_bits8(uint32_t range) {   // bit length rounded up to 8
+  const int nbits = range == 0u ? 0 : 32 - __clz((int)range);
+  return (nbits + 7) & ~7;
+}
+
+// Exact k-th best among cs[0..cnt) (cnt >= k >= 1): radix select on the key
+// offsets from the buffer minimum, 8 bits per pass from the top of the range.
+__device__ Thresh wave_select_kth(const float* cs, int cnt, int k, uint32_t* hist) {
+  uint32_t lo, hi;
+  wave_key_range(cs, cnt, lo, hi);
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
-    wave_lds_sync();
-    for (int i = l; i < cnt; i += kWave) {
-      const uint32_t key = order_key(cs[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    wave_lds_sync();
-    const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
-    const uint32_t tot = h.x + h.y + h.z + h.w;
-    const int a3 = (int)(wave_suffix_sum(tot) - tot);   // entries in higher lanes' bins
-    const int a2 = a3 + (int)h.w, a1 = a2 + (int)h.z, a0 = a1 + (int)h.y;
-    int bin = -1, above = 0;
-    if (a3 < kk && kk <= a2) { bin = 4 * l + 3; above = a3; }
-    else if (a2 < kk && kk <= a1) { bin = 4 * l + 2; above = a2; }
-    else if (a1 < kk && kk <= a0) { bin = 4 * l + 1; above = a1; }
-    else if (a0 < kk && kk <= a0 + (int)h.x) { bin = 4 * l; above = a0; }
-    const uint64_t m = __ballot(bin >= 0);
-    const int src = __ffsll((unsigned long long)m) - 1;
-    const int b = __shfl(bin, src);
-    kk -= __shfl(above, src);
+  for (int shift = range_bits8(hi - lo) - 8; shift >= 0; shift -= 8) {
+    int above, in_bin;
+    const int b = wave_hist_pick(cs, cnt, lo, shift, pmask, prefix, kk, hist, above, in_bin);
+    kk -= above;
     prefix |= (uint32_t)b << shift;
     pmask |= 0xFFu << shift;
   }
-  return Thresh{prefix, kk};
+  return Thresh{lo + prefix, kk};
 }
 
 // Stable in-place compaction: keeps entries with key > t.v and the first
@@ -106,6 +155,78 @@ __device__ int wave_compact(float* cs, int* cp, int cnt, Thresh t) {
   return out;
 }
 
+// Buffer compaction during the stream, in the score-value domain.  One
+// histogram over [lo, hi] (lo: a lower bound of every entry, hi: the largest
+// entry) gives the bin b holding the k-th best; every entry in bins >= b is
+// kept.  The bin map is monotone in the score, so the kept set is {s >= s*}
+// with at least k members: the k-th best is >= s*, nothing below s* can win,
+// and a later key equal to s* loses the position tie, so tau = s* keeps the
+// strict filter exact.  A crowded bin (ties, or a range too wide to split)
+// falls back to the exact select.
+__device__ void wave_shrink(float* cs, int* cp, int& cnt, float& tau, float hi, int k, int keep_max,
+                            uint32_t* hist) {
+  const int l = lane_id();
+  float lo = tau;
+  if (lo == -INFINITY) {                       // first shrink: entries may be anything
+    float a = INFINITY;
+    for (int i = l; i < cnt; i += kWave) a = fminf(a, cs[i]);
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) a = fminf(a, __shfl_xor(a, dd));
+    lo = a;
+  }
+  const float inv = 256.0f / (hi - lo);
+  if (hi > lo && inv > 0.0f && inv < INFINITY) {
+    *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
+    wave_lds_sync();
+    for (int i = l; i < cnt; i += kWave) {
+      const int bin = min(255, max(0, (int)((cs[i] - lo) * inv)));
+      atomicAdd(&hist[bin], 1u);
+    }
+    wave_lds_sync();
+    const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
+    const uint32_t tot = h.x + h.y + h.z + h.w;
+    const int a3 = (int)(wave_suffix_sum(tot) - tot);
+    const int a2 = a3 + (int)h.w, a1 = a2 + (int)h.z, a0 = a1 + (int)h.y;
+    int bin = -1, kept = 0;
+    if (a3 < k && k <= a2) { bin = 4 * l + 3; kept = a2; }
+    else if (a2 < k && k <= a1) { bin = 4 * l + 2; kept = a1; }
+    else if (a1 < k && k <= a0) { bin = 4 * l + 1; kept = a0; }
+    else if (a0 < k && k <= a0 + (int)h.x) { bin = 4 * l; kept = a0 + (int)h.x; }
+    const uint64_t mb = __ballot(bin >= 0);
+    const int src = __ffsll((unsigned long long)mb) - 1;
+    const int b = __shfl(bin, src);
+    if (__shfl(kept, src) <= keep_max) {
+      int out = 0;
+      float smin = INFINITY;
+      for (int base = 0; base < cnt; base += kWave) {
+        const int i = base + l;
+        const bool in = i < cnt;
+        const float sc = in ? cs[i] : 0.0f;
+        const int ps = in ? cp[i] : 0;
+        const bool keep = in && min(255, max(0, (int)((sc - lo) * inv))) >= b;
+        const uint64_t km = __ballot(keep);
+        wave_lds_sync();
+        if (keep) {
+          const int o = out + wave_prefix(km);
+          cs[o] = sc;
+          cp[o] = ps;
+          smin = fminf(smin, sc);
+        }
+        out += __popcll(km);
+      }
+#pragma unroll
+      for (int dd = 32; dd >= 1; dd >>= 1) smin = fminf(smin, __shfl_xor(smin, dd));
+      wave_lds_sync();
+      cnt = out;
+      tau = smin;
+      return;
+    }
+  }
+  const Thresh th = wave_select_kth(cs, cnt, k, hist);
+  cnt = wave_compact(cs, cp, cnt, th);
+  tau = key_value(th.v);
+}
+
 // Same selection as wave_compact, but writes the kept positions to `dst`.
 __device__ void wave_emit(const float* cs, const int* cp, int cnt, Thresh t, int32_t* dst) {
   const int l = lane_id();
@@ -131,16 +252,62 @@ struct TileGeom {
   static constexpr int tile_bytes = kTileKeys * row_bytes;
   static constexpr int chunks = kTileKeys * d / 8;    // 16-byte pieces per tile
   static constexpr int per_thread = (chunks + kThreads - 1) / kThreads;
+  static constexpr bool exact_split = chunks % kThreads == 0;
 };
 
-template <int HT, int KS>
+// One half-tile block: the MFMAs of key half `nt` of the current tile into
+// acc[nt] and/or the epilogue of the other accumulator half (`ep`), in one
+// basic block so the scheduler can put the VALU work between MFMAs.  Returns
+// the partial (this lane's 16 x HT heads) score of the epilogue half.
+template <int HT, int KS, bool MMA, bool EPI>
+__device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const float (&wr)[HT][16],
+                                            const unsigned char* kb, int nt, int m, int hf,
+                                            f32x16 (&acc_mma)[HT], const f32x16 (&acc_epi)[HT]) {
+  using G = TileGeom<KS>;
+  constexpr int d = G::d;
+  if constexpr (MMA) {
+    bf16x8 bfr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + (nt * 32 + m) * G::row_bytes + hf * d + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc_mma[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[ks],
+                                                              ks == 0 ? f32x16{} : acc_mma[ht], 0, 0, 0);
+  }
+  float part = 0.0f;
+  if constexpr (EPI) {
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // 4 independent chains
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r & 3] = fmaf(wr[ht][r], fmaxf(acc_epi[ht][r], 0.0f), s[r & 3]);
+    part = (s[0] + s[1]) + (s[2] + s[3]);
+  }
+  if constexpr (MMA && EPI) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // ds_read
+#pragma unroll
+    for (int i = 0; i < HT * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                          // 4 VALU
+    }
+  }
+  return part;
+}
+
+template <int HT, int KS, bool SCALE>
 __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedArgs a) {
   using G = TileGeom<KS>;
   constexpr int d = G::d;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* key_lds0 = smem;
-  float* scale_lds = reinterpret_cast<float*>(smem + 2 * G::tile_bytes);      // [2][64]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(scale_lds + 2 * kTileKeys);    // [4][256]
+  unsigned char* key_lds0 = smem;                                                   // [2][tile]
+  float* scale_lds = reinterpret_cast<float*>(smem + 2 * G::tile_bytes);           // [2][64]
+  int* need_flags = reinterpret_cast<int*>(scale_lds + 2 * kTileKeys);             // [2][4]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(need_flags + 8);                    // [4][256]
+  float* cand = reinterpret_cast<float*>(hist + kRowsPerWG * 256);                 // [4][2C]
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int m = l & 31, hf = l >> 5;
@@ -148,13 +315,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   const int row0 = (gridDim.x - 1 - blockIdx.x) * kRowsPerWG;
   const int t = row0 + wave;
   const bool row_ok = t < a.n_q;
-  const int64_t p = a.q_start + (row_ok ? t : 0);
+  const int p = (int)a.q_start + (row_ok ? t : 0);              // positions fit in int32
   const int last_row = min(row0 + kRowsPerWG - 1, a.n_q - 1);
-  const int64_t n_keys = a.q_start + last_row + 1;
-  const int n_tiles = (int)((n_keys + kTileKeys - 1) / kTileKeys);
-
-  float* cs = reinterpret_cast<float*>(hist + kRowsPerWG * 256) + (size_t)wave * 2 * a.C;
-  int* cp = reinterpret_cast<int*>(cs + a.C);
+  const int n_keys = (int)a.q_start + last_row + 1;
+  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int C = a.C;
+  float* cs = cand + (size_t)wave * 2 * C;
+  int* cp = reinterpret_cast<int*>(cs + C);
   uint32_t* my_hist = hist + wave * 256;
 
   // Query slice (A operand): lane (m, hf) holds head ht*32+m, elements
@@ -169,13 +336,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       const int h = ht * 32 + m;
       const bool ok = row_ok && h < a.H;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ok) {
-          qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks);
-        } else {
-          qf[ht][ks] = bf16x8{};
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ht][ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks)
+                        : bf16x8{};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hh = ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);   // MFMA output row of acc[r]
@@ -185,23 +348,22 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   }
 
   const uint16_t* keys_b = a.keys + (int64_t)b * a.key_bstride;
-  const float* scale_b = a.scale ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
+  const float* scale_b = SCALE ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
 
+  // tile loads: thread tid moves 16-byte pieces c = tid + j*256 (row c/(d/8),
+  // column c%(d/8)); rows past the last key are clamped (and masked later)
   u32x4 pre[G::per_thread];
   float pre_scale = 1.0f;
   auto load_tile = [&](int it) {
-    const int64_t s0 = (int64_t)it * kTileKeys;
+    const int s0 = it * kTileKeys;
 #pragma unroll
     for (int j = 0; j < G::per_thread; ++j) {
       const int c = tid + j * kThreads;
-      const int r = c / (d / 8), col = c % (d / 8);
-      if (c < G::chunks && s0 + r < n_keys) {
-        pre[j] = *reinterpret_cast<const u32x4*>(keys_b + (s0 + r) * d + col * 8);
-      } else {
-        pre[j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int r = min(s0 + c / (d / 8), n_keys - 1), col = c % (d / 8);
+      if (G::exact_split || c < G::chunks)
+        pre[j] = *reinterpret_cast<const u32x4*>(keys_b + (int64_t)r * d + col * 8);
     }
-    if (tid < kTileKeys) pre_scale = (scale_b && s0 + tid < n_keys) ? scale_b[s0 + tid] : 1.0f;
+    if (SCALE && tid < kTileKeys) pre_scale = scale_b[min(s0 + tid, n_keys - 1)];
   };
   auto store_tile = [&](int buf) {
     unsigned char* dst = key_lds0 + buf * G::tile_bytes;
@@ -209,73 +371,70 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
     for (int j = 0; j < G::per_thread; ++j) {
       const int c = tid + j * kThreads;
       const int r = c / (d / 8), col = c % (d / 8);
-      if (c < G::chunks) *reinterpret_cast<u32x4*>(dst + r * G::row_bytes + col * 16) = pre[j];
+      if (G::exact_split || c < G::chunks) *reinterpret_cast<u32x4*>(dst + r * G::row_bytes + col * 16) = pre[j];
     }
-    if (tid < kTileKeys) scale_lds[buf * kTileKeys + tid] = pre_scale;
+    if (SCALE && tid < kTileKeys) scale_lds[buf * kTileKeys + tid] = pre_scale;
   };
 
-  float tau = -INFINITY;
+  float tau = -INFINITY, vmax = -INFINITY;
   int cnt = 0;
+  const int keep_max = C - 2 * kWave;          // after a shrink the next trigger is >= 64 appends away
+  float sc_prev = 1.0f;
+  float part0 = 0.0f;                           // nt=0 partial score of the tile being finished
 
   load_tile(0);
   store_tile(0);
+  if (tid < 8) need_flags[tid] = 0;
   __syncthreads();
 
-  for (int it = 0; it < n_tiles; ++it) {
+  f32x16 acc0[HT], acc1[HT];
+  for (int it = 0; it <= n_tiles; ++it) {
     const int buf = it & 1;
+    const bool mma = row_ok && it < n_tiles && it * kTileKeys <= p;
+    const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
+    const unsigned char* kb = key_lds0 + buf * G::tile_bytes;
+    const float sc_cur = SCALE ? scale_lds[buf * kTileKeys + l] : 1.0f;
+    const int* nf = need_flags + (buf ^ 1) * 4;          // flags of the previous step
+    const int flags = (nf[0] | nf[1] | nf[2] | nf[3]);
     if (it + 1 < n_tiles) load_tile(it + 1);
-    const int64_t s0 = (int64_t)it * kTileKeys;
-    if (row_ok && s0 <= p) {
-      const unsigned char* kb = key_lds0 + buf * G::tile_bytes;
-      f32x16 acc[2][HT];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[nt][ht] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 bfr[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          bfr[nt] = *reinterpret_cast<const bf16x8*>(kb + (nt * 32 + m) * G::row_bytes + hf * d + 16 * ks);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-            acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt], acc[nt][ht], 0, 0, 0);
-      }
-      float part[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float s = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), s);
-        part[nt] = s;
-      }
-      // lanes 0-31: key tile 0 (own half + partner half); lanes 32-63: tile 1.
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
-                                                       __float_as_uint(part[1]), false, false);
+
+    // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
+    float part1 = 0.0f;
+    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, kb, 0, m, hf, acc0, acc1);
+    else if (mma) half_block<HT, KS, true, false>(qf, wr, kb, 0, m, hf, acc0, acc1);
+    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, kb, 0, m, hf, acc0, acc1);
+
+    if (epi) {
+      // finish tile it-1: lanes 0-31 take key half 0, lanes 32-63 half 1
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1),
+                                                       false, false);
       float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      score *= scale_lds[buf * kTileKeys + l];
-      const int64_t s = s0 + l;
+      if (SCALE) score *= sc_prev;
+      const int s = (it - 1) * kTileKeys + l;
       if (s > p) score = -INFINITY;
+      if (flags && cnt > a.k + (C - a.k) / 2) {      // some row of the block is nearly full
+        wave_lds_sync();
+        wave_shrink(cs, cp, cnt, tau, vmax, a.k, keep_max, my_hist);
+      }
       const bool pass = score > tau;
       const uint64_t pm = __ballot(pass);
-      if (pass) {
-        const int o = cnt + wave_prefix(pm);
-        cs[o] = score;
-        cp[o] = (int)s;
-      }
-      cnt += __popcll(pm);
-      if (cnt > a.C - kWave) {
-        wave_lds_sync();
-        const Thresh th = wave_select_kth(cs, cnt, a.k, my_hist);
-        cnt = wave_compact(cs, cp, cnt, th);
-        tau = key_value(th.v);
+      if (pm) {
+        if (pass) {
+          const int o = cnt + wave_prefix(pm);
+          cs[o] = score;
+          cp[o] = s;
+        }
+        cnt += __popcll(pm);
+        float mx = pass ? score : -INFINITY;
+#pragma unroll
+        for (int dd = 32; dd >= 1; dd >>= 1) mx = fmaxf(mx, __shfl_xor(mx, dd));
+        vmax = fmaxf(vmax, mx);
       }
     }
+    // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
+    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, kb, 1, m, hf, acc1, acc0);
+    sc_prev = sc_cur;
+    if (l == 0) need_flags[buf * 4 + wave] = (row_ok && cnt > C - kWave) ? 1 : 0;
     if (it + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -310,34 +469,39 @@ __global__ void upcast_fp8_kernel(const uint8_t* __restrict__ src, int64_t src_b
     r = e4m3x4_to_bf16x4(v.y); o0.z = r.x; o0.w = r.y;
     r = e4m3x4_to_bf16x4(v.z); o1.x = r.x; o1.y = r.y;
     r = e4m3x4_to_bf16x4(v.w); o1.z = r.x; o1.w = r.y;
-    u32x4* d = reinterpret_cast<u32x4*>(dst + b * dst_bstride + off);
-    d[0] = o0;
-    d[1] = o1;
+    u32x4* dd = reinterpret_cast<u32x4*>(dst + b * dst_bstride + off);
+    dd[0] = o0;
+    dd[1] = o1;
   }
+}
+
+template <int HT, int KS, bool SCALE>
+hipError_t launch_fused_s(const FusedArgs& a, int B, hipStream_t s) {
+  const size_t lds = fused_lds_bytes(KS * 16, a.C);
+  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((a.n_q + kRowsPerWG - 1) / kRowsPerWG, B);
+  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS, SCALE>), grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int HT, int KS>
 hipError_t launch_fused_t(const FusedArgs& a, int B, hipStream_t s) {
-  const size_t lds = fused_lds_bytes(KS * 16, a.C);
-  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  dim3 grid((a.n_q + kRowsPerWG - 1) / kRowsPerWG, B);
-  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS>), grid, dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return a.scale ? launch_fused_s<HT, KS, true>(a, B, s) : launch_fused_s<HT, KS, false>(a, B, s);
 }
 
 }  // namespace
 
 int fused_candidates(int k) {
-  int extra = k / 2 > kWave ? k / 2 : kWave;
+  int extra = k / 2 > 2 * kWave ? k / 2 : 2 * kWave;
   return ((k + extra + kWave - 1) / kWave) * kWave;
 }
 
 size_t fused_lds_bytes(int d, int C) {
   const size_t tile = (size_t)kTileKeys * (2 * d + 16);
-  return 2 * tile + 2 * kTileKeys * sizeof(float) + kRowsPerWG * 256 * sizeof(uint32_t) +
-         (size_t)kRowsPerWG * C * 8;
+  return 2 * tile + 2 * kTileKeys * sizeof(float) + 8 * sizeof(int) +
+         kRowsPerWG * 256 * sizeof(uint32_t) + (size_t)kRowsPerWG * C * 8;
 }
 
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s) {
