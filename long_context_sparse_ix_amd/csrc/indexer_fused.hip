@@ -166,6 +166,8 @@ __device__ int wave_compact(float* cs, int* cp, int cnt, Thresh t) {
 __device__ void wave_shrink(float* cs, int* cp, int& cnt, float& tau, float hi, int k, int keep_max,
                             uint32_t* hist) {
   const int l = lane_id();
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) hi = fmaxf(hi, __shfl_xor(hi, dd));
   float lo = tau;
   if (lo == -INFINITY) {                       // first shrink: entries may be anything
     float a = INFINITY;
@@ -352,9 +354,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
 
   // tile loads: thread tid moves 16-byte pieces c = tid + j*256 (row c/(d/8),
   // column c%(d/8)); rows past the last key are clamped (and masked later)
-  u32x4 pre[G::per_thread];
-  float pre_scale = 1.0f;
-  auto load_tile = [&](int it) {
+  u32x4 pre0[G::per_thread + 1], pre1[G::per_thread + 1];   // last slot: this thread's key scale
+  auto load_tile = [&](int it, u32x4* pre) {
     const int s0 = it * kTileKeys;
 #pragma unroll
     for (int j = 0; j < G::per_thread; ++j) {
@@ -363,9 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       if (G::exact_split || c < G::chunks)
         pre[j] = *reinterpret_cast<const u32x4*>(keys_b + (int64_t)r * d + col * 8);
     }
-    if (SCALE && tid < kTileKeys) pre_scale = scale_b[min(s0 + tid, n_keys - 1)];
+    if (SCALE && tid < kTileKeys) pre[G::per_thread].x = __float_as_uint(scale_b[min(s0 + tid, n_keys - 1)]);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4* pre) {
     unsigned char* dst = key_lds0 + buf * G::tile_bytes;
 #pragma unroll
     for (int j = 0; j < G::per_thread; ++j) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       const int r = c / (d / 8), col = c % (d / 8);
       if (G::exact_split || c < G::chunks) *reinterpret_cast<u32x4*>(dst + r * G::row_bytes + col * 16) = pre[j];
     }
-    if (SCALE && tid < kTileKeys) scale_lds[buf * kTileKeys + tid] = pre_scale;
+    if (SCALE && tid < kTileKeys) scale_lds[buf * kTileKeys + tid] = __uint_as_float(pre[G::per_thread].x);
   };
 
   float tau = -INFINITY, vmax = -INFINITY;
@@ -382,21 +383,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   float sc_prev = 1.0f;
   float part0 = 0.0f;                           // nt=0 partial score of the tile being finished
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, pre0);
+  store_tile(0, pre0);
+  if (n_tiles > 1) load_tile(1, pre1);
   if (tid < 8) need_flags[tid] = 0;
   __syncthreads();
 
   f32x16 acc0[HT], acc1[HT];
-  for (int it = 0; it <= n_tiles; ++it) {
+  // One pipeline step for tile `it`; `pre_ld` receives tile it+2, `pre_st`
+  // (loaded one step earlier) holds tile it+1.  Unrolled by two below so both
+  // register sets keep static names.
+  auto step = [&](int it, u32x4 (&pre_ld)[G::per_thread + 1], u32x4 (&pre_st)[G::per_thread + 1]) {
     const int buf = it & 1;
     const bool mma = row_ok && it < n_tiles && it * kTileKeys <= p;
     const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
     const unsigned char* kb = key_lds0 + buf * G::tile_bytes;
     const float sc_cur = SCALE ? scale_lds[buf * kTileKeys + l] : 1.0f;
-    const int* nf = need_flags + (buf ^ 1) * 4;          // flags of the previous step
-    const int flags = (nf[0] | nf[1] | nf[2] | nf[3]);
-    if (it + 1 < n_tiles) load_tile(it + 1);
+    const u32x4 nf = *reinterpret_cast<const u32x4*>(need_flags + (buf ^ 1) * 4);   // previous step's
+    if (it + 2 < n_tiles) load_tile(it + 2, pre_ld);
 
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
     float part1 = 0.0f;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       if (SCALE) score *= sc_prev;
       const int s = (it - 1) * kTileKeys + l;
       if (s > p) score = -INFINITY;
-      if (flags && cnt > a.k + (C - a.k) / 2) {      // some row of the block is nearly full
+      if ((nf.x | nf.y | nf.z | nf.w) && cnt > a.k + (C - a.k) / 2) {   // some row is nearly full
         wave_lds_sync();
         wave_shrink(cs, cp, cnt, tau, vmax, a.k, keep_max, my_hist);
       }
@@ -425,18 +429,19 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
           cp[o] = s;
         }
         cnt += __popcll(pm);
-        float mx = pass ? score : -INFINITY;
-#pragma unroll
-        for (int dd = 32; dd >= 1; dd >>= 1) mx = fmaxf(mx, __shfl_xor(mx, dd));
-        vmax = fmaxf(vmax, mx);
+        if (pass) vmax = fmaxf(vmax, score);      // per lane; reduced when a shrink needs it
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
     if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, kb, 1, m, hf, acc1, acc0);
     sc_prev = sc_cur;
     if (l == 0) need_flags[buf * 4 + wave] = (row_ok && cnt > C - kWave) ? 1 : 0;
-    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    if (it + 1 < n_tiles) store_tile(buf ^ 1, pre_st);
     __syncthreads();
+  };
+  for (int it = 0; it <= n_tiles; it += 2) {
+    step(it, pre0, pre1);
+    if (it + 1 <= n_tiles) step(it + 1, pre1, pre0);
   }
 
   if (row_ok) {
