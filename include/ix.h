@@ -65,7 +65,8 @@ typedef enum ix_dtype {
 
 typedef enum ix_indexer_path {
   IX_PATH_AUTO = 0,         /* library picks: fused when there are many rows   */
-  IX_PATH_FUSED = 1,        /* scores streamed straight into the top-k, never stored */
+  IX_PATH_FUSED = 1,        /* scores streamed straight into the top-k, never stored;
+                               needs dim in {16, 32, 64, 128} (else IX_E_SHAPE) */
   IX_PATH_MATERIALIZED = 2  /* one fp32 score row per query in the workspace, then top-k */
 } ix_indexer_path;
 

@@ -46,6 +46,16 @@ constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 4;
 constexpr int kThreads = kRowsPerWG * kWave;
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (direct-to-LDS loads are invisible to the compiler's own waitcnt tracking).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 struct Thresh {
   uint32_t v;   // order key of the k-th best entry
   int need;     // how many entries with key == v belong to the top k
@@ -247,31 +257,34 @@ __device__ void wave_emit(const float* cs, const int* cp, int cnt, Thresh t, int
   }
 }
 
+// Key tile in LDS: 64 rows of d bf16 (CPR = d/8 16-byte chunks per row),
+// unpadded, with chunk c of row r stored in slot c ^ f(r), f(r) = (r / RPB) %
+// CPR where RPB = 16 / CPR rows share one 256-byte bank cycle.  The 16 rows a
+// B-operand read touches then land in 16 distinct bank groups.
 template <int KS>
 struct TileGeom {
   static constexpr int d = KS * 16;
-  static constexpr int row_bytes = 2 * d + 16;        // padded LDS row: conflict-free B reads
+  static constexpr int CPR = d / 8;
+  static constexpr int RPB = 16 / CPR;
+  static constexpr int row_bytes = d * 2;
   static constexpr int tile_bytes = kTileKeys * row_bytes;
-  static constexpr int chunks = kTileKeys * d / 8;    // 16-byte pieces per tile
-  static constexpr int per_thread = (chunks + kThreads - 1) / kThreads;
-  static constexpr bool exact_split = chunks % kThreads == 0;
+  static constexpr int inst_per_wave = CPR >= 4 ? CPR / 4 : 1;      // 16-byte direct loads per wave
+  static constexpr int lanes_per_inst = CPR >= 4 ? 64 : 16 * CPR;
+  static_assert(CPR == 2 || CPR == 4 || CPR == 8 || CPR == 16, "d must be 16, 32, 64 or 128");
+  __device__ static __forceinline__ int swz(int r, int c) { return c ^ ((r / RPB) & (CPR - 1)); }
 };
 
+constexpr int kRing = 3;   // LDS tile buffers: tiles it, it+1 ready/landing, it+2 loading
+
 // One half-tile block: the MFMAs of key half `nt` of the current tile into
-// acc[nt] and/or the epilogue of the other accumulator half (`ep`), in one
+// acc_mma and/or the epilogue of the other accumulator half (acc_epi), in one
 // basic block so the scheduler can put the VALU work between MFMAs.  Returns
 // the partial (this lane's 16 x HT heads) score of the epilogue half.
 template <int HT, int KS, bool MMA, bool EPI>
 __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const float (&wr)[HT][16],
-                                            const unsigned char* kb, int nt, int m, int hf,
-                                            f32x16 (&acc_mma)[HT], const f32x16 (&acc_epi)[HT]) {
-  using G = TileGeom<KS>;
-  constexpr int d = G::d;
+                                            const bf16x8 (&bfr)[KS], f32x16 (&acc_mma)[HT],
+                                            const f32x16 (&acc_epi)[HT]) {
   if constexpr (MMA) {
-    bf16x8 bfr[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + (nt * 32 + m) * G::row_bytes + hf * d + 16 * ks);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -290,8 +303,6 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
   }
   if constexpr (MMA && EPI) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // ds_read
-#pragma unroll
     for (int i = 0; i < HT * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                          // 4 VALU
@@ -300,14 +311,24 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
   return part;
 }
 
+template <int KS>
+__device__ __forceinline__ void read_bfrags(const unsigned char* kb, int nt, int m, int hf, bf16x8 (&bfr)[KS]) {
+  using G = TileGeom<KS>;
+  const int r = nt * 32 + m;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + r * G::row_bytes + G::swz(r, hf * (G::CPR / 2) + ks) * 16);
+}
+
 template <int HT, int KS, bool SCALE>
 __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedArgs a) {
   using G = TileGeom<KS>;
   constexpr int d = G::d;
+  constexpr int kLoads = G::inst_per_wave + (SCALE ? 1 : 0);   // direct loads per wave per tile
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* key_lds0 = smem;                                                   // [2][tile]
-  float* scale_lds = reinterpret_cast<float*>(smem + 2 * G::tile_bytes);           // [2][64]
-  int* need_flags = reinterpret_cast<int*>(scale_lds + 2 * kTileKeys);             // [2][4]
+  unsigned char* key_lds0 = smem;                                                   // [3][tile]
+  float* scale_lds = reinterpret_cast<float*>(smem + kRing * G::tile_bytes);       // [3][64]
+  int* need_flags = reinterpret_cast<int*>(scale_lds + kRing * kTileKeys);         // [2][4]
   uint32_t* hist = reinterpret_cast<uint32_t*>(need_flags + 8);                    // [4][256]
   float* cand = reinterpret_cast<float*>(hist + kRowsPerWG * 256);                 // [4][2C]
 
@@ -352,29 +373,28 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   const uint16_t* keys_b = a.keys + (int64_t)b * a.key_bstride;
   const float* scale_b = SCALE ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
 
-  // tile loads: thread tid moves 16-byte pieces c = tid + j*256 (row c/(d/8),
-  // column c%(d/8)); rows past the last key are clamped (and masked later)
-  u32x4 pre0[G::per_thread + 1], pre1[G::per_thread + 1];   // last slot: this thread's key scale
-  auto load_tile = [&](int it, u32x4* pre) {
+  // Direct HBM -> LDS loads of tile `it` into ring slot `slot`: load j of this
+  // wave fills LDS slots [64J, 64J+64) (J = wave + 4j) in lane order, so lane l
+  // fetches the global chunk that belongs in slot 64J + l.  Rows past the last
+  // key are clamped (their scores are masked).
+  auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
+    unsigned char* tb = key_lds0 + slot * G::tile_bytes;
 #pragma unroll
-    for (int j = 0; j < G::per_thread; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = min(s0 + c / (d / 8), n_keys - 1), col = c % (d / 8);
-      if (G::exact_split || c < G::chunks)
-        pre[j] = *reinterpret_cast<const u32x4*>(keys_b + (int64_t)r * d + col * 8);
+    for (int j = 0; j < G::inst_per_wave; ++j) {
+      const int J = wave + 4 * j;
+      const int S = J * G::lanes_per_inst + l;                 // LDS slot this lane fills
+      const int r = S / G::CPR, sl = S % G::CPR;
+      const int c = G::swz(r, sl);                             // swz is an involution
+      const uint16_t* src = keys_b + (int64_t)min(s0 + r, n_keys - 1) * d + c * 8;
+      if (G::lanes_per_inst == 64 || l < G::lanes_per_inst)
+        __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16, 0, 0);
     }
-    if (SCALE && tid < kTileKeys) pre[G::per_thread].x = __float_as_uint(scale_b[min(s0 + tid, n_keys - 1)]);
-  };
-  auto store_tile = [&](int buf, const u32x4* pre) {
-    unsigned char* dst = key_lds0 + buf * G::tile_bytes;
-#pragma unroll
-    for (int j = 0; j < G::per_thread; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / (d / 8), col = c % (d / 8);
-      if (G::exact_split || c < G::chunks) *reinterpret_cast<u32x4*>(dst + r * G::row_bytes + col * 16) = pre[j];
+    if constexpr (SCALE) {
+      const float* src = scale_b + min(s0 + 16 * wave + (l & 15), n_keys - 1);
+      if (l < 16)
+        __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4, 0, 0);
     }
-    if (SCALE && tid < kTileKeys) scale_lds[buf * kTileKeys + tid] = __uint_as_float(pre[G::per_thread].x);
   };
 
   float tau = -INFINITY, vmax = -INFINITY;
@@ -383,30 +403,37 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   float sc_prev = 1.0f;
   float part0 = 0.0f;                           // nt=0 partial score of the tile being finished
 
-  load_tile(0, pre0);
-  store_tile(0, pre0);
-  if (n_tiles > 1) load_tile(1, pre1);
+  issue_tile(0, 0);
+  if (n_tiles > 1) {
+    issue_tile(1, 1);
+    wait_vmcnt<kLoads>();
+  } else {
+    wait_vmcnt<0>();
+  }
   if (tid < 8) need_flags[tid] = 0;
   __syncthreads();
 
   f32x16 acc0[HT], acc1[HT];
-  // One pipeline step for tile `it`; `pre_ld` receives tile it+2, `pre_st`
-  // (loaded one step earlier) holds tile it+1.  Unrolled by two below so both
-  // register sets keep static names.
-  auto step = [&](int it, u32x4 (&pre_ld)[G::per_thread + 1], u32x4 (&pre_st)[G::per_thread + 1]) {
-    const int buf = it & 1;
+  int slot = 0;                                  // ring slot of tile it
+  for (int it = 0; it <= n_tiles; ++it) {
     const bool mma = row_ok && it < n_tiles && it * kTileKeys <= p;
     const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
-    const unsigned char* kb = key_lds0 + buf * G::tile_bytes;
-    const float sc_cur = SCALE ? scale_lds[buf * kTileKeys + l] : 1.0f;
-    const u32x4 nf = *reinterpret_cast<const u32x4*>(need_flags + (buf ^ 1) * 4);   // previous step's
-    if (it + 2 < n_tiles) load_tile(it + 2, pre_ld);
+    const unsigned char* kb = key_lds0 + slot * G::tile_bytes;
+    const float sc_cur = SCALE ? scale_lds[slot * kTileKeys + l] : 1.0f;
+    const u32x4 nf = *reinterpret_cast<const u32x4*>(need_flags + ((it & 1) ^ 1) * 4);   // previous step's
+    const bool more = it + 2 < n_tiles;
+    if (more) issue_tile(it + 2, slot == 0 ? 2 : slot - 1);   // (slot + 2) % 3
 
+    bf16x8 bx[KS], by[KS];
+    if (mma) {
+      read_bfrags<KS>(kb, 0, m, hf, bx);
+      read_bfrags<KS>(kb, 1, m, hf, by);
+    }
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
     float part1 = 0.0f;
-    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, kb, 0, m, hf, acc0, acc1);
-    else if (mma) half_block<HT, KS, true, false>(qf, wr, kb, 0, m, hf, acc0, acc1);
-    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, kb, 0, m, hf, acc0, acc1);
+    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, bx, acc0, acc1);
+    else if (mma) half_block<HT, KS, true, false>(qf, wr, bx, acc0, acc1);
+    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, bx, acc0, acc1);
 
     if (epi) {
       // finish tile it-1: lanes 0-31 take key half 0, lanes 32-63 half 1
@@ -433,15 +460,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
-    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, kb, 1, m, hf, acc1, acc0);
+    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, by, acc1, acc0);
     sc_prev = sc_cur;
-    if (l == 0) need_flags[buf * 4 + wave] = (row_ok && cnt > C - kWave) ? 1 : 0;
-    if (it + 1 < n_tiles) store_tile(buf ^ 1, pre_st);
+    if (l == 0) need_flags[(it & 1) * 4 + wave] = (row_ok && cnt > C - kWave) ? 1 : 0;
+    if (more) wait_vmcnt<kLoads>();              // tile it+1 landed (it+2 may still fly)
+    else wait_vmcnt<0>();
     __syncthreads();
-  };
-  for (int it = 0; it <= n_tiles; it += 2) {
-    step(it, pre0, pre1);
-    if (it + 1 <= n_tiles) step(it + 1, pre1, pre0);
+    slot = slot == 2 ? 0 : slot + 1;
   }
 
   if (row_ok) {
@@ -504,20 +529,20 @@ int fused_candidates(int k) {
 }
 
 size_t fused_lds_bytes(int d, int C) {
-  const size_t tile = (size_t)kTileKeys * (2 * d + 16);
-  return 2 * tile + 2 * kTileKeys * sizeof(float) + 8 * sizeof(int) +
+  const size_t tile = (size_t)kTileKeys * 2 * d;
+  return kRing * tile + kRing * kTileKeys * sizeof(float) + 8 * sizeof(int) +
          kRowsPerWG * 256 * sizeof(uint32_t) + (size_t)kRowsPerWG * C * 8;
 }
+
+bool fused_dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s) {
   const int HT = a.H > 32 ? 2 : 1;
   const int KS = d / 16;
 #define IX_FUSED_CASE(ht, ks) \
   if (HT == ht && KS == ks) return launch_fused_t<ht, ks>(a, B, s);
-  IX_FUSED_CASE(1, 1) IX_FUSED_CASE(1, 2) IX_FUSED_CASE(1, 3) IX_FUSED_CASE(1, 4)
-  IX_FUSED_CASE(1, 5) IX_FUSED_CASE(1, 6) IX_FUSED_CASE(1, 7) IX_FUSED_CASE(1, 8)
-  IX_FUSED_CASE(2, 1) IX_FUSED_CASE(2, 2) IX_FUSED_CASE(2, 3) IX_FUSED_CASE(2, 4)
-  IX_FUSED_CASE(2, 5) IX_FUSED_CASE(2, 6) IX_FUSED_CASE(2, 7) IX_FUSED_CASE(2, 8)
+  IX_FUSED_CASE(1, 1) IX_FUSED_CASE(1, 2) IX_FUSED_CASE(1, 4) IX_FUSED_CASE(1, 8)
+  IX_FUSED_CASE(2, 1) IX_FUSED_CASE(2, 2) IX_FUSED_CASE(2, 4) IX_FUSED_CASE(2, 8)
 #undef IX_FUSED_CASE
   return hipErrorInvalidValue;
 }

@@ -45,6 +45,7 @@ int32_t check_indexer(const ix_problem* p, const ix_indexer_in* in) {
   if (in->heads < 1 || in->heads > 64 || in->dim < 16 || in->dim > 128 || in->dim % 16 != 0)
     return IX_E_SHAPE;
   if (in->path < IX_PATH_AUTO || in->path > IX_PATH_MATERIALIZED) return IX_E_SHAPE;
+  if (in->path == IX_PATH_FUSED && !ix::fused_dim_supported(in->dim)) return IX_E_SHAPE;
   if (!aligned16(in->q) || !aligned16(in->w) || !aligned16(in->k) ||
       (in->k_scale && !aligned16(in->k_scale)))
     return IX_E_SHAPE;
@@ -67,7 +68,7 @@ int32_t check_attn(const ix_attn_in* in) {
 
 bool use_fused(const ix_problem* p, const ix_indexer_in* in) {
   if (in->path == IX_PATH_FUSED) return true;
-  if (in->path == IX_PATH_MATERIALIZED) return false;
+  if (in->path == IX_PATH_MATERIALIZED || !ix::fused_dim_supported(in->dim)) return false;
   const int64_t rows = (int64_t)p->batch * p->n_q;
   const int64_t score_bytes = rows * p->kv_len * 4;
   return rows >= 128 || score_bytes > ((int64_t)1 << 30);

@@ -20,6 +20,7 @@ struct FusedArgs {
   int n_q, H, k, C;       // C: candidate slots per row (>= k + 64)
 };
 size_t fused_lds_bytes(int d, int C);
+bool fused_dim_supported(int d);   // d in {16, 32, 64, 128}
 int fused_candidates(int k);
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s);
 

@@ -113,7 +113,7 @@ def test_problem_validation(kw, status):
     (dict(k_dtype=7), ix.IX_E_DTYPE), (dict(k_dtype=ix.IX_DTYPE_FP8_E4M3FN), ix.IX_E_NULL),
     (dict(k_scale=DUMMY), ix.IX_E_SHAPE), (dict(heads=65), ix.IX_E_SHAPE),
     (dict(dim=24), ix.IX_E_SHAPE), (dict(dim=144), ix.IX_E_SHAPE), (dict(path=3), ix.IX_E_SHAPE),
-    (dict(q=DUMMY + 8), ix.IX_E_SHAPE),
+    (dict(q=DUMMY + 8), ix.IX_E_SHAPE), (dict(dim=48, path=1), ix.IX_E_SHAPE),
 ])
 def test_indexer_validation(kw, status):
     assert _call_ix(_prob(), _ixr(**kw)) == status
