@@ -11,28 +11,29 @@
 // candidates that can still reach the top k are kept.
 //
 // Layout of the work
-//   * one workgroup = 4 waves = 4 consecutive query rows (one row per wave);
-//     row blocks are issued longest-first so the causal triangle drains evenly;
-//   * keys stream through LDS in 64-key bf16 tiles (double-buffered, one
-//     barrier per tile) shared by the 4 rows; the next tile's global loads are
-//     in flight while the current one is consumed;
-//   * each wave keeps its row's heads x d query slice in VGPRs as the MFMA A
-//     operand (M = heads) and reads key tiles as the B operand (N = keys):
-//     v_mfma_f32_32x32x16_bf16, output lane l holds key l%32 and 16 heads.
-//     All B operands of a tile are read from LDS before its first MFMA;
-//   * software pipeline: while tile i's MFMAs run, the VALU finishes tile
-//     i-1 (ReLU, head weight, sum over the lane's heads; one permlane32 swap +
-//     add completes the head sum and leaves lane l with the score of key
-//     tile_start + l), so the epilogue hides under the matrix pipe;
+//   * one workgroup = 4 waves = 4 consecutive query rows (one row per wave),
+//     two workgroups per CU (two waves per SIMD, so one wave's memory and LDS
+//     waits overlap the other's MFMAs); row blocks are issued longest-first so
+//     the causal triangle drains evenly;
+//   * keys stream HBM -> LDS with direct loads (global_load_lds_dwordx4, no
+//     VGPR staging) into a 3-deep ring of 64-key bf16 tiles shared by the 4
+//     rows, rows XOR-swizzled so B-operand reads are bank-conflict free; one
+//     barrier per tile;
+//   * each wave keeps its row's heads x d query slice in registers as the MFMA
+//     A operand (M = heads) and reads 32-key halves of a tile as the B operand
+//     (N = keys): v_mfma_f32_32x32x16_bf16, output lane l holds key l%32 and 16
+//     heads.  Software pipeline by half tile: while the MFMAs of one half run,
+//     the VALU does the epilogue of the other (ReLU, head weight, sum over the
+//     lane's heads); one permlane32 swap + add completes the head sum and
+//     leaves lane l with the score of key tile_start + l;
 //   * streaming top-k per row: a strict "score > tau" filter appends survivors
-//     to a wave-private LDS candidate buffer kept in ascending position order.
-//     When any row of the workgroup nears capacity, every row compacts at the
-//     same barrier (one stall per workgroup, not one per row): one histogram
-//     pass over the buffer's key range finds a bin edge T with at least k
-//     entries >= T, entries below T are dropped and tau becomes T.  Because
-//     keys arrive in ascending position, a later key tying tau always loses the
-//     tie, so the strict filter is exact.  If a bin is too crowded (many equal
-//     scores) the exact select below is used instead;
+//     to the row's candidate buffer in the workspace (L2-resident, ascending
+//     position order).  When it nears capacity, one histogram pass over the
+//     score range picks the bin holding the k-th best and everything below
+//     that bin is dropped; tau becomes the smallest kept score.  Because keys
+//     arrive in ascending position, a later key tying tau always loses the
+//     tie, so the strict filter is exact.  A crowded bin (ties) falls back to
+//     an exact radix select;
 //   * at the end an exact radix select (score desc, position asc) picks the k
 //     winners and a stable pass writes their positions in ascending order.
 #include "device_common.hpp"
@@ -45,11 +46,14 @@ namespace {
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 4;
 constexpr int kThreads = kRowsPerWG * kWave;
+constexpr int kRing = 3;        // LDS tile buffers: tile it being read, it+1 landing, it+2 loading
+constexpr int kUnroll = 8;      // candidate entries per lane in flight in buffer passes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (direct-to-LDS loads are invisible to the compiler's own waitcnt tracking).
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (direct-to-LDS loads are invisible to the compiler's waitcnt
+// tracking, so the tile ring waits explicitly).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 15, "vmcnt immediate");
@@ -61,43 +65,38 @@ struct Thresh {
   int need;     // how many entries with key == v belong to the top k
 };
 
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) v = fminf(v, __shfl_xor(v, dd));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) v = fmaxf(v, __shfl_xor(v, dd));
+  return v;
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
+  for (int dd = 32; dd >= 1; dd >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, dd));
   return v;
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+  for (int dd = 32; dd >= 1; dd >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, dd));
   return v;
 }
 
-// Smallest and largest order key in cs[0..cnt).
-__device__ __forceinline__ void wave_key_range(const float* cs, int cnt, uint32_t& lo, uint32_t& hi) {
-  uint32_t a = 0xFFFFFFFFu, b = 0u;
-  for (int i = lane_id(); i < cnt; i += kWave) {
-    const uint32_t key = order_key(cs[i]);
-    a = min(a, key);
-    b = max(b, key);
-  }
-  lo = wave_min_u32(a);
-  hi = wave_max_u32(b);
-}
+// Candidate buffer of one row: float2 entries (score, position bits).
+struct Cand {
+  float2* e;
+  __device__ __forceinline__ float score(int i) const { return e[i].x; }
+};
 
-// Histogram of rel = key - lo over 256 bins (bin = (rel >> shift) & 255 for
-// entries whose rel matches `prefix` above the digit) and the bin holding the
-// kk-th largest entry.  Returns the bin; `above` = entries in higher bins,
-// `in_bin` = entries in the bin.
-__device__ int wave_hist_pick(const float* cs, int cnt, uint32_t lo, int shift, uint32_t pmask,
-                              uint32_t prefix, int kk, uint32_t* hist, int& above, int& in_bin) {
+// Bin holding the kk-th largest entry of a 256-bin LDS histogram (lane l owns
+// bins 4l..4l+3).  Returns the bin; `above` = entries in higher bins, `in_bin`
+// = entries in the bin.
+__device__ __forceinline__ int pick_bin(const uint32_t* hist, int kk, int& above, int& in_bin) {
   const int l = lane_id();
-  *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
-  wave_lds_sync();
-  for (int i = l; i < cnt; i += kWave) {
-    const uint32_t rel = order_key(cs[i]) - lo;
-    if ((rel & pmask) == prefix) atomicAdd(&hist[(rel >> shift) & 255u], 1u);
-  }
-  wave_lds_sync();
   const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
   const uint32_t tot = h.x + h.y + h.z + h.w;
   const int a3 = (int)(wave_suffix_sum(tot) - tot);   // entries in higher lanes' bins
@@ -114,21 +113,60 @@ __device__ int wave_hist_pick(const float* cs, int cnt, uint32_t lo, int shift, 
   return __shfl(bin, src);
 }
 
+__device__ __forceinline__ void clear_hist(uint32_t* hist) {
+  *reinterpret_cast<u32x4*>(hist + 4 * lane_id()) = u32x4{0u, 0u, 0u, 0u};
+  wave_lds_sync();
+}
+
 __device__ __forceinline__ int range_bits8(uint32_t range) {   // bit length rounded up to 8
   const int nbits = range == 0u ? 0 : 32 - __clz((int)range);
   return (nbits + 7) & ~7;
 }
 
-// Exact k-th best among cs[0..cnt) (cnt >= k >= 1): radix select on the key
-// offsets from the buffer minimum, 8 bits per pass from the top of the range.
-__device__ Thresh wave_select_kth(const float* cs, int cnt, int k, uint32_t* hist) {
-  uint32_t lo, hi;
-  wave_key_range(cs, cnt, lo, hi);
+// Exact k-th best among the cnt >= k >= 1 entries (score desc): radix select
+// on order-key offsets from the minimum, 8 bits per pass from the top of the
+// key range.
+__device__ Thresh select_kth(Cand c, int cnt, int k, uint32_t* hist) {
+  const int l = lane_id();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int base = 0; base < cnt; base += kWave * kUnroll) {
+    float v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * kWave + l;
+      v[u] = i < cnt ? c.score(i) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kWave + l < cnt) {
+        const uint32_t key = order_key(v[u]);
+        lo = min(lo, key);
+        hi = max(hi, key);
+      }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;
   for (int shift = range_bits8(hi - lo) - 8; shift >= 0; shift -= 8) {
+    clear_hist(hist);
+    for (int base = 0; base < cnt; base += kWave * kUnroll) {
+      float v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * kWave + l;
+        v[u] = i < cnt ? c.score(i) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t rel = order_key(v[u]) - lo;
+        if (base + u * kWave + l < cnt && (rel & pmask) == prefix)
+          atomicAdd(&hist[(rel >> shift) & 255u], 1u);
+      }
+    }
+    wave_lds_sync();
     int above, in_bin;
-    const int b = wave_hist_pick(cs, cnt, lo, shift, pmask, prefix, kk, hist, above, in_bin);
+    const int b = pick_bin(hist, kk, above, in_bin);
     kk -= above;
     prefix |= (uint32_t)b << shift;
     pmask |= 0xFFu << shift;
@@ -136,125 +174,115 @@ __device__ Thresh wave_select_kth(const float* cs, int cnt, int k, uint32_t* his
   return Thresh{lo + prefix, kk};
 }
 
-// Stable in-place compaction: keeps entries with key > t.v and the first
-// t.need entries with key == t.v (the lowest positions, since the buffer is
-// in ascending position order).  Returns the new count.
-__device__ int wave_compact(float* cs, int* cp, int cnt, Thresh t) {
+// Stable pass over the buffer keeping key > t.v and the first t.need entries
+// with key == t.v (the lowest positions: the buffer is in position order).
+// EMIT: write the kept positions to dst; otherwise compact in place and
+// return the new count.  In place is safe: every chunk is read before any of
+// its slots can be overwritten, and writes never pass the chunk being read.
+template <bool EMIT>
+__device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
   const int l = lane_id();
   int out = 0, eq_seen = 0;
-  for (int base = 0; base < cnt; base += kWave) {
-    const int i = base + l;
-    const bool in = i < cnt;
-    const float sc = in ? cs[i] : 0.0f;
-    const int ps = in ? cp[i] : 0;
-    const uint32_t key = order_key(sc);
-    const bool eq = in && key == t.v;
-    const uint64_t em = __ballot(eq);
-    const bool keep = (in && key > t.v) || (eq && eq_seen + wave_prefix(em) < t.need);
-    const uint64_t km = __ballot(keep);
-    wave_lds_sync();   // this chunk is in registers before anything is overwritten
-    if (keep) {
-      const int o = out + wave_prefix(km);
-      cs[o] = sc;
-      cp[o] = ps;
+  for (int base = 0; base < cnt; base += kWave * kUnroll) {
+    float2 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * kWave + l;
+      v[u] = i < cnt ? c.e[i] : make_float2(0.0f, 0.0f);
     }
-    out += __popcll(km);
-    eq_seen += __popcll(em);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool in = base + u * kWave + l < cnt;
+      const uint32_t key = order_key(v[u].x);
+      const bool eq = in && key == t.v;
+      const uint64_t em = __ballot(eq);
+      const bool keep = (in && key > t.v) || (eq && eq_seen + wave_prefix(em) < t.need);
+      const uint64_t km = __ballot(keep);
+      if (keep) {
+        const int o = out + wave_prefix(km);
+        if constexpr (EMIT) dst[o] = __float_as_int(v[u].y);
+        else c.e[o] = v[u];
+      }
+      out += __popcll(km);
+      eq_seen += __popcll(em);
+    }
   }
-  wave_lds_sync();
   return out;
 }
 
-// Buffer compaction during the stream, in the score-value domain.  One
-// histogram over [lo, hi] (lo: a lower bound of every entry, hi: the largest
-// entry) gives the bin b holding the k-th best; every entry in bins >= b is
-// kept.  The bin map is monotone in the score, so the kept set is {s >= s*}
-// with at least k members: the k-th best is >= s*, nothing below s* can win,
-// and a later key equal to s* loses the position tie, so tau = s* keeps the
-// strict filter exact.  A crowded bin (ties, or a range too wide to split)
-// falls back to the exact select.
-__device__ void wave_shrink(float* cs, int* cp, int& cnt, float& tau, float hi, int k, int keep_max,
-                            uint32_t* hist) {
+// Buffer shrink during the stream, in the score-value domain.  One histogram
+// over [lo, hi] (lo: a lower bound of every entry, hi: the largest entry)
+// gives the bin b holding the k-th best; every entry in bins >= b is kept.
+// The bin map is monotone in the score, so the kept set is {s >= s*} with at
+// least k members: the k-th best is >= s*, nothing below s* can win, and a
+// later key equal to s* loses the position tie, so tau = s* keeps the strict
+// filter exact.  A crowded bin (ties, or a range too wide to split) falls back
+// to the exact select.
+__device__ void shrink(Cand c, int& cnt, float& tau, float hi_lane, int k, int keep_max, uint32_t* hist) {
   const int l = lane_id();
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) hi = fmaxf(hi, __shfl_xor(hi, dd));
+  wait_vmcnt<0>();                               // this wave's appends are visible
+  const float hi = wave_max_f(hi_lane);
   float lo = tau;
-  if (lo == -INFINITY) {                       // first shrink: entries may be anything
+  if (lo == -INFINITY) {                         // first shrink: entries may be anything
     float a = INFINITY;
-    for (int i = l; i < cnt; i += kWave) a = fminf(a, cs[i]);
+    for (int base = 0; base < cnt; base += kWave * kUnroll) {
+      float v[kUnroll];
 #pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) a = fminf(a, __shfl_xor(a, dd));
-    lo = a;
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * kWave + l;
+        v[u] = i < cnt ? c.score(i) : INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) a = fminf(a, v[u]);
+    }
+    lo = wave_min_f(a);
   }
   const float inv = 256.0f / (hi - lo);
   if (hi > lo && inv > 0.0f && inv < INFINITY) {
-    *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
-    wave_lds_sync();
-    for (int i = l; i < cnt; i += kWave) {
-      const int bin = min(255, max(0, (int)((cs[i] - lo) * inv)));
-      atomicAdd(&hist[bin], 1u);
-    }
-    wave_lds_sync();
-    const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
-    const uint32_t tot = h.x + h.y + h.z + h.w;
-    const int a3 = (int)(wave_suffix_sum(tot) - tot);
-    const int a2 = a3 + (int)h.w, a1 = a2 + (int)h.z, a0 = a1 + (int)h.y;
-    int bin = -1, kept = 0;
-    if (a3 < k && k <= a2) { bin = 4 * l + 3; kept = a2; }
-    else if (a2 < k && k <= a1) { bin = 4 * l + 2; kept = a1; }
-    else if (a1 < k && k <= a0) { bin = 4 * l + 1; kept = a0; }
-    else if (a0 < k && k <= a0 + (int)h.x) { bin = 4 * l; kept = a0 + (int)h.x; }
-    const uint64_t mb = __ballot(bin >= 0);
-    const int src = __ffsll((unsigned long long)mb) - 1;
-    const int b = __shfl(bin, src);
-    if (__shfl(kept, src) <= keep_max) {
-      int out = 0;
-      float smin = INFINITY;
-      for (int base = 0; base < cnt; base += kWave) {
-        const int i = base + l;
-        const bool in = i < cnt;
-        const float sc = in ? cs[i] : 0.0f;
-        const int ps = in ? cp[i] : 0;
-        const bool keep = in && min(255, max(0, (int)((sc - lo) * inv))) >= b;
-        const uint64_t km = __ballot(keep);
-        wave_lds_sync();
-        if (keep) {
-          const int o = out + wave_prefix(km);
-          cs[o] = sc;
-          cp[o] = ps;
-          smin = fminf(smin, sc);
-        }
-        out += __popcll(km);
+    clear_hist(hist);
+    for (int base = 0; base < cnt; base += kWave * kUnroll) {
+      float v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * kWave + l;
+        v[u] = i < cnt ? c.score(i) : lo;
       }
 #pragma unroll
-      for (int dd = 32; dd >= 1; dd >>= 1) smin = fminf(smin, __shfl_xor(smin, dd));
-      wave_lds_sync();
+      for (int u = 0; u < kUnroll; ++u)
+        if (base + u * kWave + l < cnt) atomicAdd(&hist[min(255, max(0, (int)((v[u] - lo) * inv)))], 1u);
+    }
+    wave_lds_sync();
+    int above, in_bin;
+    const int b = pick_bin(hist, k, above, in_bin);
+    if (above + in_bin <= keep_max) {
+      int out = 0;
+      float smin = INFINITY;
+      for (int base = 0; base < cnt; base += kWave * kUnroll) {
+        float2 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int i = base + u * kWave + l;
+          v[u] = i < cnt ? c.e[i] : make_float2(0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const bool keep = base + u * kWave + l < cnt && min(255, max(0, (int)((v[u].x - lo) * inv))) >= b;
+          const uint64_t km = __ballot(keep);
+          if (keep) {
+            c.e[out + wave_prefix(km)] = v[u];
+            smin = fminf(smin, v[u].x);
+          }
+          out += __popcll(km);
+        }
+      }
       cnt = out;
-      tau = smin;
+      tau = wave_min_f(smin);
       return;
     }
   }
-  const Thresh th = wave_select_kth(cs, cnt, k, hist);
-  cnt = wave_compact(cs, cp, cnt, th);
+  const Thresh th = select_kth(c, cnt, k, hist);
+  cnt = keep_pass<false>(c, cnt, th, nullptr);
   tau = key_value(th.v);
-}
-
-// Same selection as wave_compact, but writes the kept positions to `dst`.
-__device__ void wave_emit(const float* cs, const int* cp, int cnt, Thresh t, int32_t* dst) {
-  const int l = lane_id();
-  int out = 0, eq_seen = 0;
-  for (int base = 0; base < cnt; base += kWave) {
-    const int i = base + l;
-    const bool in = i < cnt;
-    const uint32_t key = order_key(in ? cs[i] : 0.0f);
-    const bool eq = in && key == t.v;
-    const uint64_t em = __ballot(eq);
-    const bool keep = (in && key > t.v) || (eq && eq_seen + wave_prefix(em) < t.need);
-    const uint64_t km = __ballot(keep);
-    if (keep) dst[out + wave_prefix(km)] = cp[i];
-    out += __popcll(km);
-    eq_seen += __popcll(em);
-  }
 }
 
 // Key tile in LDS: 64 rows of d bf16 (CPR = d/8 16-byte chunks per row),
@@ -274,12 +302,19 @@ struct TileGeom {
   __device__ static __forceinline__ int swz(int r, int c) { return c ^ ((r / RPB) & (CPR - 1)); }
 };
 
-constexpr int kRing = 3;   // LDS tile buffers: tiles it, it+1 ready/landing, it+2 loading
+template <int KS>
+__device__ __forceinline__ void read_bfrags(const unsigned char* kb, int nt, int m, int hf, bf16x8 (&bfr)[KS]) {
+  using G = TileGeom<KS>;
+  const int r = nt * 32 + m;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + r * G::row_bytes + G::swz(r, hf * (G::CPR / 2) + ks) * 16);
+}
 
-// One half-tile block: the MFMAs of key half `nt` of the current tile into
-// acc_mma and/or the epilogue of the other accumulator half (acc_epi), in one
-// basic block so the scheduler can put the VALU work between MFMAs.  Returns
-// the partial (this lane's 16 x HT heads) score of the epilogue half.
+// One half-tile block: the MFMAs of one 32-key half into acc_mma and/or the
+// epilogue of the other accumulator half (acc_epi), in one basic block so the
+// scheduler can put the VALU work between MFMAs.  Returns the partial (this
+// lane's heads) score of the epilogue half.
 template <int HT, int KS, bool MMA, bool EPI>
 __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const float (&wr)[HT][16],
                                             const bf16x8 (&bfr)[KS], f32x16 (&acc_mma)[HT],
@@ -311,26 +346,15 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
   return part;
 }
 
-template <int KS>
-__device__ __forceinline__ void read_bfrags(const unsigned char* kb, int nt, int m, int hf, bf16x8 (&bfr)[KS]) {
-  using G = TileGeom<KS>;
-  const int r = nt * 32 + m;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + r * G::row_bytes + G::swz(r, hf * (G::CPR / 2) + ks) * 16);
-}
-
 template <int HT, int KS, bool SCALE>
-__global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedArgs a) {
   using G = TileGeom<KS>;
   constexpr int d = G::d;
   constexpr int kLoads = G::inst_per_wave + (SCALE ? 1 : 0);   // direct loads per wave per tile
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* key_lds0 = smem;                                                   // [3][tile]
   float* scale_lds = reinterpret_cast<float*>(smem + kRing * G::tile_bytes);       // [3][64]
-  int* need_flags = reinterpret_cast<int*>(scale_lds + kRing * kTileKeys);         // [2][4]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(need_flags + 8);                    // [4][256]
-  float* cand = reinterpret_cast<float*>(hist + kRowsPerWG * 256);                 // [4][2C]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(scale_lds + kRing * kTileKeys);     // [4][256]
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int m = l & 31, hf = l >> 5;
@@ -343,8 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   const int n_keys = (int)a.q_start + last_row + 1;
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
   const int C = a.C;
-  float* cs = cand + (size_t)wave * 2 * C;
-  int* cp = reinterpret_cast<int*>(cs + C);
+  const Cand cand{a.cand + ((int64_t)b * a.n_q + (row_ok ? t : 0)) * C};
   uint32_t* my_hist = hist + wave * 256;
 
   // Query slice (A operand): lane (m, hf) holds head ht*32+m, elements
@@ -374,9 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   const float* scale_b = SCALE ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
 
   // Direct HBM -> LDS loads of tile `it` into ring slot `slot`: load j of this
-  // wave fills LDS slots [64J, 64J+64) (J = wave + 4j) in lane order, so lane l
-  // fetches the global chunk that belongs in slot 64J + l.  Rows past the last
-  // key are clamped (their scores are masked).
+  // wave fills LDS slots [J*n, J*n+n) (J = wave + 4j, n lanes) in lane order, so
+  // lane l fetches the global chunk that belongs in slot J*n + l.  Rows past
+  // the last key are clamped (their scores are masked).
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   int cnt = 0;
   const int keep_max = C - 2 * kWave;          // after a shrink the next trigger is >= 64 appends away
   float sc_prev = 1.0f;
-  float part0 = 0.0f;                           // nt=0 partial score of the tile being finished
+  float part0 = 0.0f;                           // key-half-0 partial score of the tile being finished
 
   issue_tile(0, 0);
   if (n_tiles > 1) {
@@ -410,7 +433,6 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
   } else {
     wait_vmcnt<0>();
   }
-  if (tid < 8) need_flags[tid] = 0;
   __syncthreads();
 
   f32x16 acc0[HT], acc1[HT];
@@ -420,20 +442,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
     const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
     const unsigned char* kb = key_lds0 + slot * G::tile_bytes;
     const float sc_cur = SCALE ? scale_lds[slot * kTileKeys + l] : 1.0f;
-    const u32x4 nf = *reinterpret_cast<const u32x4*>(need_flags + ((it & 1) ^ 1) * 4);   // previous step's
     const bool more = it + 2 < n_tiles;
     if (more) issue_tile(it + 2, slot == 0 ? 2 : slot - 1);   // (slot + 2) % 3
 
-    bf16x8 bx[KS], by[KS];
-    if (mma) {
-      read_bfrags<KS>(kb, 0, m, hf, bx);
-      read_bfrags<KS>(kb, 1, m, hf, by);
-    }
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
+    bf16x8 bfr[KS];
     float part1 = 0.0f;
-    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, bx, acc0, acc1);
-    else if (mma) half_block<HT, KS, true, false>(qf, wr, bx, acc0, acc1);
-    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, bx, acc0, acc1);
+    if (mma) read_bfrags<KS>(kb, 0, m, hf, bfr);
+    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, bfr, acc0, acc1);
+    else if (mma) half_block<HT, KS, true, false>(qf, wr, bfr, acc0, acc1);
+    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, bfr, acc0, acc1);
 
     if (epi) {
       // finish tile it-1: lanes 0-31 take key half 0, lanes 32-63 half 1
@@ -443,26 +461,23 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
       if (SCALE) score *= sc_prev;
       const int s = (it - 1) * kTileKeys + l;
       if (s > p) score = -INFINITY;
-      if ((nf.x | nf.y | nf.z | nf.w) && cnt > a.k + (C - a.k) / 2) {   // some row is nearly full
-        wave_lds_sync();
-        wave_shrink(cs, cp, cnt, tau, vmax, a.k, keep_max, my_hist);
-      }
+      if (cnt > C - kWave) shrink(cand, cnt, tau, vmax, a.k, keep_max, my_hist);
       const bool pass = score > tau;
       const uint64_t pm = __ballot(pass);
       if (pm) {
         if (pass) {
-          const int o = cnt + wave_prefix(pm);
-          cs[o] = score;
-          cp[o] = s;
+          cand.e[cnt + wave_prefix(pm)] = make_float2(score, __int_as_float(s));
+          vmax = fmaxf(vmax, score);              // per lane; reduced when a shrink needs it
         }
         cnt += __popcll(pm);
-        if (pass) vmax = fmaxf(vmax, score);      // per lane; reduced when a shrink needs it
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
-    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, by, acc1, acc0);
+    if (mma) {
+      read_bfrags<KS>(kb, 1, m, hf, bfr);
+      part0 = half_block<HT, KS, true, true>(qf, wr, bfr, acc1, acc0);
+    }
     sc_prev = sc_cur;
-    if (l == 0) need_flags[(it & 1) * 4 + wave] = (row_ok && cnt > C - kWave) ? 1 : 0;
     if (more) wait_vmcnt<kLoads>();              // tile it+1 landed (it+2 may still fly)
     else wait_vmcnt<0>();
     __syncthreads();
@@ -471,14 +486,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_indexer_topk_kernel(FusedAr
 
   if (row_ok) {
     int32_t* dst = a.idx + ((int64_t)b * a.n_q + t) * a.k;
-    wave_lds_sync();
+    wait_vmcnt<0>();
     int written;
     if (cnt > a.k) {
-      const Thresh th = wave_select_kth(cs, cnt, a.k, my_hist);
-      wave_emit(cs, cp, cnt, th, dst);
+      const Thresh th = select_kth(cand, cnt, a.k, my_hist);
+      keep_pass<true>(cand, cnt, th, dst);
       written = a.k;
     } else {
-      for (int i = l; i < cnt; i += kWave) dst[i] = cp[i];
+      for (int i = l; i < cnt; i += kWave) dst[i] = __float_as_int(cand.e[i].y);
       written = cnt;
     }
     for (int i = written + l; i < a.k; i += kWave) dst[i] = -1;
@@ -507,7 +522,7 @@ __global__ void upcast_fp8_kernel(const uint8_t* __restrict__ src, int64_t src_b
 
 template <int HT, int KS, bool SCALE>
 hipError_t launch_fused_s(const FusedArgs& a, int B, hipStream_t s) {
-  const size_t lds = fused_lds_bytes(KS * 16, a.C);
+  const size_t lds = fused_lds_bytes(KS * 16);
   const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -524,14 +539,13 @@ hipError_t launch_fused_t(const FusedArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 int fused_candidates(int k) {
-  int extra = k / 2 > 2 * kWave ? k / 2 : 2 * kWave;
+  const int extra = k > 4 * kWave ? k : 4 * kWave;
   return ((k + extra + kWave - 1) / kWave) * kWave;
 }
 
-size_t fused_lds_bytes(int d, int C) {
-  const size_t tile = (size_t)kTileKeys * 2 * d;
-  return kRing * tile + kRing * kTileKeys * sizeof(float) + 8 * sizeof(int) +
-         kRowsPerWG * 256 * sizeof(uint32_t) + (size_t)kRowsPerWG * C * 8;
+size_t fused_lds_bytes(int d) {
+  return (size_t)kRing * kTileKeys * 2 * d + kRing * kTileKeys * sizeof(float) +
+         kRowsPerWG * 256 * sizeof(uint32_t);
 }
 
 bool fused_dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }

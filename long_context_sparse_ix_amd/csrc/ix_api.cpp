@@ -74,11 +74,18 @@ bool use_fused(const ix_problem* p, const ix_indexer_in* in) {
   return rows >= 128 || score_bytes > ((int64_t)1 << 30);
 }
 
+// Fused path: per-row candidate buffers, then (fp8 keys) a bf16 copy of the
+// keys any query can reach.  Materialised path: one fp32 score row per query.
+size_t fused_cand_bytes(const ix_problem* p) {
+  return round_up((size_t)p->batch * p->n_q * (size_t)ix::fused_candidates(p->k) * 8);
+}
+
 size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
   if (use_fused(p, in)) {
-    if (in->k_dtype == IX_DTYPE_FP8_E4M3FN)   // bf16 copy of the keys a query can reach
-      return round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
-    return 0;
+    size_t need = fused_cand_bytes(p);
+    if (in->k_dtype == IX_DTYPE_FP8_E4M3FN)
+      need += round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
+    return need;
   }
   return round_up((size_t)p->batch * p->n_q * (size_t)p->kv_len * 4);
 }
@@ -126,8 +133,9 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
     a.H = in->heads;
     a.k = p->k;
     a.C = ix::fused_candidates(p->k);
+    a.cand = static_cast<float2*>(ws);
     if (fp8) {
-      uint16_t* kb = static_cast<uint16_t*>(ws);
+      uint16_t* kb = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fused_cand_bytes(p));
       hipError_t e = ix::launch_upcast_fp8(static_cast<const uint8_t*>(in->k), p->kv_cap * in->dim,
                                            kb, p->kv_len * in->dim, p->batch, p->kv_len, in->dim, s);
       if (e != hipSuccess) return hip_fail(e);

@@ -14,12 +14,13 @@ struct FusedArgs {
   const uint16_t* keys;   // bf16 rows, row stride d, sequence stride key_bstride
   const float* scale;     // per-key fp32 scale, or nullptr
   int32_t* idx;           // [B][n_q][k]
+  float2* cand;           // workspace: [B][n_q][C] (score, position bits) candidate buffers
   int64_t key_bstride;    // elements
   int64_t scale_bstride;  // elements
   int64_t q_start;
   int n_q, H, k, C;       // C: candidate slots per row (>= k + 64)
 };
-size_t fused_lds_bytes(int d, int C);
+size_t fused_lds_bytes(int d);
 bool fused_dim_supported(int d);   // d in {16, 32, 64, 128}
 int fused_candidates(int k);
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s);
