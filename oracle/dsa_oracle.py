@@ -40,7 +40,7 @@ import numpy as np
 
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "key_matrix", "indexer_scores", "select_topk",
-    "indexer_topk", "attention_row", "sparse_attention", "group_forward",
+    "indexer_topk", "indexer_topk_rows", "attention_row", "sparse_attention", "group_forward",
 ]
 
 
@@ -127,6 +127,26 @@ def indexer_topk(q, w, keys, key_dtype, scale, q_start: int, kv_len: int, k: int
             s = indexer_scores(decode_bf16(q[b, t]), np.asarray(w[b, t], np.float64),
                                kmat[:n])
             out[b, i] = select_topk(s, k)
+    return out
+
+
+def indexer_topk_rows(q_rows, w_rows, keys_b, key_dtype, scale_b, positions, kv_len: int,
+                      k: int) -> np.ndarray:
+    """Indexer + top-k for individual query rows of one sequence, given their
+    absolute positions (decodes the reachable keys once).
+
+    q_rows: bf16 bits [R, H, d]; w_rows: fp32 [R, H]; keys_b: [cap, d] of one
+    sequence; scale_b: [cap] (fp8 only); positions: [R].  Returns int32 [R, k].
+    """
+    positions = [int(p) for p in positions]
+    p_max = min(max(positions), kv_len - 1)
+    sc = None if scale_b is None else np.asarray(scale_b)[: p_max + 1]
+    kmat = key_matrix(np.asarray(keys_b)[: p_max + 1], key_dtype, sc)
+    out = np.full((len(positions), k), -1, dtype=np.int32)
+    for i, p in enumerate(positions):
+        n = min(p, kv_len - 1) + 1
+        s = indexer_scores(decode_bf16(q_rows[i]), np.asarray(w_rows[i], np.float64), kmat[:n])
+        out[i] = select_topk(s, k)
     return out
 
 

@@ -1,0 +1,183 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times: every row is computed on the GPU; sampled rows are checked
+against the CPU oracle (indices by overlap in float mode, bit for bit in exact
+mode; attention outputs within 2e-2 given the GPU's indices), and structural
+invariants are checked on every row on the device."""
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import bits16, ensure_lib, host, key_bytes, overlap
+import ix_synth as synth
+from oracle import dsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def ix():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_lib()
+    import long_context_sparse_ix_amd as m
+    return m
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def device_idx_invariants(idx: torch.Tensor, q_start: int, k: int):
+    """On the device, for every row: ascending valid positions <= p, exactly
+    min(k, p+1) of them, then -1."""
+    B, n_q, _ = idx.shape
+    p = q_start + torch.arange(n_q, device=idx.device).view(1, n_q, 1)
+    n_valid = torch.clamp(p + 1, max=k)
+    slot = torch.arange(k, device=idx.device).view(1, 1, k)
+    valid = slot < n_valid
+    assert bool(((idx >= 0) == valid).all()), "valid slots are not exactly the first min(k, p+1)"
+    assert bool(((idx <= p) | ~valid).all()), "position beyond the query row"
+    inc = idx[:, :, 1:] > idx[:, :, :-1]
+    assert bool((inc | ~valid[:, :, 1:]).all()), "valid positions not strictly ascending"
+
+
+def oracle_idx(w, e, rows, b=0):
+    kb, kd = key_bytes(e["keys"][b:b + 1])
+    sc = None if e["k_scale"] is None else host(e["k_scale"][b])
+    return O.indexer_topk_rows(bits16(e["q"][b, rows]), host(e["w"][b, rows]), kb[0], kd, sc,
+                               [w.q_start + t for t in rows], w.kv_len, w.k)
+
+
+def run_group(ix, w, roles, step=0, mode=None):
+    wl = w if mode is None else w.with_(mode=mode)
+    ixl, atl = [], []
+    for l, r in enumerate(roles):
+        if r == "F":
+            q, wt = synth.indexer_queries(wl, "cuda", l, step)
+            keys, scale = synth.indexer_keys(wl, "cuda", l)
+            ixl.append(dict(q=q, w=wt, keys=keys, k_scale=scale))
+        else:
+            ixl.append(None)
+        atl.append(dict(q=synth.attn_queries(wl, "cuda", l, step), kv=synth.latent_kv(wl, "cuda", l),
+                        out=torch.empty((w.batch, w.n_q, w.q_heads, w.d_v), dtype=torch.bfloat16, device="cuda"),
+                        lse=torch.empty((w.batch, w.n_q, w.q_heads), device="cuda")))
+    mask = sum(1 << i for i, r in enumerate(roles) if r == "F")
+    idx = torch.empty((roles.count("F"), w.batch, w.n_q, w.k), dtype=torch.int32, device="cuda")
+    print(f"[full] {wl.name} mode={wl.mode} roles={roles} B={w.batch} n_q={w.n_q} kv_len={w.kv_len}",
+          flush=True)
+    ix.ix_group_forward(ixl, atl, mask, idx, q_start=w.q_start, kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    return ixl, atl, idx
+
+
+def check_group(w, ixl, atl, idx, rows, b=0, exact=False):
+    f = -1
+    for l, e in enumerate(ixl):
+        if e is not None:
+            f += 1
+            ref = oracle_idx(w, e, rows, b)
+            got = host(idx[f, b, rows])
+            if exact:
+                np.testing.assert_array_equal(got, ref)
+            else:
+                ov, worst = overlap(got, ref)
+                print(f"  layer {l}: overlap {ov:.6f} worst {worst:.4f}")
+                assert ov >= 0.999
+        a = atl[l]
+        gidx = host(idx[f, b:b + 1, rows])
+        ref_o, ref_lse = O.sparse_attention(bits16(a["q"][b:b + 1, rows]), bits16(a["kv"][b:b + 1]), gidx,
+                                            w.kv_len, 1.0 / math.sqrt(w.d_qk), w.d_v)
+        err = np.abs(a["out"][b:b + 1, rows].float().cpu().numpy() - ref_o).max()
+        lerr = np.abs(host(a["lse"][b:b + 1, rows]) - ref_lse).max()
+        print(f"  layer {l}: attention max-abs {err:.2e} lse {lerr:.2e}")
+        assert err <= ATOL and lerr <= 1e-3
+
+
+def test_prefill_l16k_group(ix):
+    w = synth.L16K
+    ixl, atl, idx = run_group(ix, w, w.roles)
+    device_idx_invariants(idx[0], w.q_start, w.k)
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 16))
+
+
+def test_prefill_l16k_exact_indices(ix):
+    w = synth.L16K.with_(mode="exact")
+    q, wt = synth.indexer_queries(w, "cuda", 0)
+    keys, _ = synth.indexer_keys(w, "cuda", 0)
+    idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
+    ix.ix_indexer_topk(q, wt, keys, idx, q_start=0, kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, 16)
+    np.testing.assert_array_equal(host(idx[0, rows]),
+                                  oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=None), rows))
+
+
+def test_prefill_l128k_group(ix):
+    """The headline shape (one of its two F,S,S,S groups; the second group
+    repeats the same kernels on its own inputs)."""
+    w = synth.L128K
+    ixl, atl, idx = run_group(ix, w, "FSSS")
+    device_idx_invariants(idx[0], w.q_start, w.k)
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 10))
+
+
+def test_prefill_l128k_exact_indices(ix):
+    w = synth.L128K.with_(mode="exact")
+    q, wt = synth.indexer_queries(w, "cuda", 4)
+    keys, scale = synth.indexer_keys(w, "cuda", 4)
+    idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
+    ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=0, kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, 8)
+    np.testing.assert_array_equal(host(idx[0, rows]),
+                                  oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=scale), rows))
+
+
+def test_chunked_prefill_1m(ix):
+    w = synth.CHUNK_1M
+    ixl, atl, idx = run_group(ix, w, w.roles)
+    device_idx_invariants(idx[0], w.q_start, w.k)
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 6))
+
+
+def test_chunked_prefill_1m_exact_indices(ix):
+    w = synth.CHUNK_1M.with_(mode="exact")
+    q, wt = synth.indexer_queries(w, "cuda", 0)
+    keys, scale = synth.indexer_keys(w, "cuda", 0)
+    idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
+    ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    rows = [0, 4095, 8191]
+    np.testing.assert_array_equal(host(idx[0, rows]),
+                                  oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=scale), rows))
+
+
+@pytest.mark.parametrize("step", [0, 63])
+def test_decode_b32_step(ix, step):
+    """Decode: 32 sequences with a 200,000-token cache, one new query each;
+    step j sees kv_len = 200,001 + j."""
+    base = synth.DECODE_B32
+    w = base.with_(q_start=base.q_start + step, kv_len=base.kv_len + step)
+    ixl, atl, idx = run_group(ix, w, base.roles, step=step)
+    device_idx_invariants(idx[0], w.q_start, w.k)
+    for b in (0, 13, 31):
+        check_group(w, ixl, atl, idx, [0], b=b)
+
+
+def test_decode_b32_exact_indices(ix):
+    base = synth.DECODE_B32.with_(mode="exact")
+    q, wt = synth.indexer_queries(base, "cuda", 0)
+    keys, scale = synth.indexer_keys(base, "cuda", 0)
+    idx = torch.empty((32, 1, base.k), dtype=torch.int32, device="cuda")
+    ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=base.q_start, kv_len=base.kv_len)
+    torch.cuda.synchronize()
+    for b in (0, 17, 31):
+        np.testing.assert_array_equal(host(idx[b]), oracle_idx(base, dict(q=q, w=wt, keys=keys, k_scale=scale), [0], b))

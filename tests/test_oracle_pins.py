@@ -338,3 +338,17 @@ def test_schedule_rejects_leading_shared_layer():
 def test_oracle_exports():
     for name in oracle.__all__:
         assert callable(getattr(oracle, name))
+
+
+def test_row_form_agrees_with_batch_form():
+    """indexer_topk_rows (rows given by absolute position) and indexer_topk
+    (rows given by index) compute the same rows."""
+    rng = np.random.default_rng(15)
+    n, H, d, k = 90, 3, 8, 11
+    q = bf16_bits(rng.integers(-8, 9, (1, 30, H, d)))
+    w = rng.choice([1.0, 2.0, 4.0], (1, 30, H)).astype(np.float32)
+    keys = bf16_bits(rng.integers(-8, 9, (1, n, d)))
+    full = O.indexer_topk(q, w, keys, "bf16", None, 60, n, k)
+    rows = [0, 7, 29]
+    part = O.indexer_topk_rows(q[0, rows], w[0, rows], keys[0], "bf16", None, [60 + r for r in rows], n, k)
+    np.testing.assert_array_equal(part, full[0, rows])
