@@ -9,6 +9,8 @@
 // straight from HBM into MFMA B operands (no LDS).  fp8 e4m3fn keys are
 // widened to bf16 in registers (exact) and the per-key scale is applied to the
 // finished score.  The rows are then reduced by the per-row top-k kernel.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -21,7 +23,7 @@ constexpr int kTilesPerWave = 16;           // 1024 keys per wave
 constexpr int kWavesPerWG = 4;
 
 template <int HT, int KS, bool FP8>
-__global__ __launch_bounds__(kWavesPerWG * kWave) void indexer_scores_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scores_kernel(ScoreArgs a) {
   constexpr int d = KS * 16;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 31, hf = l >> 5;
@@ -52,60 +54,75 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void indexer_scores_kernel(Sco
   const float* scale_b = FP8 ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
   float* out = a.scores + (int64_t)row * a.ld;
 
-  for (int j = 0; j < kTilesPerWave; ++j) {
-    const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
-    if (s0 > p) break;
-    f32x16 acc[2][HT];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[nt][ht] = f32x16{};
-    bf16x8 bfr[2][KS];
+  // Raw key bytes of one 64-key tile for this lane: key s0 + nt*32 + m, bytes
+  // (fp8) or elements (bf16) [hf*d/2, +d/2).  The next tile's raw bytes are
+  // loaded while the current one is widened and multiplied.
+  constexpr int RAW = FP8 ? (KS % 2 == 0 ? KS / 2 : KS) : KS;   // 16-byte (or 8-byte) pieces per half
+  typedef typename std::conditional<FP8 && (KS % 2 != 0), u32x2, u32x4>::type piece_t;
+  piece_t raw_cur[2][RAW], raw_nxt[2][RAW];
+  auto load_raw = [&](int64_t s0, piece_t (&raw)[2][RAW]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       int64_t s = s0 + nt * 32 + m;
       if (s > p) s = p;                       // stays inside the cache; masked below
-      if constexpr (FP8) {
-        const uint8_t* kr = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.key_bstride + s * d + hf * (d / 2);
-        if constexpr (KS % 2 == 0) {
+      const unsigned char* kr = static_cast<const unsigned char*>(a.keys) +
+                                ((int64_t)b * a.key_bstride + s * d + hf * (d / 2)) * (FP8 ? 1 : 2);
 #pragma unroll
-          for (int c = 0; c < KS / 2; ++c) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(kr + 16 * c);
-            const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-            const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
-            bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
-            bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
-          }
-        } else {
+      for (int c = 0; c < RAW; ++c) raw[nt][c] = *reinterpret_cast<const piece_t*>(kr + c * sizeof(piece_t));
+    }
+  };
+  auto widen = [&](const piece_t (&raw)[2][RAW], bf16x8 (&bfr)[2][KS]) {
 #pragma unroll
-          for (int c = 0; c < KS; ++c) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(kr + 8 * c);
-            const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-            bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
-          }
+    for (int nt = 0; nt < 2; ++nt) {
+      if constexpr (FP8 && KS % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < KS / 2; ++c) {
+          const u32x4 v = raw[nt][c];
+          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+          const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
+          bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+          bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
+        }
+      } else if constexpr (FP8) {
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          const u32x2 v = raw[nt][c];
+          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+          bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
         }
       } else {
-        const uint16_t* kr = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.key_bstride + s * d + hf * (d / 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = *reinterpret_cast<const bf16x8*>(kr + 8 * ks);
+        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = __builtin_bit_cast(bf16x8, raw[nt][ks]);
       }
     }
+  };
+
+  load_raw(s_begin, raw_cur);
+  for (int j = 0; j < kTilesPerWave; ++j) {
+    const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
+    if (s0 > p) break;
+    const bool more = j + 1 < kTilesPerWave && s0 + kTileKeys <= p;
+    if (more) load_raw(s0 + kTileKeys, raw_nxt);
+    bf16x8 bfr[2][KS];
+    widen(raw_cur, bfr);
+    f32x16 acc[2][HT];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
-          acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks], acc[nt][ht], 0, 0, 0);
+          acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks],
+                                                                ks == 0 ? f32x16{} : acc[nt][ht], 0, 0, 0);
     float part[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float s = 0.0f;
+      float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), s);
-      part[nt] = s;
+        for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), sacc[r & 3]);
+      part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
                                                      __float_as_uint(part[1]), false, false);
@@ -115,6 +132,10 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void indexer_scores_kernel(Sco
       if constexpr (FP8) score *= scale_b[s];
       out[s] = score;
     }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int c = 0; c < RAW; ++c) raw_cur[nt][c] = raw_nxt[nt][c];
   }
 }
 

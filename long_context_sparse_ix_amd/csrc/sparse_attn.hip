@@ -191,32 +191,47 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   }
 }
 
-// Merge the split partials of one (row, head): base-2 log-sum-exp weights.
+// Merge the split partials of one (row, head): base-2 log-sum-exp weights
+// exp2(m_s - M) / L are computed once into LDS, then every thread folds four
+// consecutive value dims over the splits.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int Dv) {
+  __shared__ float wgt[64];
+  __shared__ float stat[2];
   const int item = blockIdx.x;              // r * Hq + h
   const int r = item / a.Hq, h = item % a.Hq;
   const int S = a.splits;
-  const float* ml = a.part_ml + ((int64_t)r * S * 16 + h) * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(int64_t)s * 32]);
-  float L = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = ml[(int64_t)s * 32];
-    if (ms != -INFINITY) L += ml[(int64_t)s * 32 + 1] * exp2f(ms - M);
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * Dv;
-  for (int dv = threadIdx.x; dv < Dv; dv += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = ml[(int64_t)s * 32];
-      if (ms == -INFINITY) continue;
-      acc += a.part_o[(((int64_t)r * S + s) * 16 + h) * Dv + dv] * exp2f(ms - M);
+  const float* ml = a.part_ml + ((int64_t)r * S * 16 + h) * 2;     // split s at + s*32
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    const float ms = l < S ? ml[(int64_t)l * 32] : -INFINITY;
+    const float ls = l < S ? ml[(int64_t)l * 32 + 1] : 0.0f;
+    float M = ms;
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) M = fmaxf(M, __shfl_xor(M, dd));
+    const float e = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+    float L = ls * e;
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) L += __shfl_xor(L, dd);
+    if (l < S) wgt[l] = L > 0.0f ? e / L : 0.0f;
+    if (l == 0) {
+      stat[0] = M;
+      stat[1] = L;
     }
-    orow[dv] = (uint16_t)bf16_rne(acc * inv);
+  }
+  __syncthreads();
+  const float* po = a.part_o + ((int64_t)r * S * 16 + h) * Dv;     // split s at + s*16*Dv
+  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * Dv;
+  for (int dv = threadIdx.x * 4; dv < Dv; dv += blockDim.x * 4) {
+    f32x4 acc = f32x4{};
+    for (int s = 0; s < S; ++s) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)s * 16 * Dv + dv);
+      acc += v * wgt[s];
+    }
+    const u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(orow + dv) = o;
   }
   if (threadIdx.x == 0 && a.lse)
-    a.lse[(int64_t)r * a.Hq + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    a.lse[(int64_t)r * a.Hq + h] = stat[1] > 0.0f ? (stat[0] + log2f(stat[1])) * kLn2 : -INFINITY;
 }
 
 template <int KS, int MT>
