@@ -165,7 +165,10 @@ int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_ma
 
 /* Top-k over caller-provided fp32 score rows: scores[(b*n_q + t)*ld + s] for
  * s <= p = q_start + t (entries beyond p are ignored).  Same selection rule
- * and output layout as ix_indexer_topk.  ld >= kv_len. */
+ * and output layout as ix_indexer_topk.  ld >= kv_len.  Scores must not be
+ * NaN.  Calls with few long rows (B*n_q < 1024 and q_start + n_q > k) keep
+ * their select state in ws, of ix_workspace_bytes(prob, IX_OP_TOPK_SCORES,
+ * NULL) bytes; other calls need none (ws may be NULL). */
 int32_t ix_topk_scores(const ix_problem* prob, const float* scores, int64_t ld, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream);
 

@@ -272,5 +272,6 @@ def ix_topk_scores(scores, idx, *, q_start=0, kv_len=None, stream=None):
     ld = scores.shape[2]
     prob = _problem(scores.shape[0], scores.shape[1], q_start, ld if kv_len is None else kv_len,
                     ld if kv_len is None else kv_len, idx.shape[2])
-    _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), None, 0,
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_TOPK_SCORES, None), scores.device)
+    _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), _ptr(ws), nb,
                               _stream(stream)), "ix_topk_scores")

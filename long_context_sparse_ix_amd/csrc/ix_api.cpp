@@ -80,6 +80,16 @@ size_t fused_cand_bytes(const ix_problem* p) {
   return round_up((size_t)p->batch * p->n_q * (size_t)ix::fused_candidates(p->k) * 8);
 }
 
+// Materialised path: fp32 score rows with a 16-byte aligned row stride, then
+// the row top-k's own state.
+int64_t score_ld(const ix_problem* p) { return (p->kv_len + 3) & ~(int64_t)3; }
+size_t score_bytes(const ix_problem* p) {
+  return round_up((size_t)p->batch * p->n_q * (size_t)score_ld(p) * 4);
+}
+size_t topk_ws(const ix_problem* p) {
+  return round_up(ix::topk_rows_ws_bytes(p->batch * p->n_q, p->q_start + p->n_q, p->k));
+}
+
 size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
   if (use_fused(p, in)) {
     size_t need = fused_cand_bytes(p);
@@ -87,7 +97,7 @@ size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
       need += round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
     return need;
   }
-  return round_up((size_t)p->batch * p->n_q * (size_t)p->kv_len * 4);
+  return score_bytes(p) + topk_ws(p);
 }
 
 int attn_splits(const ix_problem* p, const ix_attn_in* in) {
@@ -160,13 +170,14 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
   a.scores = static_cast<float*>(ws);
   a.key_bstride = p->kv_cap * in->dim;
   a.scale_bstride = p->kv_cap;
-  a.ld = p->kv_len;
+  a.ld = score_ld(p);
   a.q_start = p->q_start;
   a.n_q = p->n_q;
   a.H = in->heads;
   hipError_t e = ix::launch_indexer_scores(a, p->batch, in->dim, fp8, p->kv_len, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k, s);
+  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
+                           static_cast<char*>(ws) + score_bytes(p), s);
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
@@ -277,7 +288,7 @@ size_t ix_workspace_bytes(const ix_problem* p, int32_t op, const void* desc) {
       return group_ws(p, g->n_layers, g->f_mask, g->ixr, g->attn);
     }
     case IX_OP_TOPK_SCORES:
-      return 0;
+      return topk_ws(p);
     default:
       return 0;
   }
@@ -335,14 +346,14 @@ int32_t ix_group_forward(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
 
 int32_t ix_topk_scores(const ix_problem* p, const float* scores, int64_t ld, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int32_t st = check_problem(p);
   if (st != IX_OK) return st;
   if (!scores || !idx) return IX_E_NULL;
   if (ld < p->kv_len || !aligned16(scores) || !aligned16(idx)) return IX_E_SHAPE;
+  st = check_ws(topk_ws(p), ws, ws_bytes);
+  if (st != IX_OK) return st;
   hipError_t e = ix::launch_topk_rows(scores, ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
-                                      static_cast<hipStream_t>(stream));
+                                      ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 

@@ -45,9 +45,12 @@ struct ScoreArgs {
 hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
                                  hipStream_t s);
 
-// Per-row top-k over materialised fp32 score rows.
+// Per-row top-k over materialised fp32 score rows.  Few rows use a chunked
+// multi-workgroup select whose state lives in a workspace of
+// topk_rows_ws_bytes(rows, q_start + n_q, k) bytes (0: none needed).
+size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k);
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, hipStream_t s);
+                            int64_t q_start, int k, void* ws, hipStream_t s);
 
 // Sparse gather attention.
 struct AttnArgs {

@@ -5,18 +5,24 @@
 // selected positions): keep the min(k, p+1) best positions of row p under
 // (score desc, position asc); emit them in ascending position order, then -1.
 //
-// One 1024-thread workgroup per row, all passes over the row in L2:
-//   1. min / max of the row (register reductions, no atomics);
-//   2. a 2048-bin histogram over [min, max] in the value domain (LDS atomics
-//      spread over the bins) gives the bin b holding the k-th best and the
-//      number of entries above it;
-//   3. an exact radix select on the order keys of bin b's entries only (8 bits
-//      per pass over the bin's key range) finds the k-th key v and how many
-//      ties at v are needed;
-//   4. a stable pass in position order keeps key > v and the first ties at v,
-//      with block-wide prefix sums giving each kept position its slot.
-// The value-domain first pass keeps histogram contention low: a first pass on
-// the top bits of the float key would put nearly every score in 2-3 bins.
+// Few long rows (decode: 32 rows of ~200K scores) cannot fill the chip with one
+// workgroup per row, so a row is cut into 8192-score chunks, each with its own
+// workgroup, and the select runs as five short passes:
+//   R  range:   min / max of every chunk;
+//   H  hist:    a 1024-bin value-domain histogram of every chunk over the
+//               row's [min, max] (bins are monotone in the score);
+//   S  select:  per row, the bin vb holding the k-th best, the number m of
+//               scores in bins >= vb and, per chunk, where its share of those
+//               m starts in the row's candidate list;
+//   C  collect: every chunk writes its scores in bins >= vb, in position order,
+//               as (order key, position) into the candidate list;
+//   F  finish:  per row, an exact radix select over the m candidates in LDS
+//               gives the k-th key v and how many ties at v are kept, then a
+//               stable pass over the list (already in position order) emits.
+// A row whose m exceeds the candidate capacity (a flat or adversarial score
+// distribution) is finished instead by a single-workgroup exact select over
+// the whole row.  Many-row calls use that single-workgroup select directly: one
+// workgroup per row already fills the chip and needs no workspace.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,33 +30,85 @@ namespace ix {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kBins = 2048;
+constexpr int kCT = 512;                 // threads of the chunk passes
+constexpr int kPT = 16;                  // scores per thread in a chunk pass
+constexpr int kChunk = kCT * kPT;        // 8192 scores per chunk
+constexpr int kVB = 1024;                // value bins of a chunk histogram
+constexpr int kST = 256;                 // threads of the select pass (4 bins each)
+constexpr int kFT = 1024;                // threads of the finish / single-row select
+constexpr int kCap = 8192;               // candidate capacity per row
+constexpr int kMultiRowLimit = 1024;     // rows below this use the chunked select
 
-__device__ __forceinline__ int vbin(float s, float lo, float inv) {
-  return min(kBins - 1, max(0, (int)((s - lo) * inv)));
+constexpr int kSingleBins = 2048;        // value bins of the single-workgroup select
+
+// Row state handed from S to C and F.
+struct RowSel {
+  float lo, inv;   // value binning of the row
+  int vb;          // bin holding the k-th best
+  int m;           // scores in bins >= vb; kFallback / kTrivial as below
+};
+constexpr int kFallback = -1;            // too many candidates: whole-row select
+constexpr int kTrivial = -2;             // p + 1 <= k: keep every position
+
+__device__ __forceinline__ int row_len(int row, int n_q, int64_t q_start) {
+  return (int)(q_start + row % n_q + 1);
 }
 
-// Block-wide reductions through LDS scratch (one slot per wave).
-__device__ __forceinline__ float block_min(float v, float* red) {
-  for (int d = 32; d >= 1; d >>= 1) v = fminf(v, __shfl_xor(v, d));
+__device__ __forceinline__ int vbin(float s, float lo, float inv, int nbins) {
+  return min(nbins - 1, max(0, (int)((s - lo) * inv)));
+}
+
+// Bin scale over [lo, hi]; 0 (every score in bin 0) when the range cannot be
+// split.
+__device__ __forceinline__ float bin_scale(float lo, float hi, int nbins) {
+  float inv = nbins / (hi - lo);
+  if (!(hi > lo) || !(inv > 0.0f) || !(inv < INFINITY)) inv = 0.0f;
+  return inv;
+}
+
+// ---- block-wide helpers (NT threads, one LDS slot per wave) ----
+
+template <int NT, typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T* red, Op op) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = op(v, __shfl_xor(v, d));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kWaves; ++w) r = fminf(r, red[w]);
+  T r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) r = op(r, red[w]);
   __syncthreads();
   return r;
 }
-__device__ __forceinline__ float block_max(float v, float* red) {
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+
+// Exclusive prefix sum over the block in thread order; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int* total) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (l >= d) x += y;
+  }
+  if (l == kWave - 1) red[w] = x;
   __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int s = red[i];
+    before += i < w ? s : 0;
+    tot += s;
+  }
   __syncthreads();
-  return r;
+  *total = tot;
+  return before + x - v;
 }
+
+struct MinOp { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct UMinOp { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct UMaxOp { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 
 // Bin b of hist[0..nbins) with above(b) < kk <= above(b) + hist[b], where
 // above(b) counts entries in bins > b.  Wave 0 scans; result via LDS.
@@ -77,102 +135,84 @@ __device__ void pick_from_top(const uint32_t* hist, int nbins, int kk, int* out_
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float* __restrict__ scores,
-                                                             int64_t ld, int32_t* __restrict__ idx,
-                                                             int n_q, int64_t q_start, int k) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ float red[kWaves];
-  __shared__ int sel_bin, sel_above;
-  __shared__ int wave_keep[kWaves], wave_eq[kWaves];
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int row = blockIdx.x;
-  const int t = row % n_q;
-  const int n = (int)(q_start + t + 1);
-  const float* src = scores + (int64_t)row * ld;
-  int32_t* dst = idx + (int64_t)row * k;
-
-  if (n <= k) {
-    for (int i = tid; i < k; i += kThreads) dst[i] = i < n ? i : -1;
-    return;
-  }
-
-  // 1. range
-  float a = INFINITY, b = -INFINITY;
-  for (int i = tid; i < n; i += kThreads) {
-    const float s = src[i];
-    a = fminf(a, s);
-    b = fmaxf(b, s);
-  }
-  const float lo = block_min(a, red);
-  const float hi = block_max(b, red);
-
-  // 2. value-domain histogram (skipped when all scores are equal or the
-  //    range cannot be split: then every entry counts as bin 0)
-  float inv = kBins / (hi - lo);
-  if (!(hi > lo) || !(inv > 0.0f) || !(inv < INFINITY)) inv = 0.0f;
-  for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kThreads) atomicAdd(&hist[vbin(src[i], lo, inv)], 1u);
-  __syncthreads();
-  pick_from_top(hist, kBins, k, &sel_bin, &sel_above);
-  const int vb = sel_bin;
-  int kk = k - sel_above;
-  __syncthreads();
-
-  // 3. exact radix select among bin vb's entries, on order-key offsets from
-  //    the smallest key in the bin
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  {
-    uint32_t a_min = 0xFFFFFFFFu, a_max = 0u;
-    for (int i = tid; i < n; i += kThreads) {
-      const float s = src[i];
-      if (vbin(s, lo, inv) == vb) {
-        const uint32_t key = order_key(s);
-        a_min = min(a_min, key);
-        a_max = max(a_max, key);
-      }
-    }
-    for (int d = 32; d >= 1; d >>= 1) {
-      a_min = min(a_min, (uint32_t)__shfl_xor((int)a_min, d));
-      a_max = max(a_max, (uint32_t)__shfl_xor((int)a_max, d));
-    }
-    __shared__ uint32_t kred[2][kWaves];
-    if (l == 0) {
-      kred[0][wave] = a_min;
-      kred[1][wave] = a_max;
-    }
-    __syncthreads();
-    for (int w = 0; w < kWaves; ++w) {
-      kmin = min(kmin, kred[0][w]);
-      kmax = max(kmax, kred[1][w]);
-    }
-    __syncthreads();
-  }
+// The kk-th largest of the order keys key(i), i in [0, n), among those with
+// pred(i), by 8-bit radix passes over key - kmin (kmin/kmax: the range of the
+// keys that pass pred).  Returns v; *need = kk - #{key > v}, the ties at v
+// that are kept.  hist holds >= 256 words of LDS.
+template <int NT, typename KeyF, typename PredF>
+__device__ uint32_t radix_kth(int n, int kk, uint32_t kmin, uint32_t kmax, KeyF key, PredF pred,
+                              uint32_t* hist, int* sel_bin, int* sel_above, int* need) {
   const uint32_t range = kmax - kmin;
   const int nbits = range == 0u ? 0 : 32 - __clz((int)range);
   uint32_t prefix = 0u, pmask = 0u;
   for (int shift = ((nbits + 7) & ~7) - 8; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0u;
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const float s = src[i];
-      if (vbin(s, lo, inv) != vb) continue;
-      const uint32_t rel = order_key(s) - kmin;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      if (!pred(i)) continue;
+      const uint32_t rel = key(i) - kmin;
       if ((rel & pmask) == prefix) atomicAdd(&hist[(rel >> shift) & 255u], 1u);
     }
     __syncthreads();
-    pick_from_top(hist, 256, kk, &sel_bin, &sel_above);
-    kk -= sel_above;
-    prefix |= (uint32_t)sel_bin << shift;
+    pick_from_top(hist, 256, kk, sel_bin, sel_above);
+    kk -= *sel_above;
+    prefix |= (uint32_t)*sel_bin << shift;
     pmask |= 0xFFu << shift;
     __syncthreads();
   }
-  const uint32_t v = kmin + prefix;
-  const int need = kk;
+  *need = kk;
+  return kmin + prefix;
+}
 
-  // 4. stable emission in position order
+// ---- single-workgroup select of one whole row (kFT threads) ----
+//   1. min / max of the row;  2. a 2048-bin value histogram gives the bin
+//   holding the k-th best;  3. exact radix select on the order keys of that
+//   bin's entries;  4. stable emission in position order.
+__device__ void select_row_single(const float* __restrict__ src, int n, int k, int32_t* __restrict__ dst) {
+  __shared__ uint32_t hist[kSingleBins];
+  __shared__ float redf[kFT / kWave];
+  __shared__ uint32_t redu[kFT / kWave];
+  __shared__ int sel_bin, sel_above;
+  __shared__ int wave_keep[kFT / kWave], wave_eq[kFT / kWave];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+
+  float a = INFINITY, b = -INFINITY;
+  for (int i = tid; i < n; i += kFT) {
+    const float s = src[i];
+    a = fminf(a, s);
+    b = fmaxf(b, s);
+  }
+  const float lo = block_reduce<kFT>(a, redf, MinOp{});
+  const float hi = block_reduce<kFT>(b, redf, MaxOp{});
+  const float inv = bin_scale(lo, hi, kSingleBins);
+
+  for (int i = tid; i < kSingleBins; i += kFT) hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += kFT) atomicAdd(&hist[vbin(src[i], lo, inv, kSingleBins)], 1u);
+  __syncthreads();
+  pick_from_top(hist, kSingleBins, k, &sel_bin, &sel_above);
+  const int vb = sel_bin;
+  const int kk = k - sel_above;
+  __syncthreads();
+
+  uint32_t a_min = 0xFFFFFFFFu, a_max = 0u;
+  for (int i = tid; i < n; i += kFT) {
+    const float s = src[i];
+    if (vbin(s, lo, inv, kSingleBins) == vb) {
+      const uint32_t key = order_key(s);
+      a_min = min(a_min, key);
+      a_max = max(a_max, key);
+    }
+  }
+  const uint32_t kmin = block_reduce<kFT>(a_min, redu, UMinOp{});
+  const uint32_t kmax = block_reduce<kFT>(a_max, redu, UMaxOp{});
+  int need = 0;
+  const uint32_t v = radix_kth<kFT>(
+      n, kk, kmin, kmax, [&](int i) { return order_key(src[i]); },
+      [&](int i) { return vbin(src[i], lo, inv, kSingleBins) == vb; }, hist, &sel_bin, &sel_above, &need);
+
   int out_base = 0, eq_base = 0;
-  for (int base = 0; base < n; base += kThreads) {
+  for (int base = 0; base < n; base += kFT) {
     const int i = base + tid;
     const bool in = i < n;
     const uint32_t key = in ? order_key(src[i]) : 0u;
@@ -188,21 +228,325 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float* __rest
     __syncthreads();
     int keep_before = out_base;
     for (int w = 0; w < wave; ++w) keep_before += wave_keep[w];
-    if (keep) dst[keep_before + wave_prefix(km)] = i;
+    const int o = keep_before + wave_prefix(km);
+    if (keep && o < k) dst[o] = i;
     int kt = 0, et = 0;
-    for (int w = 0; w < kWaves; ++w) { kt += wave_keep[w]; et += wave_eq[w]; }
+    for (int w = 0; w < kFT / kWave; ++w) { kt += wave_keep[w]; et += wave_eq[w]; }
     out_base += kt;
     eq_base += et;
     __syncthreads();
   }
 }
 
+__device__ void write_trivial(int32_t* dst, int n, int k) {
+  for (int i = threadIdx.x; i < k; i += blockDim.x) dst[i] = i < n ? i : -1;
+}
+
+__global__ __launch_bounds__(kFT) void topk_rows_single_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               int32_t* __restrict__ idx, int n_q,
+                                                               int64_t q_start, int k) {
+  const int row = blockIdx.x;
+  const int n = row_len(row, n_q, q_start);
+  int32_t* dst = idx + (int64_t)row * k;
+  if (n <= k) {
+    write_trivial(dst, n, k);
+    return;
+  }
+  select_row_single(scores + (int64_t)row * ld, n, k, dst);
+}
+
+// ---- chunked passes ----
+
+struct ChunkArgs {
+  const float* scores;
+  int64_t ld;
+  int n_q;
+  int64_t q_start;
+  int k;
+  int G;           // chunks per row (of the longest row)
+  int vec;         // rows are 16-byte aligned: load float4
+  float2* rng;     // [rows][G]
+  uint32_t* hist;  // [rows][G][kVB]
+  int32_t* off;    // [rows][G]
+  RowSel* sel;     // [rows]
+  uint2* cand;     // [rows][kCap]
+};
+
+// This thread's kPT scores, positions i0 .. i0 + kPT - 1 (entries at or
+// beyond n are not read and must be masked by the caller).
+__device__ __forceinline__ void load_run(const float* __restrict__ row, int i0, int n, bool vec,
+                                         float (&v)[kPT]) {
+  if (vec && i0 + kPT <= n) {
+#pragma unroll
+    for (int j = 0; j < kPT / 4; ++j) {
+      const float4 x = *reinterpret_cast<const float4*>(row + i0 + 4 * j);
+      v[4 * j] = x.x;
+      v[4 * j + 1] = x.y;
+      v[4 * j + 2] = x.z;
+      v[4 * j + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) v[j] = i0 + j < n ? row[i0 + j] : 0.0f;
+  }
+}
+
+// lo / inv of a row from its chunks' ranges (all threads of the block).
+template <int NT>
+__device__ __forceinline__ void row_binning(const float2* rng, int G, float* red, float& lo, float& inv) {
+  float a = INFINITY, b = -INFINITY;
+  for (int g = threadIdx.x; g < G; g += NT) {
+    const float2 r = rng[g];
+    a = fminf(a, r.x);
+    b = fmaxf(b, r.y);
+  }
+  lo = block_reduce<NT>(a, red, MinOp{});
+  const float hi = block_reduce<NT>(b, red, MaxOp{});
+  inv = bin_scale(lo, hi, kVB);
+}
+
+__global__ __launch_bounds__(kCT) void tk_range_kernel(ChunkArgs a) {
+  __shared__ float red[kCT / kWave];
+  const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
+  const int n = row_len(row, a.n_q, a.q_start);
+  const int base = g * kChunk;
+  if (n <= a.k || base >= n) return;
+  const int i0 = base + threadIdx.x * kPT;
+  float v[kPT];
+  load_run(a.scores + (int64_t)row * a.ld, i0, n, a.vec, v);
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kPT; ++j)
+    if (i0 + j < n) {
+      mn = fminf(mn, v[j]);
+      mx = fmaxf(mx, v[j]);
+    }
+  mn = block_reduce<kCT>(mn, red, MinOp{});
+  mx = block_reduce<kCT>(mx, red, MaxOp{});
+  if (threadIdx.x == 0) a.rng[(int64_t)row * a.G + g] = make_float2(mn, mx);
+}
+
+__global__ __launch_bounds__(kCT) void tk_hist_kernel(ChunkArgs a) {
+  __shared__ uint32_t h[kVB];
+  __shared__ float red[kCT / kWave];
+  const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
+  const int n = row_len(row, a.n_q, a.q_start);
+  const int base = g * kChunk;
+  if (n <= a.k || base >= n) return;
+  const int i0 = base + threadIdx.x * kPT;
+  float v[kPT];
+  load_run(a.scores + (int64_t)row * a.ld, i0, n, a.vec, v);
+  for (int i = threadIdx.x; i < kVB; i += kCT) h[i] = 0u;
+  float lo, inv;
+  row_binning<kCT>(a.rng + (int64_t)row * a.G, (n + kChunk - 1) / kChunk, red, lo, inv);
+#pragma unroll
+  for (int j = 0; j < kPT; ++j)
+    if (i0 + j < n) atomicAdd(&h[vbin(v[j], lo, inv, kVB)], 1u);
+  __syncthreads();
+  uint32_t* dst = a.hist + ((int64_t)row * a.G + g) * kVB;
+  for (int i = threadIdx.x; i < kVB; i += kCT) dst[i] = h[i];
+}
+
+__global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
+  __shared__ float red[kST / kWave];
+  __shared__ int redi[kST / kWave];
+  __shared__ int sh_vb, sh_above, sh_h;
+  __shared__ int cnt[kST];                       // per-chunk counts, kST at a time
+  const int row = blockIdx.x, tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+  const int n = row_len(row, a.n_q, a.q_start);
+  if (n <= a.k) {
+    if (tid == 0) a.sel[row] = RowSel{0.0f, 0.0f, 0, kTrivial};
+    return;
+  }
+  const int Gr = (n + kChunk - 1) / kChunk;
+  float lo, inv;
+  row_binning<kST>(a.rng + (int64_t)row * a.G, Gr, red, lo, inv);
+
+  // row histogram: bins 4*tid .. 4*tid + 3
+  const uint32_t* hb = a.hist + (int64_t)row * a.G * kVB;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int g = 0; g < Gr; ++g) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(hb + (int64_t)g * kVB + 4 * tid);
+    acc += x;
+  }
+  const int tot = (int)(acc.x + acc.y + acc.z + acc.w);
+  // entries in bins above this thread's: total minus inclusive prefix
+  int all;
+  const int before = block_excl_scan<kST>(tot, redi, &all);
+  int ab = all - before - tot;
+  const int hs[4] = {(int)acc.x, (int)acc.y, (int)acc.z, (int)acc.w};
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    if (ab < a.k && a.k <= ab + hs[j]) {
+      sh_vb = 4 * tid + j;
+      sh_above = ab;
+      sh_h = hs[j];
+    }
+    ab += hs[j];
+  }
+  __syncthreads();
+  const int vb = sh_vb;
+  const int m = sh_above + sh_h;
+  if (m > kCap) {
+    if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, kFallback};
+    return;
+  }
+  // per-chunk counts of bins >= vb (one wave per chunk, 16 bins per lane),
+  // then their exclusive prefix in chunk order, kST chunks at a time
+  int carry = 0;
+  for (int g0 = 0; g0 < Gr; g0 += kST) {
+    const int gn = min(kST, Gr - g0);
+    for (int gi = wave; gi < gn; gi += kST / kWave) {
+      const uint32_t* hc = hb + (int64_t)(g0 + gi) * kVB + 16 * l;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(hc + 4 * j);
+        const int b0 = 16 * l + 4 * j;
+        c += (b0 >= vb ? (int)x.x : 0) + (b0 + 1 >= vb ? (int)x.y : 0) +
+             (b0 + 2 >= vb ? (int)x.z : 0) + (b0 + 3 >= vb ? (int)x.w : 0);
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+      if (l == 0) cnt[gi] = c;
+    }
+    __syncthreads();
+    const int c = tid < gn ? cnt[tid] : 0;
+    int chunk_tot;
+    const int ex = block_excl_scan<kST>(c, redi, &chunk_tot);
+    if (tid < gn) a.off[(int64_t)row * a.G + g0 + tid] = carry + ex;
+    carry += chunk_tot;
+  }
+  if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, m};
+}
+
+__global__ __launch_bounds__(kCT) void tk_collect_kernel(ChunkArgs a) {
+  __shared__ int redi[kCT / kWave];
+  const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
+  const int n = row_len(row, a.n_q, a.q_start);
+  const int base = g * kChunk;
+  if (n <= a.k || base >= n) return;
+  const RowSel rs = a.sel[row];
+  if (rs.m < 0) return;
+  const int i0 = base + threadIdx.x * kPT;
+  float v[kPT];
+  load_run(a.scores + (int64_t)row * a.ld, i0, n, a.vec, v);
+  uint32_t take = 0u;
+#pragma unroll
+  for (int j = 0; j < kPT; ++j)
+    if (i0 + j < n && vbin(v[j], rs.lo, rs.inv, kVB) >= rs.vb) take |= 1u << j;
+  int total;
+  const int ex = block_excl_scan<kCT>(__popc(take), redi, &total);
+  uint2* dst = a.cand + (int64_t)row * kCap;
+  int o = a.off[(int64_t)row * a.G + g] + ex;
+#pragma unroll
+  for (int j = 0; j < kPT; ++j)
+    if ((take & (1u << j)) && o < rs.m) dst[o++] = make_uint2(order_key(v[j]), (uint32_t)(i0 + j));
+}
+
+__global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __restrict__ idx) {
+  __shared__ uint32_t ck[kCap];
+  __shared__ int cp[kCap];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t redu[kFT / kWave];
+  __shared__ int redi[kFT / kWave];
+  __shared__ int sel_bin, sel_above;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = row_len(row, a.n_q, a.q_start);
+  int32_t* dst = idx + (int64_t)row * a.k;
+  const RowSel rs = a.sel[row];
+  if (rs.m == kTrivial) {
+    write_trivial(dst, n, a.k);
+    return;
+  }
+  if (rs.m == kFallback) {
+    select_row_single(a.scores + (int64_t)row * a.ld, n, a.k, dst);
+    return;
+  }
+  const int m = rs.m;
+  const uint2* src = a.cand + (int64_t)row * kCap;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = tid; i < m; i += kFT) {
+    const uint2 e = src[i];
+    ck[i] = e.x;
+    cp[i] = (int)e.y;
+    kmin = min(kmin, e.x);
+    kmax = max(kmax, e.x);
+  }
+  kmin = block_reduce<kFT>(kmin, redu, UMinOp{});
+  kmax = block_reduce<kFT>(kmax, redu, UMaxOp{});   // its barriers publish ck / cp
+  int need = 0;
+  const uint32_t v = radix_kth<kFT>(
+      m, a.k, kmin, kmax, [&](int i) { return ck[i]; }, [](int) { return true; }, hist, &sel_bin,
+      &sel_above, &need);
+
+  // stable emission: thread t owns list entries [t*P, t*P + P)
+  const int P = (m + kFT - 1) / kFT;
+  const int e0 = min(m, tid * P), e1 = min(m, e0 + P);
+  int eq = 0;
+  for (int i = e0; i < e1; ++i) eq += ck[i] == v;
+  int tot;
+  int eq_rank = block_excl_scan<kFT>(eq, redi, &tot);
+  int keep = 0;
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t key = ck[i];
+    keep += key > v || (key == v && eq_rank++ < need);
+  }
+  int out = block_excl_scan<kFT>(keep, redi, &tot);
+  eq_rank -= eq;
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t key = ck[i];
+    if ((key > v || (key == v && eq_rank++ < need)) && out < a.k) dst[out++] = cp[i];
+  }
+}
+
+int64_t chunks_per_row(int64_t max_n) { return (max_n + kChunk - 1) / kChunk; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
+size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k) {
+  if (rows >= kMultiRowLimit || max_n <= k) return 0;
+  const size_t G = (size_t)chunks_per_row(max_n);
+  return align256((size_t)rows * G * sizeof(float2)) + align256((size_t)rows * G * kVB * 4) +
+         align256((size_t)rows * G * 4) + align256((size_t)rows * sizeof(RowSel)) +
+         align256((size_t)rows * kCap * sizeof(uint2));
+}
+
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, hipStream_t s) {
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kThreads), 0, s, scores, ld, idx, n_q,
-                     q_start, k);
+                            int64_t q_start, int k, void* ws, hipStream_t s) {
+  const int64_t max_n = q_start + n_q;
+  if (topk_rows_ws_bytes(rows, max_n, k) == 0) {
+    hipLaunchKernelGGL(topk_rows_single_kernel, dim3(rows), dim3(kFT), 0, s, scores, ld, idx, n_q,
+                       q_start, k);
+    return hipGetLastError();
+  }
+  if (ws == nullptr) return hipErrorInvalidValue;
+  ChunkArgs a{};
+  a.scores = scores;
+  a.ld = ld;
+  a.n_q = n_q;
+  a.q_start = q_start;
+  a.k = k;
+  a.G = (int)chunks_per_row(max_n);
+  a.vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0) ? 1 : 0;
+  char* p = static_cast<char*>(ws);
+  a.rng = reinterpret_cast<float2*>(p);
+  p += align256((size_t)rows * a.G * sizeof(float2));
+  a.hist = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * a.G * kVB * 4);
+  a.off = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)rows * a.G * 4);
+  a.sel = reinterpret_cast<RowSel*>(p);
+  p += align256((size_t)rows * sizeof(RowSel));
+  a.cand = reinterpret_cast<uint2*>(p);
+  const dim3 chunk_grid((unsigned)((int64_t)rows * a.G));
+  hipLaunchKernelGGL(tk_range_kernel, chunk_grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(tk_hist_kernel, chunk_grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(tk_select_kernel, dim3(rows), dim3(kST), 0, s, a);
+  hipLaunchKernelGGL(tk_collect_kernel, chunk_grid, dim3(kCT), 0, s, a);
+  hipLaunchKernelGGL(tk_finish_kernel, dim3(rows), dim3(kFT), 0, s, a, idx);
   return hipGetLastError();
 }
 

@@ -1,0 +1,87 @@
+"""Row top-k over caller-provided fp32 scores (ix_topk_scores), on every
+select path: the chunked multi-workgroup select for few long rows (with its
+whole-row fallback when the k-th best sits in an over-full value bin), the
+single-workgroup select for many rows, unaligned row strides and rows short
+enough to keep every position.  Compared with the oracle's stable sort,
+element for element."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import ensure_lib, host
+from oracle import dsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ix():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_lib()
+    import long_context_sparse_ix_amd as m
+    return m
+
+
+def _check(ix, scores, k, q_start, kv_len, rows=None):
+    B, n_q, _ = scores.shape
+    idx = torch.full((B, n_q, k), -7, dtype=torch.int32, device="cuda")
+    print(f"[topk] B={B} n_q={n_q} ld={scores.shape[2]} kv_len={kv_len} q_start={q_start} k={k}", flush=True)
+    ix.ix_topk_scores(scores, idx, q_start=q_start, kv_len=kv_len)
+    torch.cuda.synchronize()
+    s, got = host(scores), host(idx)
+    for b in range(B):
+        for t in (range(n_q) if rows is None else rows):
+            p = q_start + t
+            np.testing.assert_array_equal(got[b, t], O.select_topk(s[b, t, :p + 1].astype(np.float64), k),
+                                          err_msg=f"row b={b} t={t}")
+
+
+def test_chunked_long_rows_normal(ix):
+    g = torch.Generator(device="cuda").manual_seed(11)
+    L = 200_003
+    scores = torch.randn((4, 1, L), generator=g, device="cuda")
+    _check(ix, scores, 2048, L - 1, L)
+
+
+def test_chunked_long_rows_integer_ties(ix):
+    g = torch.Generator(device="cuda").manual_seed(12)
+    L = 70_000
+    scores = torch.randint(-300, 300, (3, 2, L), generator=g, device="cuda").float()
+    _check(ix, scores, 2048, L - 2, L)
+
+
+def test_chunked_unaligned_stride(ix):
+    g = torch.Generator(device="cuda").manual_seed(13)
+    L = 30_001
+    base = torch.randn((2, 1, L + 1), generator=g, device="cuda")
+    _check(ix, base, 1000, L - 1, L)       # ld = L + 1: rows not 16-byte aligned
+
+
+def test_chunked_fallback_flat_rows(ix):
+    """Every score equal, or one outlier stretching the range: the k-th best
+    shares its bin with far more than the candidate capacity."""
+    L = 40_000
+    flat = torch.full((1, 1, L), 3.25, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(14)
+    outlier = torch.randn((1, 1, L), generator=g, device="cuda")
+    outlier[0, 0, 123] = 1e30
+    signed_zero = torch.zeros((1, 1, L), device="cuda")
+    signed_zero[0, 0, ::3] = -0.0
+    for s in (flat, outlier, signed_zero):
+        _check(ix, s, 2048, L - 1, L)
+
+
+def test_chunked_ragged_rows_with_short_prefix(ix):
+    """Rows 0.. of a prefill chunk: the first rows keep every position."""
+    g = torch.Generator(device="cuda").manual_seed(15)
+    n_q = 600
+    scores = torch.randn((1, n_q, n_q), generator=g, device="cuda")
+    _check(ix, scores, 256, 0, n_q)
+
+
+def test_single_workgroup_many_rows(ix):
+    g = torch.Generator(device="cuda").manual_seed(16)
+    n_q, L = 1100, 3000
+    scores = torch.randn((1, n_q, L), generator=g, device="cuda")
+    _check(ix, scores, 512, L - n_q, L, rows=[0, 1, 517, 1099])
