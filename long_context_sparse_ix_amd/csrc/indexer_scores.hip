@@ -21,9 +21,10 @@ namespace {
 constexpr int kTileKeys = 64;
 constexpr int kTilesPerWave = 16;           // 1024 keys per wave
 constexpr int kWavesPerWG = 4;
+constexpr int kDepth = 4;                   // tiles per wave in registers: 1 in use, 3 in flight
 
 template <int HT, int KS, bool FP8>
-__global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scores_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(ScoreArgs a) {
   constexpr int d = KS * 16;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 31, hf = l >> 5;
@@ -32,6 +33,59 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   const int64_t p = a.q_start + t;
   const int64_t s_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kTilesPerWave * kTileKeys;
   if (s_begin > p) return;
+  const int n_tiles = (int)min<int64_t>(kTilesPerWave, (p - s_begin) / kTileKeys + 1);
+
+  const float* scale_b = FP8 ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
+  float* out = a.scores + (int64_t)row * a.ld;
+
+  // Raw key bytes of one 64-key tile for this lane: key s0 + nt*32 + m, bytes
+  // (fp8) or elements (bf16) [hf*d/2, +d/2), plus (fp8) the scale of key
+  // s0 + l.  kDepth - 1 tiles are in flight while one is widened and used.
+  constexpr int RAW = FP8 ? (KS % 2 == 0 ? KS / 2 : KS) : KS;   // 16-byte (or 8-byte) pieces per half
+  typedef typename std::conditional<FP8 && (KS % 2 != 0), u32x2, u32x4>::type piece_t;
+  piece_t raw[kDepth][2][RAW];
+  float sc[kDepth];
+  auto load_raw = [&](int64_t s0, piece_t (&rw)[2][RAW], float& scl) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      int64_t s = s0 + nt * 32 + m;
+      if (s > p) s = p;                       // stays inside the cache; masked below
+      const unsigned char* kr = static_cast<const unsigned char*>(a.keys) +
+                                ((int64_t)b * a.key_bstride + s * d + hf * (d / 2)) * (FP8 ? 1 : 2);
+#pragma unroll
+      for (int c = 0; c < RAW; ++c) rw[nt][c] = *reinterpret_cast<const piece_t*>(kr + c * sizeof(piece_t));
+    }
+    if constexpr (FP8) scl = scale_b[min<int64_t>(s0 + l, p)];
+  };
+  auto widen = [&](const piece_t (&rw)[2][RAW], bf16x8 (&bfr)[2][KS]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if constexpr (FP8 && KS % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < KS / 2; ++c) {
+          const u32x4 v = rw[nt][c];
+          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+          const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
+          bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+          bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
+        }
+      } else if constexpr (FP8) {
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          const u32x2 v = rw[nt][c];
+          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+          bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = __builtin_bit_cast(bf16x8, rw[nt][ks]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kDepth - 1; ++j)
+    if (j < n_tiles) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
 
   bf16x8 qf[HT][KS];
   float wr[HT][16];
@@ -51,91 +105,47 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
       }
     }
   }
-  const float* scale_b = FP8 ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
-  float* out = a.scores + (int64_t)row * a.ld;
 
-  // Raw key bytes of one 64-key tile for this lane: key s0 + nt*32 + m, bytes
-  // (fp8) or elements (bf16) [hf*d/2, +d/2).  The next tile's raw bytes are
-  // loaded while the current one is widened and multiplied.
-  constexpr int RAW = FP8 ? (KS % 2 == 0 ? KS / 2 : KS) : KS;   // 16-byte (or 8-byte) pieces per half
-  typedef typename std::conditional<FP8 && (KS % 2 != 0), u32x2, u32x4>::type piece_t;
-  piece_t raw_cur[2][RAW], raw_nxt[2][RAW];
-  auto load_raw = [&](int64_t s0, piece_t (&raw)[2][RAW]) {
+  for (int j0 = 0; j0 < n_tiles; j0 += kDepth) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      int64_t s = s0 + nt * 32 + m;
-      if (s > p) s = p;                       // stays inside the cache; masked below
-      const unsigned char* kr = static_cast<const unsigned char*>(a.keys) +
-                                ((int64_t)b * a.key_bstride + s * d + hf * (d / 2)) * (FP8 ? 1 : 2);
+    for (int u = 0; u < kDepth; ++u) {
+      const int j = j0 + u;
+      if (j < n_tiles) {
+        const int jn = j + kDepth - 1;
+        if (jn < n_tiles)
+          load_raw(s_begin + (int64_t)jn * kTileKeys, raw[(u + kDepth - 1) % kDepth], sc[(u + kDepth - 1) % kDepth]);
+        const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
+        bf16x8 bfr[2][KS];
+        widen(raw[u], bfr);
+        f32x16 acc[2][HT];
 #pragma unroll
-      for (int c = 0; c < RAW; ++c) raw[nt][c] = *reinterpret_cast<const piece_t*>(kr + c * sizeof(piece_t));
-    }
-  };
-  auto widen = [&](const piece_t (&raw)[2][RAW], bf16x8 (&bfr)[2][KS]) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if constexpr (FP8 && KS % 2 == 0) {
+          for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int c = 0; c < KS / 2; ++c) {
-          const u32x4 v = raw[nt][c];
-          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-          const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
-          bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
-          bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
+            for (int ht = 0; ht < HT; ++ht)
+              acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks],
+                                                                    ks == 0 ? f32x16{} : acc[nt][ht], 0, 0, 0);
+        float part[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), sacc[r & 3]);
+          part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         }
-      } else if constexpr (FP8) {
-#pragma unroll
-        for (int c = 0; c < KS; ++c) {
-          const u32x2 v = raw[nt][c];
-          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-          bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                         __float_as_uint(part[1]), false, false);
+        float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int64_t s = s0 + l;
+        if (s <= p) {
+          if constexpr (FP8) score *= sc[u];
+          out[s] = score;
         }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = __builtin_bit_cast(bf16x8, raw[nt][ks]);
       }
     }
-  };
-
-  load_raw(s_begin, raw_cur);
-  for (int j = 0; j < kTilesPerWave; ++j) {
-    const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
-    if (s0 > p) break;
-    const bool more = j + 1 < kTilesPerWave && s0 + kTileKeys <= p;
-    if (more) load_raw(s0 + kTileKeys, raw_nxt);
-    bf16x8 bfr[2][KS];
-    widen(raw_cur, bfr);
-    f32x16 acc[2][HT];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks],
-                                                                ks == 0 ? f32x16{} : acc[nt][ht], 0, 0, 0);
-    float part[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), sacc[r & 3]);
-      part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
-    }
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
-                                                     __float_as_uint(part[1]), false, false);
-    float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int64_t s = s0 + l;
-    if (s <= p) {
-      if constexpr (FP8) score *= scale_b[s];
-      out[s] = score;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int c = 0; c < RAW; ++c) raw_cur[nt][c] = raw_nxt[nt][c];
   }
 }
 

@@ -100,26 +100,35 @@ size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
   return score_bytes(p) + topk_ws(p);
 }
 
-int attn_splits(const ix_problem* p, const ix_attn_in* in) {
-  if (in->kv_splits > 0) return in->kv_splits;
-  const int64_t rows = (int64_t)p->batch * p->n_q;
-  if (rows >= 2048) return 1;
-  int64_t s = (2048 + rows - 1) / rows;
-  const int64_t by_slots = p->k / 128 > 1 ? p->k / 128 : 1;   // >= 128 slots per split
-  if (s > by_slots) s = by_slots;
-  if (s > 64) s = 64;
-  return (int)(s < 1 ? 1 : s);
-}
+// Work split of the attention.  Many rows: one wave per row.  Few rows: four
+// waves share every (row, split) and merge in LDS, and the k slots of a row are
+// cut into enough splits for about 1024 waves, each with >= 64 slots; the
+// splits' partials are merged by a second kernel.
+struct AttnPlan {
+  int splits, slots_per_split, wpi;
+};
 
-int splits_effective(const ix_problem* p, const ix_attn_in* in) {
-  int s = attn_splits(p, in);
-  // never more splits than 16-slot steps
-  const int steps = (p->k + 15) / 16;
-  return s > steps ? steps : s;
+AttnPlan attn_plan(const ix_problem* p, const ix_attn_in* in) {
+  const int64_t rows = (int64_t)p->batch * p->n_q;
+  AttnPlan pl{};
+  pl.wpi = rows < 1024 ? 4 : 1;
+  int64_t s = in->kv_splits;
+  if (s <= 0) {
+    s = pl.wpi == 1 ? 1 : (1024 + rows * 4 - 1) / (rows * 4);
+    const int64_t by_slots = p->k / (64 * pl.wpi);
+    if (s > by_slots) s = by_slots;
+    if (s > 64) s = 64;
+    if (s < 1) s = 1;
+  }
+  const int64_t steps = (p->k + 15) / 16;                  // 16-slot steps
+  const int64_t per_wave = (steps + s * pl.wpi - 1) / (s * pl.wpi);
+  pl.slots_per_split = (int)(per_wave * 16 * pl.wpi);
+  pl.splits = (int)((p->k + pl.slots_per_split - 1) / pl.slots_per_split);   // none empty, <= s
+  return pl;
 }
 
 size_t attn_ws(const ix_problem* p, const ix_attn_in* in) {
-  const int s = splits_effective(p, in);
+  const int s = attn_plan(p, in).splits;
   if (s <= 1) return 0;
   const size_t items = (size_t)p->batch * p->n_q * s * 16;
   return round_up(items * in->d_v * 4) + round_up(items * 2 * 4);
@@ -195,11 +204,10 @@ int32_t run_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, 
   a.n_q = p->n_q;
   a.Hq = in->q_heads;
   a.k = p->k;
-  a.splits = splits_effective(p, in);
-  const int steps = (p->k + 15) / 16;
-  a.slots_per_split = ((steps + a.splits - 1) / a.splits) * 16;
-  // recompute so that no split is empty
-  a.splits = (p->k + a.slots_per_split - 1) / a.slots_per_split;
+  const AttnPlan pl = attn_plan(p, in);
+  a.splits = pl.splits;
+  a.slots_per_split = pl.slots_per_split;
+  a.wpi = pl.wpi;
   const float sm = in->sm_scale > 0.0f ? in->sm_scale : 1.0f / std::sqrt((float)in->d_qk);
   a.scale_log2 = sm * 1.4426950408889634f;
   if (a.splits > 1) {

@@ -64,6 +64,7 @@ struct AttnArgs {
   int64_t kv_bstride;     // elements
   int64_t kv_len;
   int rows, n_q, Hq, k, splits, slots_per_split;
+  int wpi;                // waves per (row, split): 1, or 4 sharing the split's slots
   float scale_log2;       // sm_scale * log2(e)
 };
 bool attn_shape_supported(int d_qk, int d_v);

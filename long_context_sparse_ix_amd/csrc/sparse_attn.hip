@@ -23,8 +23,10 @@
 //     O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16);
 //   * online softmax in base 2, rescaling the accumulators only when some
 //     head's running max grows;
-//   * with several slot-range splits per row (few-row decode), partial
-//     (o, m, l) go to the workspace and a combine kernel merges them.
+//   * few rows (decode): the four waves of a workgroup share one (row, split),
+//     each taking a quarter of its slots, and merge their (o, m, l) through
+//     LDS; with several splits per row the merged partials go to the
+//     workspace and a combine kernel merges them.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -45,15 +47,27 @@ struct VTile {
   static constexpr int bytes = 16 * stride_dw * 4;
 };
 
-template <int KS, int MT>
+// LDS of a workgroup: the waves' value tiles, reused after the slot loop as
+// the buffer of the in-workgroup merge (two waves' accumulators), then the
+// merge's per-wave (m, l) of every head.
+template <int MT>
+struct AttnLds {
+  static constexpr int tiles = kWavesPerWG * VTile<MT>::bytes;
+  static constexpr int merge = 2 * MT * kWave * 16;
+  static constexpr int stat_off = ((tiles > merge ? tiles : merge) + 15) / 16 * 16;
+  static constexpr int bytes = stat_off + 2 * kWavesPerWG * 16 * 4;
+};
+
+template <int KS, int MT, int WPI>
 __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(AttnArgs a) {
   constexpr int D = 32 * KS, QD = 8 * KS, Dv = 16 * MT;
   using V = VTile<MT>;
+  static_assert(WPI == 1 || WPI == kWavesPerWG, "a (row, split) has one wave or the whole workgroup");
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int n16 = l & 15, g = l >> 4;
-  const int item = blockIdx.x * kWavesPerWG + wave;
-  if (item >= a.rows * a.splits) return;
+  const int item = WPI == 1 ? blockIdx.x * kWavesPerWG + wave : blockIdx.x;
+  if (item >= a.rows * a.splits) return;     // whole workgroup when WPI > 1
   const int r = item / a.splits, sp = item % a.splits;
   const int b = r / a.n_q;
   uint16_t* vl = reinterpret_cast<uint16_t*>(smem + wave * V::bytes);
@@ -68,8 +82,13 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
       qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * ks) : bf16x8{};
   }
 
-  const int j0 = sp * a.slots_per_split;
-  const int j1 = min(a.k, j0 + a.slots_per_split);
+  int j0 = sp * a.slots_per_split;
+  int j1 = min(a.k, j0 + a.slots_per_split);
+  if (WPI > 1) {                              // this wave's quarter of the split
+    const int per = a.slots_per_split / WPI;
+    j0 = min(j1, j0 + wave * per);
+    j1 = min(j1, j0 + per);
+  }
   const int32_t* irow = a.idx + (int64_t)r * a.k;
   const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride + g * QD;
 
@@ -166,6 +185,48 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   }
 
   // oacc[mt][i] = O^T[dv = 16mt + 4g + i][head n16]
+  if constexpr (WPI > 1) {
+    // merge the waves: common max per head, rescale, then sum the
+    // accumulators pairwise through LDS (waves 2,3 -> 0,1, then 1 -> 0)
+    float* st_m = reinterpret_cast<float*>(smem + AttnLds<MT>::stat_off);
+    float* st_l = st_m + kWavesPerWG * 16;
+    f32x4* buf = reinterpret_cast<f32x4*>(smem);
+    __syncthreads();                          // every wave is done with its tile
+    if (g == 0) {
+      st_m[wave * 16 + n16] = m_run;
+      st_l[wave * 16 + n16] = l_run;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, st_m[w * 16 + n16]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWG; ++w) {
+      const float mw = st_m[w * 16 + n16];
+      L += mw == -INFINITY ? 0.0f : st_l[w * 16 + n16] * exp2f(mw - M);
+    }
+    const float sc = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= sc;
+    if (wave >= 2)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) buf[((wave - 2) * MT + mt) * kWave + l] = oacc[mt];
+    __syncthreads();
+    if (wave < 2)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[mt] += buf[(wave * MT + mt) * kWave + l];
+    __syncthreads();
+    if (wave == 1)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) buf[mt * kWave + l] = oacc[mt];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] += buf[mt * kWave + l];
+    m_run = M;
+    l_run = L;
+  }
   if (a.splits == 1) {
     if (hq_ok) {
       const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -234,16 +295,23 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int Dv) {
     a.lse[(int64_t)r * a.Hq + h] = stat[1] > 0.0f ? (stat[0] + log2f(stat[1])) * kLn2 : -INFINITY;
 }
 
-template <int KS, int MT>
-hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)kWavesPerWG * VTile<MT>::bytes;
-  const void* fn = reinterpret_cast<const void*>(&sparse_attn_kernel<KS, MT>);
+template <int KS, int MT, int WPI>
+hipError_t launch_attn_w(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = WPI == 1 ? (size_t)kWavesPerWG * VTile<MT>::bytes : (size_t)AttnLds<MT>::bytes;
+  const void* fn = reinterpret_cast<const void*>(&sparse_attn_kernel<KS, MT, WPI>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t items = (int64_t)a.rows * a.splits;
-  dim3 grid((unsigned)((items + kWavesPerWG - 1) / kWavesPerWG));
-  hipLaunchKernelGGL((sparse_attn_kernel<KS, MT>), grid, dim3(kWavesPerWG * kWave), lds, s, a);
-  e = hipGetLastError();
+  dim3 grid((unsigned)(WPI == 1 ? (items + kWavesPerWG - 1) / kWavesPerWG : items));
+  hipLaunchKernelGGL((sparse_attn_kernel<KS, MT, WPI>), grid, dim3(kWavesPerWG * kWave), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int KS, int MT>
+hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+  if (a.wpi != 1 && a.wpi != kWavesPerWG) return hipErrorInvalidValue;
+  if (a.wpi > 1 && a.slots_per_split % (16 * kWavesPerWG) != 0) return hipErrorInvalidValue;
+  hipError_t e = a.wpi == 1 ? launch_attn_w<KS, MT, 1>(a, s) : launch_attn_w<KS, MT, kWavesPerWG>(a, s);
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.rows * a.Hq)), dim3(128), 0, s, a, 16 * MT);
   return hipGetLastError();
