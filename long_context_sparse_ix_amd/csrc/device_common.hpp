@@ -75,6 +75,11 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   return v;
 }
 
+// max(x, 0) as one v_med3_f32 (x clamped to [0, +inf]).  fmaxf would add a
+// NaN-quieting max in front; the callers' inputs (MFMA dot products of finite
+// bf16 values) are never NaN.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }

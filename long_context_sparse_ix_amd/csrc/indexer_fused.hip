@@ -60,6 +60,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also drains every
+// outstanding global access of the wave (vmcnt(0)), which would wait for the
+// tile prefetched two steps ahead; the ring's own vmcnt waits cover global ->
+// LDS data, and candidate-buffer stores are private to their wave.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct Thresh {
   uint32_t v;   // order key of the k-th best entry
   int need;     // how many entries with key == v belong to the top k
@@ -333,7 +341,7 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r & 3] = fmaf(wr[ht][r], fmaxf(acc_epi[ht][r], 0.0f), s[r & 3]);
+      for (int r = 0; r < 16; ++r) s[r & 3] = fmaf(wr[ht][r], relu(acc_epi[ht][r]), s[r & 3]);
     part = (s[0] + s[1]) + (s[2] + s[3]);
   }
   if constexpr (MMA && EPI) {
@@ -480,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     sc_prev = sc_cur;
     if (more) wait_vmcnt<kLoads>();              // tile it+1 landed (it+2 may still fly)
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     slot = slot == 2 ? 0 : slot + 1;
   }
 

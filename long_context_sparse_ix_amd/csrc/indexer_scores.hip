@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], fmaxf(acc[nt][ht][r], 0.0f), sacc[r & 3]);
+            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], relu(acc[nt][ht][r]), sacc[r & 3]);
           part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
