@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   float* scale_lds = reinterpret_cast<float*>(smem + kRing * G::tile_bytes);       // [3][64]
   uint32_t* hist = reinterpret_cast<uint32_t*>(scale_lds + kRing * kTileKeys);     // [4][256]
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), l = tid & 63;
   const int m = l & 31, hf = l >> 5;
   const int b = blockIdx.y;
   const int row0 = (gridDim.x - 1 - blockIdx.x) * kRowsPerWG;
@@ -406,23 +406,39 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
 
   // Direct HBM -> LDS loads of tile `it` into ring slot `slot`: load j of this
   // wave fills LDS slots [J*n, J*n+n) (J = wave + 4j, n lanes) in lane order, so
-  // lane l fetches the global chunk that belongs in slot J*n + l.  Rows past
-  // the last key are clamped (their scores are masked).
+  // lane l fetches the global chunk that belongs in slot J*n + l (tile row r,
+  // chunk swz(r, slot % CPR); swz is an involution).  With several loads per
+  // wave (d >= 64) load j covers the 4 KB after load j-1 and the swizzle
+  // repeats, so one per-lane byte offset serves all of them.  Only the last,
+  // partial tile clamps its rows to the last key (their scores are masked).
+  static_assert(G::inst_per_wave == 1 || G::lanes_per_inst * 4 * 16 == 4096, "4 KB per load round");
+  const int key_off = [&] {
+    const int S = wave * G::lanes_per_inst + l;
+    const int r = S / G::CPR;
+    return (r * d + G::swz(r, S % G::CPR) * 8) * 2;
+  }();
+  const unsigned char* key_bytes = reinterpret_cast<const unsigned char*>(keys_b);
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
+    const bool full = s0 + kTileKeys <= n_keys;
+    const unsigned char* tile = key_bytes + (int64_t)s0 * d * 2;
 #pragma unroll
     for (int j = 0; j < G::inst_per_wave; ++j) {
       const int J = wave + 4 * j;
-      const int S = J * G::lanes_per_inst + l;                 // LDS slot this lane fills
-      const int r = S / G::CPR, sl = S % G::CPR;
-      const int c = G::swz(r, sl);                             // swz is an involution
-      const uint16_t* src = keys_b + (int64_t)min(s0 + r, n_keys - 1) * d + c * 8;
+      const unsigned char* src;
+      if (full) {
+        src = tile + key_off + 4096 * j;
+      } else {
+        const int r = (J * G::lanes_per_inst + l) / G::CPR;
+        src = key_bytes + (int64_t)min(s0 + r, n_keys - 1) * d * 2 + (key_off + 4096 * j - r * d * 2);
+      }
       if (G::lanes_per_inst == 64 || l < G::lanes_per_inst)
         __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16, 0, 0);
     }
     if constexpr (SCALE) {
-      const float* src = scale_b + min(s0 + 16 * wave + (l & 15), n_keys - 1);
+      const int sk = s0 + 16 * wave + (l & 15);
+      const float* src = scale_b + (full ? sk : min(sk, n_keys - 1));
       if (l < 16)
         __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4, 0, 0);
     }
@@ -449,17 +465,20 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     const bool mma = row_ok && it < n_tiles && it * kTileKeys <= p;
     const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
     const unsigned char* kb = key_lds0 + slot * G::tile_bytes;
+    // B operand of half 0 first (a stale, unused read when !mma), so its LDS
+    // latency hides behind the tile issue
+    bf16x8 bfr[KS];
+    read_bfrags<KS>(kb, 0, m, hf, bfr);
     const float sc_cur = SCALE ? scale_lds[slot * kTileKeys + l] : 1.0f;
     const bool more = it + 2 < n_tiles;
     if (more) issue_tile(it + 2, slot == 0 ? 2 : slot - 1);   // (slot + 2) % 3
 
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
-    bf16x8 bfr[KS];
     float part1 = 0.0f;
-    if (mma) read_bfrags<KS>(kb, 0, m, hf, bfr);
     if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, bfr, acc0, acc1);
     else if (mma) half_block<HT, KS, true, false>(qf, wr, bfr, acc0, acc1);
     else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, bfr, acc0, acc1);
+    read_bfrags<KS>(kb, 1, m, hf, bfr);          // half 1, in flight during the finish
 
     if (epi) {
       // finish tile it-1: lanes 0-31 take key half 0, lanes 32-63 half 1
@@ -469,8 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       if (SCALE) score *= sc_prev;
       const int s = (it - 1) * kTileKeys + l;
       if (s > p) score = -INFINITY;
-      if (cnt > C - kWave) shrink(cand, cnt, tau, vmax, a.k, keep_max, my_hist);
-      const bool pass = score > tau;
+      const bool pass = score > tau;             // room for 64: see the shrink below
       const uint64_t pm = __ballot(pass);
       if (pm) {
         if (pass) {
@@ -481,10 +499,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
-    if (mma) {
-      read_bfrags<KS>(kb, 1, m, hf, bfr);
-      part0 = half_block<HT, KS, true, true>(qf, wr, bfr, acc1, acc0);
-    }
+    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, bfr, acc1, acc0);
+    // keep room for the next tile's up to 64 appends (here, where no B
+    // fragments are live)
+    if (cnt > C - kWave) shrink(cand, cnt, tau, vmax, a.k, keep_max, my_hist);
     sc_prev = sc_cur;
     if (more) wait_vmcnt<kLoads>();              // tile it+1 landed (it+2 may still fly)
     else wait_vmcnt<0>();
