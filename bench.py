@@ -11,6 +11,8 @@ generated on the device before timing starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -23,6 +25,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_HBM_GBPS = 8000.0
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_prefill_l128k.json")
+ATTN_SOURCE = os.path.join(ROOT, "long_context_sparse_ix_amd", "csrc", "sparse_attn.hip")
+CAL_BYTES = 1 << 30            # plain device copy used to scale the HBM byte counters
 
 CONFIGS = {"tiny": "tiny_l1k_exact", "l16k": "prefill_l16k", "l128k": "prefill_l128k_2groups",
            "decode": "decode_b32_ctx200k", "chunk1m": "chunked_prefill_1m_8k"}
@@ -72,6 +78,64 @@ class Inputs:
                                                   device=dev)))
         self.idx_fs = torch.empty((w.roles.count("F"), w.batch, w.n_q, w.k), dtype=torch.int32, device=dev)
         self.idx_ff = torch.empty((n, w.batch, w.n_q, w.k), dtype=torch.int32, device=dev) if all_full else None
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def attention_bytes(w):
+    """Algorithmic bytes of one sparse-attention launch: gathered latent rows
+    plus every row's Q, O and index words."""
+    rows = w.batch * w.n_q
+    return (gathered_rows(w) * w.d_qk * 2 + rows * w.q_heads * (w.d_qk + w.d_v) * 2 + rows * w.k * 4)
+
+
+def load_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha(ATTN_SOURCE):
+        return None
+    return t
+
+
+def write_traffic(fetch_dir, write_dir, command):
+    """Turns two rocprofv3 --pmc runs of `bench.py --copy-calibration` (one
+    with FETCH_SIZE, one with WRITE_SIZE) into the traffic summary: the
+    attention kernel's KiB per dispatch, scaled by CAL_BYTES over what the
+    same counter reads for the calibration copy."""
+    def per_kernel(d, counter):
+        path = os.path.join(d, "pmc_counter_collection.csv")
+        att, cal = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if "sparse_attn_kernel" in r["Kernel_Name"]:
+                    att.append(v)
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    cal.append(v)
+        cal = sorted(cal)[-4:]                     # the CAL_BYTES copies are the largest
+        return sum(att) / len(att), sum(cal) / len(cal), len(att)
+    fa, fc, n = per_kernel(fetch_dir, "FETCH_SIZE")
+    wa, wc, _ = per_kernel(write_dir, "WRITE_SIZE")
+    f_fac, w_fac = CAL_BYTES / (fc * 1024), CAL_BYTES / (wc * 1024)
+    out = {"kernel": "sparse_attn_kernel", "workload": "prefill_l128k_2groups", "dispatches": n,
+           "fetch_kib_per_dispatch": fa, "write_kib_per_dispatch": wa,
+           "calibration": {"copy_bytes": CAL_BYTES, "fetch_kib": fc, "write_kib": wc,
+                           "fetch_factor": f_fac, "write_factor": w_fac},
+           "hbm_bytes_per_launch": fa * 1024 * f_fac + wa * 1024 * w_fac,
+           "source_sha256": source_sha(ATTN_SOURCE), "command": command}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def event_time(torch, fn, reps):
@@ -168,7 +232,15 @@ def main(argv=None):
     ap.add_argument("--sample-rows", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-full", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the run, copy a 1 GiB device buffer 4 times (HBM counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the attention traffic summary from two rocprofv3 --pmc output dirs")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, args.traffic_command)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -231,9 +303,20 @@ def main(argv=None):
     ix_flop = causal_pairs(w) * 2 * w.ix_heads * w.ix_dim
     ix_tflops = ix_flop / (ix_ms / 1e3) / 1e12
     g_rows = gathered_rows(w)
-    at_bytes = g_rows * w.d_qk * 2
+    at_bytes = attention_bytes(w)
     at_gbps = at_bytes / (at_ms / 1e3) / 1e9
     at_flop = g_rows * w.q_heads * 2 * (w.d_qk + w.d_v)
+
+    # standalone row top-k over materialised fp32 rows at the decode shape
+    # (32 rows of 200,001 scores): HBM fraction on one read of the rows
+    g = torch.Generator(device="cuda").manual_seed(0)
+    dk = synth.DECODE_B32
+    tk_scores = torch.randn((dk.batch, 1, dk.kv_len), generator=g, device="cuda")
+    tk_idx = torch.empty((dk.batch, 1, dk.k), dtype=torch.int32, device="cuda")
+    tk_ms = event_time(torch, lambda: ix.ix_topk_scores(tk_scores, tk_idx, q_start=dk.q_start, kv_len=dk.kv_len),
+                       max(args.kernel_reps, 10))
+    tk_bytes = dk.batch * (4 * dk.kv_len + 4 * dk.k)
+    del tk_scores
 
     allf_ms = None
     if not args.no_all_full:
@@ -243,6 +326,9 @@ def main(argv=None):
         # all-F baseline re-ran the F layers' slots; restore the F+3S indices
         run_group(fs_mask, inp.idx_fs)
         torch.cuda.synchronize()
+
+    tr = load_traffic()
+    traffic_bytes = None if tr is None else tr["hbm_bytes_per_launch"]
 
     rows = synth.sample_rows(w, args.sample_rows)
     result_cpu, parity = None, None
@@ -269,21 +355,32 @@ def main(argv=None):
                    "indexer": f"{w.ix_heads} heads x {w.ix_dim}, {w.key_dtype} keys",
                    "attention": f"{w.q_heads} heads over 1 latent head {w.d_qk} (V = first {w.d_v})"},
         "roofline": {"bound": "hbm", "achieved": at_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": at_gbps / PEAK_HBM_GBPS, "traffic": None,
-                     "kernel": "sparse_attn_kernel (gathered latent bytes per launch / launch time)"},
+                     "frac": at_gbps / PEAK_HBM_GBPS, "traffic": traffic_bytes,
+                     "kernel": "sparse_attn_kernel: (gathered latent rows + Q + O + idx bytes) per launch "
+                               "/ launch time; traffic = HBM bytes per launch from FETCH_SIZE + WRITE_SIZE",
+                     "algorithmic_bytes": at_bytes},
         "indexer": {"ms": ix_ms, "tflops": ix_tflops, "frac_bf16_peak": ix_tflops / PEAK_BF16_TFLOPS,
                     "frac_fp8_peak": ix_tflops / PEAK_FP8_TFLOPS, "flop": ix_flop,
                     "note": "fused score + streaming top-k, incl. fp8->bf16 key upcast"},
         "attention": {"ms_per_layer": at_ms, "tokens_per_s": w.batch * w.n_q / (at_ms / 1e3),
                       "gathered_GBps": at_gbps, "frac_hbm_peak": at_gbps / PEAK_HBM_GBPS,
                       "tflops": at_flop / (at_ms / 1e3) / 1e12},
+        "topk_standalone": {"workload": "32 rows x 200,001 fp32 scores, k=2048", "us": tk_ms * 1e3,
+                            "rows_per_s": dk.batch / (tk_ms / 1e3),
+                            "frac_hbm_peak": tk_bytes / (tk_ms / 1e3) / 1e9 / PEAK_HBM_GBPS},
         "group": {"ms_fsss": ms_step / n_groups, "ms_all_full": None if allf_ms is None else allf_ms / n_groups,
                   "speedup_vs_all_full": None if allf_ms is None else allf_ms / ms_step},
         "cpu_baseline": result_cpu,
         "parity": parity,
         "wall_s_timed": wall,
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     return 0
 
 
