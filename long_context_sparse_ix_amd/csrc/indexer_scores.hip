@@ -19,7 +19,7 @@ namespace ix {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kTilesPerWave = 16;           // 1024 keys per wave
+constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 1024 keys per wave
 constexpr int kWavesPerWG = 4;
 constexpr int kDepth = 4;                   // tiles per wave in registers: 1 in use, 3 in flight
 
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
     }
   }
 
+  float smin = INFINITY, smax = -INFINITY;     // range of this wave's scores
   for (int j0 = 0; j0 < n_tiles; j0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
@@ -143,9 +144,19 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
         if (s <= p) {
           if constexpr (FP8) score *= sc[u];
           out[s] = score;
+          smin = fminf(smin, score);
+          smax = fmaxf(smax, score);
         }
       }
     }
+  }
+  if (a.rng) {
+#pragma unroll
+    for (int dd = 32; dd >= 1; dd >>= 1) {
+      smin = fminf(smin, __shfl_xor(smin, dd));
+      smax = fmaxf(smax, __shfl_xor(smax, dd));
+    }
+    if (l == 0) a.rng[(int64_t)row * a.rng_stride + blockIdx.x * kWavesPerWG + wave] = make_float2(smin, smax);
   }
 }
 

@@ -89,6 +89,11 @@ size_t score_bytes(const ix_problem* p) {
 size_t topk_ws(const ix_problem* p) {
   return round_up(ix::topk_rows_ws_bytes(p->batch * p->n_q, p->q_start + p->n_q, p->k));
 }
+// per-wave score ranges written by the score kernel for the row select
+int rng_stride(const ix_problem* p) { return (int)((p->q_start + p->n_q + ix::kScoreSpan - 1) / ix::kScoreSpan); }
+size_t rng_bytes(const ix_problem* p) {
+  return round_up((size_t)p->batch * p->n_q * rng_stride(p) * 8);
+}
 
 size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
   if (use_fused(p, in)) {
@@ -97,7 +102,7 @@ size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
       need += round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
     return need;
   }
-  return score_bytes(p) + topk_ws(p);
+  return score_bytes(p) + rng_bytes(p) + topk_ws(p);
 }
 
 // Work split of the attention.  Many rows: one wave per row.  Few rows: four
@@ -183,10 +188,13 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
   a.q_start = p->q_start;
   a.n_q = p->n_q;
   a.H = in->heads;
+  a.rng = reinterpret_cast<float2*>(static_cast<char*>(ws) + score_bytes(p));
+  a.rng_stride = rng_stride(p);
   hipError_t e = ix::launch_indexer_scores(a, p->batch, in->dim, fp8, p->kv_len, s);
   if (e != hipSuccess) return hip_fail(e);
   e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
-                           static_cast<char*>(ws) + score_bytes(p), s);
+                           static_cast<char*>(ws) + score_bytes(p) + rng_bytes(p), s, a.rng, ix::kScoreSpan,
+                           a.rng_stride);
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 

@@ -41,16 +41,24 @@ struct ScoreArgs {
   int64_t ld;
   int64_t q_start;
   int n_q, H;
+  float2* rng;            // nullable: per-wave (min, max) of the written scores,
+                          // [rows][rng_stride], one entry per kScoreSpan keys
+  int rng_stride;
 };
+constexpr int kScoreSpan = 1024;   // keys per wave of the score kernel
 hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
                                  hipStream_t s);
 
 // Per-row top-k over materialised fp32 score rows.  Few rows use a chunked
 // multi-workgroup select whose state lives in a workspace of
 // topk_rows_ws_bytes(rows, q_start + n_q, k) bytes (0: none needed).
+// `rng` (nullable) holds per-row (min, max) partials over consecutive spans of
+// rng_span scores, rng_stride entries per row; without it the select measures
+// the ranges itself.
 size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k);
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, void* ws, hipStream_t s);
+                            int64_t q_start, int k, void* ws, hipStream_t s,
+                            const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0);
 
 // Sparse gather attention.
 struct AttnArgs {

@@ -46,6 +46,8 @@ struct RowSel {
   float lo, inv;   // value binning of the row
   int vb;          // bin holding the k-th best
   int m;           // scores in bins >= vb; kFallback / kTrivial as below
+  int above;       // scores in bins > vb
+  int pad[3];
 };
 constexpr int kFallback = -1;            // too many candidates: whole-row select
 constexpr int kTrivial = -2;             // p + 1 <= k: keep every position
@@ -265,7 +267,9 @@ struct ChunkArgs {
   int k;
   int G;           // chunks per row (of the longest row)
   int vec;         // rows are 16-byte aligned: load float4
-  float2* rng;     // [rows][G]
+  const float2* rng;  // range partials: [rows][rng_stride], one per rng_span scores
+  int rng_span, rng_stride;
+  float2* rng_own;    // [rows][G], written by the range pass when no partials are given
   uint32_t* hist;  // [rows][G][kVB]
   int32_t* off;    // [rows][G]
   RowSel* sel;     // [rows]
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kCT) void tk_range_kernel(ChunkArgs a) {
     }
   mn = block_reduce<kCT>(mn, red, MinOp{});
   mx = block_reduce<kCT>(mx, red, MaxOp{});
-  if (threadIdx.x == 0) a.rng[(int64_t)row * a.G + g] = make_float2(mn, mx);
+  if (threadIdx.x == 0) a.rng_own[(int64_t)row * a.G + g] = make_float2(mn, mx);
 }
 
 __global__ __launch_bounds__(kCT) void tk_hist_kernel(ChunkArgs a) {
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kCT) void tk_hist_kernel(ChunkArgs a) {
   load_run(a.scores + (int64_t)row * a.ld, i0, n, a.vec, v);
   for (int i = threadIdx.x; i < kVB; i += kCT) h[i] = 0u;
   float lo, inv;
-  row_binning<kCT>(a.rng + (int64_t)row * a.G, (n + kChunk - 1) / kChunk, red, lo, inv);
+  row_binning<kCT>(a.rng + (int64_t)row * a.rng_stride, (n + a.rng_span - 1) / a.rng_span, red, lo, inv);
 #pragma unroll
   for (int j = 0; j < kPT; ++j)
     if (i0 + j < n) atomicAdd(&h[vbin(v[j], lo, inv, kVB)], 1u);
@@ -355,19 +359,24 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
   const int row = blockIdx.x, tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int n = row_len(row, a.n_q, a.q_start);
   if (n <= a.k) {
-    if (tid == 0) a.sel[row] = RowSel{0.0f, 0.0f, 0, kTrivial};
+    if (tid == 0) a.sel[row] = RowSel{0.0f, 0.0f, 0, kTrivial, 0, {}};
     return;
   }
   const int Gr = (n + kChunk - 1) / kChunk;
   float lo, inv;
-  row_binning<kST>(a.rng + (int64_t)row * a.G, Gr, red, lo, inv);
+  row_binning<kST>(a.rng + (int64_t)row * a.rng_stride, (n + a.rng_span - 1) / a.rng_span, red, lo, inv);
 
   // row histogram: bins 4*tid .. 4*tid + 3
   const uint32_t* hb = a.hist + (int64_t)row * a.G * kVB;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (int g = 0; g < Gr; ++g) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(hb + (int64_t)g * kVB + 4 * tid);
-    acc += x;
+  for (int g0 = 0; g0 < Gr; g0 += 8) {          // 8 chunk loads in flight
+    u32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[j] = g0 + j < Gr ? *reinterpret_cast<const u32x4*>(hb + (int64_t)(g0 + j) * kVB + 4 * tid)
+                         : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += x[j];
   }
   const int tot = (int)(acc.x + acc.y + acc.z + acc.w);
   // entries in bins above this thread's: total minus inclusive prefix
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
   const int vb = sh_vb;
   const int m = sh_above + sh_h;
   if (m > kCap) {
-    if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, kFallback};
+    if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, kFallback, 0, {}};
     return;
   }
   // per-chunk counts of bins >= vb (one wave per chunk, 16 bins per lane),
@@ -396,19 +405,29 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
   int carry = 0;
   for (int g0 = 0; g0 < Gr; g0 += kST) {
     const int gn = min(kST, Gr - g0);
-    for (int gi = wave; gi < gn; gi += kST / kWave) {
-      const uint32_t* hc = hb + (int64_t)(g0 + gi) * kVB + 16 * l;
-      int c = 0;
+    for (int gi0 = wave; gi0 < gn; gi0 += 2 * (kST / kWave)) {   // two chunks per wave at once
+      u32x4 x[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(hc + 4 * j);
-        const int b0 = 16 * l + 4 * j;
-        c += (b0 >= vb ? (int)x.x : 0) + (b0 + 1 >= vb ? (int)x.y : 0) +
-             (b0 + 2 >= vb ? (int)x.z : 0) + (b0 + 3 >= vb ? (int)x.w : 0);
+      for (int u = 0; u < 2; ++u) {
+        const int gi = gi0 + u * (kST / kWave);
+        const uint32_t* hc = hb + (int64_t)(g0 + (gi < gn ? gi : 0)) * kVB + 16 * l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[u][j] = *reinterpret_cast<const u32x4*>(hc + 4 * j);
       }
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
-      if (l == 0) cnt[gi] = c;
+      for (int u = 0; u < 2; ++u) {
+        const int gi = gi0 + u * (kST / kWave);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b0 = 16 * l + 4 * j;
+          c += (b0 >= vb ? (int)x[u][j].x : 0) + (b0 + 1 >= vb ? (int)x[u][j].y : 0) +
+               (b0 + 2 >= vb ? (int)x[u][j].z : 0) + (b0 + 3 >= vb ? (int)x[u][j].w : 0);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+        if (l == 0 && gi < gn) cnt[gi] = c;
+      }
     }
     __syncthreads();
     const int c = tid < gn ? cnt[tid] : 0;
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
     if (tid < gn) a.off[(int64_t)row * a.G + g0 + tid] = carry + ex;
     carry += chunk_tot;
   }
-  if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, m};
+  if (tid == 0) a.sel[row] = RowSel{lo, inv, vb, m, sh_above, {}};
 }
 
 __global__ __launch_bounds__(kCT) void tk_collect_kernel(ChunkArgs a) {
@@ -465,20 +484,25 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
   }
   const int m = rs.m;
   const uint2* src = a.cand + (int64_t)row * kCap;
+  // every candidate in a bin above vb is kept; the k-th best is the
+  // (k - above)-th among bin vb's, whose key range is narrow
+  const auto in_vb = [&](uint32_t key) { return vbin(key_value(key), rs.lo, rs.inv, kVB) == rs.vb; };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < m; i += kFT) {
     const uint2 e = src[i];
     ck[i] = e.x;
     cp[i] = (int)e.y;
-    kmin = min(kmin, e.x);
-    kmax = max(kmax, e.x);
+    if (in_vb(e.x)) {
+      kmin = min(kmin, e.x);
+      kmax = max(kmax, e.x);
+    }
   }
   kmin = block_reduce<kFT>(kmin, redu, UMinOp{});
   kmax = block_reduce<kFT>(kmax, redu, UMaxOp{});   // its barriers publish ck / cp
   int need = 0;
   const uint32_t v = radix_kth<kFT>(
-      m, a.k, kmin, kmax, [&](int i) { return ck[i]; }, [](int) { return true; }, hist, &sel_bin,
-      &sel_above, &need);
+      m, a.k - rs.above, kmin, kmax, [&](int i) { return ck[i]; }, [&](int i) { return in_vb(ck[i]); }, hist,
+      &sel_bin, &sel_above, &need);
 
   // stable emission: thread t owns list entries [t*P, t*P + P)
   const int P = (m + kFT - 1) / kFT;
@@ -515,7 +539,8 @@ size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k) {
 }
 
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, void* ws, hipStream_t s) {
+                            int64_t q_start, int k, void* ws, hipStream_t s, const float2* rng,
+                            int rng_span, int rng_stride) {
   const int64_t max_n = q_start + n_q;
   if (topk_rows_ws_bytes(rows, max_n, k) == 0) {
     hipLaunchKernelGGL(topk_rows_single_kernel, dim3(rows), dim3(kFT), 0, s, scores, ld, idx, n_q,
@@ -532,7 +557,16 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
   a.G = (int)chunks_per_row(max_n);
   a.vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0) ? 1 : 0;
   char* p = static_cast<char*>(ws);
-  a.rng = reinterpret_cast<float2*>(p);
+  a.rng_own = reinterpret_cast<float2*>(p);
+  if (rng) {
+    a.rng = rng;
+    a.rng_span = rng_span;
+    a.rng_stride = rng_stride;
+  } else {
+    a.rng = a.rng_own;
+    a.rng_span = kChunk;
+    a.rng_stride = a.G;
+  }
   p += align256((size_t)rows * a.G * sizeof(float2));
   a.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * a.G * kVB * 4);
@@ -542,7 +576,7 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
   p += align256((size_t)rows * sizeof(RowSel));
   a.cand = reinterpret_cast<uint2*>(p);
   const dim3 chunk_grid((unsigned)((int64_t)rows * a.G));
-  hipLaunchKernelGGL(tk_range_kernel, chunk_grid, dim3(kCT), 0, s, a);
+  if (!rng) hipLaunchKernelGGL(tk_range_kernel, chunk_grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(tk_hist_kernel, chunk_grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(tk_select_kernel, dim3(rows), dim3(kST), 0, s, a);
   hipLaunchKernelGGL(tk_collect_kernel, chunk_grid, dim3(kCT), 0, s, a);
