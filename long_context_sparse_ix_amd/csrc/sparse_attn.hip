@@ -19,8 +19,9 @@
 //     query slice stays in VGPRs), so lane l ends with 4 logits of head l%16
 //     -- exactly the B-operand layout of the P.V product below;
 //   * the value part of the 16 rows is parked in a wave-private LDS tile and
-//     read back transposed (one key column per lane) as the A operand of
-//     O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16);
+//     read back transposed by ds_read_b64_tr_b16 (lane (dv, key group) gets 4
+//     keys of one value dim) as the A operand of O^T = V^T . P^T
+//     (v_mfma_f32_16x16x16_bf16);
 //   * online softmax in base 2, rescaling the accumulators only when some
 //     head's running max grows;
 //   * few rows (decode): the four waves of a workgroup share one (row, split),
@@ -37,12 +38,16 @@ namespace {
 constexpr int kWavesPerWG = 4;
 constexpr float kLn2 = 0.69314718055994530942f;
 
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
+
 template <int MT>
 struct VTile {
   static constexpr int Dv = 16 * MT;
-  // row stride in dwords chosen == 16 (mod 64): the 4 rows a transposed read
-  // touches land in disjoint bank groups
-  static constexpr int stride_dw = Dv / 2 + ((16 - (Dv / 2) % 64) + 64) % 64;
+  // row stride in dwords chosen == 8 (mod 64): the 8 rows x 32 bytes one
+  // half-wave of a transposed read touches cover all banks once, and the 16
+  // rows a parking store touches collide at most pairwise
+  static constexpr int stride_dw = Dv / 2 + ((8 - (Dv / 2) % 64) + 64) % 64;
   static constexpr int stride = 2 * stride_dw;      // bf16 elements
   static constexpr int bytes = 16 * stride_dw * 4;
 };
@@ -171,14 +176,13 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
 
     wave_lds_sync();
+    // transposed read: lane (n16, g) supplies 4 value dims of key 4g + n16/4
+    // and receives value dim 16mt + n16 of keys 4g .. 4g+3
+    const uint16_t* vrow = vl + (4 * g + (n16 >> 2)) * V::stride + 4 * (n16 & 3);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* col = vl + 16 * mt + n16 + 4 * g * V::stride;
-      i16x4 av;
-      av[0] = (short)col[0];
-      av[1] = (short)col[V::stride];
-      av[2] = (short)col[2 * V::stride];
-      av[3] = (short)col[3 * V::stride];
+      const v4s_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
+      const i16x4 av = __builtin_bit_cast(i16x4, t);
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, oacc[mt], 0, 0, 0);
     }
     wave_lds_sync();
