@@ -46,7 +46,7 @@ namespace {
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 4;
 constexpr int kThreads = kRowsPerWG * kWave;
-constexpr int kRing = 3;        // LDS tile buffers: tile it being read, it+1 landing, it+2 loading
+constexpr int kRing = 4;        // LDS tile buffers: a pair of tiles being read, the next pair landing
 constexpr int kUnroll = 8;      // candidate entries per lane in flight in buffer passes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -226,7 +226,7 @@ __device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
 // later key equal to s* loses the position tie, so tau = s* keeps the strict
 // filter exact.  A crowded bin (ties, or a range too wide to split) falls back
 // to the exact select.
-__device__ void shrink(Cand c, int& cnt, float& tau, float hi_lane, int k, int keep_max, uint32_t* hist) {
+__device__ __forceinline__ void shrink(Cand c, int& cnt, float& tau, float hi_lane, int k, int keep_max, uint32_t* hist) {
   const int l = lane_id();
   wait_vmcnt<0>();                               // this wave's appends are visible
   const float hi = wave_max_f(hi_lane);
@@ -451,27 +451,27 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   float part0 = 0.0f;                           // key-half-0 partial score of the tile being finished
 
   issue_tile(0, 0);
-  if (n_tiles > 1) {
-    issue_tile(1, 1);
-    wait_vmcnt<kLoads>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  if (n_tiles > 1) issue_tile(1, 1);
+  wait_vmcnt<0>();
   __syncthreads();
 
+  // Tiles are consumed in pairs with one barrier per pair: tile t sits in ring
+  // slot t % 4; while the pair (it, it+1) is read, the pair (it+2, it+3) lands.
   f32x16 acc0[HT], acc1[HT];
-  int slot = 0;                                  // ring slot of tile it
-  for (int it = 0; it <= n_tiles; ++it) {
+  auto step = [&](int it, bool issue_pair) {
     const bool mma = row_ok && it < n_tiles && it * kTileKeys <= p;
     const bool epi = row_ok && it >= 1 && (it - 1) * kTileKeys <= p;
+    const int slot = it & (kRing - 1);
     const unsigned char* kb = key_lds0 + slot * G::tile_bytes;
     // B operand of half 0 first (a stale, unused read when !mma), so its LDS
     // latency hides behind the tile issue
     bf16x8 bfr[KS];
     read_bfrags<KS>(kb, 0, m, hf, bfr);
     const float sc_cur = SCALE ? scale_lds[slot * kTileKeys + l] : 1.0f;
-    const bool more = it + 2 < n_tiles;
-    if (more) issue_tile(it + 2, slot == 0 ? 2 : slot - 1);   // (slot + 2) % 3
+    if (issue_pair) {
+      if (it + 2 < n_tiles) issue_tile(it + 2, (it + 2) & (kRing - 1));
+      if (it + 3 < n_tiles) issue_tile(it + 3, (it + 3) & (kRing - 1));
+    }
 
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
     float part1 = 0.0f;
@@ -504,10 +504,12 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     // fragments are live)
     if (cnt > C - kWave) shrink(cand, cnt, tau, vmax, a.k, keep_max, my_hist);
     sc_prev = sc_cur;
-    if (more) wait_vmcnt<kLoads>();              // tile it+1 landed (it+2 may still fly)
-    else wait_vmcnt<0>();
+  };
+  for (int it = 0; it <= n_tiles; it += 2) {
+    step(it, true);
+    if (it + 1 <= n_tiles) step(it + 1, false);
+    wait_vmcnt<0>();                             // the next pair landed
     lds_barrier();
-    slot = slot == 2 ? 0 : slot + 1;
   }
 
   if (row_ok) {
