@@ -361,7 +361,7 @@ def main(argv=None):
                      "algorithmic_bytes": at_bytes},
         "indexer": {"ms": ix_ms, "tflops": ix_tflops, "frac_bf16_peak": ix_tflops / PEAK_BF16_TFLOPS,
                     "frac_fp8_peak": ix_tflops / PEAK_FP8_TFLOPS, "flop": ix_flop,
-                    "note": "fused score + streaming top-k, incl. fp8->bf16 key upcast"},
+                    "note": "fused score + streaming top-k, incl. staging the keys as bf16 (fp8 widened exactly)"},
         "attention": {"ms_per_layer": at_ms, "tokens_per_s": w.batch * w.n_q / (at_ms / 1e3),
                       "gathered_GBps": at_gbps, "frac_hbm_peak": at_gbps / PEAK_HBM_GBPS,
                       "tflops": at_flop / (at_ms / 1e3) / 1e12},

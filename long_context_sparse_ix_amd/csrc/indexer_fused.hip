@@ -409,8 +409,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   // lane l fetches the global chunk that belongs in slot J*n + l (tile row r,
   // chunk swz(r, slot % CPR); swz is an involution).  With several loads per
   // wave (d >= 64) load j covers the 4 KB after load j-1 and the swizzle
-  // repeats, so one per-lane byte offset serves all of them.  Only the last,
-  // partial tile clamps its rows to the last key (their scores are masked).
+  // repeats, so one per-lane byte offset serves all of them.  The staged key
+  // copy is padded by a tile, so the last, partial tile loads whole (the rows
+  // past the last key are masked).
   static_assert(G::inst_per_wave == 1 || G::lanes_per_inst * 4 * 16 == 4096, "4 KB per load round");
   const int key_off = [&] {
     const int S = wave * G::lanes_per_inst + l;
@@ -421,26 +422,18 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
-    const bool full = s0 + kTileKeys <= n_keys;
-    const unsigned char* tile = key_bytes + (int64_t)s0 * d * 2;
+    const unsigned char* tile = key_bytes + (int64_t)s0 * d * 2;   // staged keys: whole tiles exist
 #pragma unroll
     for (int j = 0; j < G::inst_per_wave; ++j) {
       const int J = wave + 4 * j;
-      const unsigned char* src;
-      if (full) {
-        src = tile + key_off + 4096 * j;
-      } else {
-        const int r = (J * G::lanes_per_inst + l) / G::CPR;
-        src = key_bytes + (int64_t)min(s0 + r, n_keys - 1) * d * 2 + (key_off + 4096 * j - r * d * 2);
-      }
       if (G::lanes_per_inst == 64 || l < G::lanes_per_inst)
-        __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((void*)(tile + key_off + 4096 * j),
+                                         (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16, 0, 0);
     }
     if constexpr (SCALE) {
-      const int sk = s0 + 16 * wave + (l & 15);
-      const float* src = scale_b + (full ? sk : min(sk, n_keys - 1));
       if (l < 16)
-        __builtin_amdgcn_global_load_lds((void*)src, (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((void*)(scale_b + s0 + 16 * wave + l),
+                                         (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4, 0, 0);
     }
   };
 
@@ -528,23 +521,36 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   }
 }
 
-__global__ void upcast_fp8_kernel(const uint8_t* __restrict__ src, int64_t src_bstride,
-                                  uint16_t* __restrict__ dst, int64_t dst_bstride,
-                                  int64_t chunks_per_seq, int64_t total_chunks) {
-  // one 16-code chunk per thread per step; d % 16 == 0 keeps chunks inside rows
+__global__ void stage_keys_kernel(const void* __restrict__ src, int fp8, int64_t src_bstride,
+                                  const float* __restrict__ scale, int64_t scale_bstride,
+                                  uint16_t* __restrict__ dst, float* __restrict__ dst_scale, int64_t rows,
+                                  int64_t rows_padded, int d, int64_t total_chunks) {
+  // one 16-element chunk per thread per step; d % 16 == 0 keeps chunks inside rows
+  const int64_t chunks_per_row = d / 16;
+  const int64_t per_seq = rows_padded * chunks_per_row;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks;
        c += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = c / chunks_per_seq, off = (c % chunks_per_seq) * 16;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + b * src_bstride + off);
-    u32x4 o0, o1;
-    u32x2 r;
-    r = e4m3x4_to_bf16x4(v.x); o0.x = r.x; o0.y = r.y;
-    r = e4m3x4_to_bf16x4(v.y); o0.z = r.x; o0.w = r.y;
-    r = e4m3x4_to_bf16x4(v.z); o1.x = r.x; o1.y = r.y;
-    r = e4m3x4_to_bf16x4(v.w); o1.z = r.x; o1.w = r.y;
-    u32x4* dd = reinterpret_cast<u32x4*>(dst + b * dst_bstride + off);
+    const int64_t b = c / per_seq, rc = c % per_seq;
+    const int64_t r = rc / chunks_per_row, off = (rc % chunks_per_row) * 16;
+    u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+      if (fp8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(src) + b * src_bstride + r * d + off);
+        u32x2 t;
+        t = e4m3x4_to_bf16x4(v.x); o0.x = t.x; o0.y = t.y;
+        t = e4m3x4_to_bf16x4(v.y); o0.z = t.x; o0.w = t.y;
+        t = e4m3x4_to_bf16x4(v.z); o1.x = t.x; o1.y = t.y;
+        t = e4m3x4_to_bf16x4(v.w); o1.z = t.x; o1.w = t.y;
+      } else {
+        const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + b * src_bstride + r * d + off);
+        o0 = v[0];
+        o1 = v[1];
+      }
+    }
+    u32x4* dd = reinterpret_cast<u32x4*>(dst + b * rows_padded * d + r * d + off);
     dd[0] = o0;
     dd[1] = o1;
+    if (dst_scale && off == 0) dst_scale[b * rows_padded + r] = r < rows ? scale[b * scale_bstride + r] : 0.0f;
   }
 }
 
@@ -589,15 +595,15 @@ hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_upcast_fp8(const uint8_t* src, int64_t src_bstride, uint16_t* dst,
-                             int64_t dst_bstride, int B, int64_t rows, int d, hipStream_t s) {
-  const int64_t per_seq = rows * d / 16;
-  const int64_t total = per_seq * B;
+hipError_t launch_stage_keys(const void* src, bool fp8, int64_t src_bstride, const float* scale,
+                             int64_t scale_bstride, uint16_t* dst, float* dst_scale, int B, int64_t rows,
+                             int64_t rows_padded, int d, hipStream_t s) {
+  const int64_t total = (int64_t)B * rows_padded * (d / 16);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(upcast_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, src_bstride,
-                     dst, dst_bstride, per_seq, total);
+  hipLaunchKernelGGL(stage_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, fp8 ? 1 : 0, src_bstride,
+                     scale, scale_bstride, dst, dst_scale, rows, rows_padded, d, total);
   return hipGetLastError();
 }
 

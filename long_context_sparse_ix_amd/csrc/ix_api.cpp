@@ -95,13 +95,16 @@ size_t rng_bytes(const ix_problem* p) {
   return round_up((size_t)p->batch * p->n_q * rng_stride(p) * 8);
 }
 
+size_t stage_key_bytes(const ix_problem* p, const ix_indexer_in* in) {
+  return round_up((size_t)p->batch * (size_t)(p->kv_len + ix::kStagePad) * in->dim * 2);
+}
+size_t stage_scale_bytes(const ix_problem* p, const ix_indexer_in* in) {
+  return in->k_dtype == IX_DTYPE_FP8_E4M3FN ? round_up((size_t)p->batch * (size_t)(p->kv_len + ix::kStagePad) * 4)
+                                             : 0;
+}
+
 size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
-  if (use_fused(p, in)) {
-    size_t need = fused_cand_bytes(p);
-    if (in->k_dtype == IX_DTYPE_FP8_E4M3FN)
-      need += round_up((size_t)p->batch * (size_t)p->kv_len * in->dim * 2);
-    return need;
-  }
+  if (use_fused(p, in)) return fused_cand_bytes(p) + stage_key_bytes(p, in) + stage_scale_bytes(p, in);
   return score_bytes(p) + rng_bytes(p) + topk_ws(p);
 }
 
@@ -158,22 +161,19 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
     a.k = p->k;
     a.C = ix::fused_candidates(p->k);
     a.cand = static_cast<float2*>(ws);
-    if (fp8) {
-      uint16_t* kb = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fused_cand_bytes(p));
-      hipError_t e = ix::launch_upcast_fp8(static_cast<const uint8_t*>(in->k), p->kv_cap * in->dim,
-                                           kb, p->kv_len * in->dim, p->batch, p->kv_len, in->dim, s);
-      if (e != hipSuccess) return hip_fail(e);
-      a.keys = kb;
-      a.key_bstride = p->kv_len * in->dim;
-      a.scale = in->k_scale;
-      a.scale_bstride = p->kv_cap;
-    } else {
-      a.keys = static_cast<const uint16_t*>(in->k);
-      a.key_bstride = p->kv_cap * in->dim;
-      a.scale = nullptr;
-      a.scale_bstride = 0;
-    }
-    hipError_t e = ix::launch_fused_indexer(a, p->batch, in->dim, s);
+    // keys (widened to bf16) and scales staged into padded workspace copies
+    const int64_t rows_pad = p->kv_len + ix::kStagePad;
+    char* stage = static_cast<char*>(ws) + fused_cand_bytes(p);
+    uint16_t* kb = reinterpret_cast<uint16_t*>(stage);
+    float* sb = fp8 ? reinterpret_cast<float*>(stage + stage_key_bytes(p, in)) : nullptr;
+    hipError_t e = ix::launch_stage_keys(in->k, fp8, p->kv_cap * in->dim, in->k_scale, p->kv_cap, kb, sb,
+                                         p->batch, p->kv_len, rows_pad, in->dim, s);
+    if (e != hipSuccess) return hip_fail(e);
+    a.keys = kb;
+    a.key_bstride = rows_pad * in->dim;
+    a.scale = sb;
+    a.scale_bstride = fp8 ? rows_pad : 0;
+    e = ix::launch_fused_indexer(a, p->batch, in->dim, s);
     return e == hipSuccess ? IX_OK : hip_fail(e);
   }
   ix::ScoreArgs a{};

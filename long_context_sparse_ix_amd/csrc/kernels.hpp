@@ -26,8 +26,15 @@ int fused_candidates(int k);
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s);
 
 // e4m3fn codes -> bf16 (exact), rows [0, rows) of every sequence.
-hipError_t launch_upcast_fp8(const uint8_t* src, int64_t src_bstride, uint16_t* dst,
-                             int64_t dst_bstride, int B, int64_t rows, int d, hipStream_t s);
+// Key staging for the fused indexer: the first `rows` key rows of every
+// sequence as bf16 (e4m3fn codes widened exactly, or bf16 copied) into
+// dst [B][rows_padded][d], and (fp8) their scales into dst_scale
+// [B][rows_padded]; rows in [rows, rows_padded) are zero, so whole-tile loads
+// never leave the buffer.
+hipError_t launch_stage_keys(const void* src, bool fp8, int64_t src_bstride, const float* scale,
+                             int64_t scale_bstride, uint16_t* dst, float* dst_scale, int B, int64_t rows,
+                             int64_t rows_padded, int d, hipStream_t s);
+constexpr int kStagePad = 64;     // rows of padding after the last key (one tile)
 
 // Materialised indexer scores: scores[(b*n_q+t)*ld + s] for s <= q_start+t.
 struct ScoreArgs {
