@@ -102,39 +102,28 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // Loads are unconditional: exec-masked load branches make the compiler's
+  // memory-counter waits fall back to draining every load in flight, which
+  // would stall each step on the next step's prefetch.  An index word past
+  // the range reads an in-row slot and becomes -1; an invalid slot gathers
+  // row 0, whose logit is masked to -inf and whose value row is weighted by 0.
   auto slot_row = [&](int c0) -> int {
     const int slot = c0 + n16;
-    return slot < j1 ? irow[slot] : -1;
+    const int v = irow[min(slot, a.k - 1)];
+    return slot < j1 ? v : -1;
   };
   auto fetch = [&](int rid, bf16x8* kf) -> bool {
     const bool valid = rid >= 0 && (int64_t)rid < a.kv_len;
-    if (valid) {
-      const uint16_t* src = kvb + (int64_t)rid * D;
+    const uint16_t* src = kvb + (int64_t)(valid ? rid : 0) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
     return valid;
   };
 
-  bf16x8 kf_next[KS];
-  int rid_after = (j0 + 16 < j1) ? slot_row(j0 + 16) : -1;
-  bool valid_next = fetch(j0 < j1 ? slot_row(j0) : -1, kf_next);
-
-  for (int c0 = j0; c0 < j1; c0 += 16) {
-    bf16x8 kf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = kf_next[ks];
-    const bool valid = valid_next;
-    // prefetch: latent rows of the next step, index words of the one after
-    const int rid_next = rid_after;
-    rid_after = (c0 + 32 < j1) ? slot_row(c0 + 32) : -1;
-    valid_next = fetch(c0 + 16 < j1 ? rid_next : -1, kf_next);
-
+  // One 16-slot step on gathered rows kf.
+  auto step = [&](const bf16x8 (&kf)[KS], bool valid) {
     const uint32_t vm = (uint32_t)__ballot(valid) & 0xFFFFu;   // lanes 0..15 own slots 0..15
-    if (vm == 0u) continue;
+    if (vm == 0u) return;
 
     f32x4 sacc = f32x4{};
 #pragma unroll
@@ -186,6 +175,25 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, oacc[mt], 0, 0, 0);
     }
     wave_lds_sync();
+  };
+
+  // Two named buffers in turn (unrolled by 2): the step on one runs while the
+  // other's gathers are in flight.  A loop-carried copy of the buffer would
+  // make the compiler wait for those gathers at every step.
+  bf16x8 kA[KS], kB[KS];
+  bool vA = fetch(slot_row(j0), kA), vB = false;
+  int rid_after = slot_row(j0 + 16);             // -1 past the range
+  for (int c0 = j0; c0 < j1; c0 += 32) {
+    // prefetch: latent rows of the next step, index words of the one after
+    int rid_next = rid_after;
+    rid_after = slot_row(c0 + 32);
+    vB = fetch(rid_next, kB);
+    step(kA, vA);
+    if (c0 + 16 >= j1) break;
+    rid_next = rid_after;
+    rid_after = slot_row(c0 + 48);
+    vA = fetch(rid_next, kA);
+    step(kB, vB);
   }
 
   // oacc[mt][i] = O^T[dv = 16mt + 4g + i][head n16]
