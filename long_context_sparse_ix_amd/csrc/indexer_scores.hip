@@ -83,10 +83,6 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
     }
   };
 
-#pragma unroll
-  for (int j = 0; j < kDepth - 1; ++j)
-    if (j < n_tiles) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
-
   bf16x8 qf[HT][KS];
   float wr[HT][16];
   {
@@ -106,15 +102,20 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
     }
   }
 
+  // Loads are unconditional (keys past p are clamped to p, their scores are
+  // masked): exec-masked load branches make the compiler's memory-counter
+  // waits drain every load in flight, tiles three steps ahead included.
+#pragma unroll
+  for (int j = 0; j < kDepth - 1; ++j) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
+
   float smin = INFINITY, smax = -INFINITY;     // range of this wave's scores
-  for (int j0 = 0; j0 < n_tiles; j0 += kDepth) {
+  for (int j0 = 0; j0 < n_tiles; j0 += kDepth) {   // a partial last group computes masked tiles
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int j = j0 + u;
-      if (j < n_tiles) {
+      {
         const int jn = j + kDepth - 1;
-        if (jn < n_tiles)
-          load_raw(s_begin + (int64_t)jn * kTileKeys, raw[(u + kDepth - 1) % kDepth], sc[(u + kDepth - 1) % kDepth]);
+        load_raw(s_begin + (int64_t)jn * kTileKeys, raw[(u + kDepth - 1) % kDepth], sc[(u + kDepth - 1) % kDepth]);
         const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
         bf16x8 bfr[2][KS];
         widen(raw[u], bfr);
