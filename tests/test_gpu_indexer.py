@@ -168,3 +168,26 @@ def test_topk_scores_entry_point(ix):
         for t in range(n_q):
             p = q_start + t
             np.testing.assert_array_equal(got[b, t], O.select_topk(s[b, t, : p + 1].astype(np.float64), k))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("key_dtype", ["bf16", "fp8"])
+def test_exact_spare_cache_rows_and_batch(ix, path, key_dtype):
+    """Two sequences whose key caches hold spare rows past kv_len (kv_cap >
+    kv_len) and a query block at q_start > 0.  The spare rows are poisoned with
+    the largest key values, so reading keys with the wrong sequence stride, or
+    past kv_len, would change the selection."""
+    w = synth.L16K.with_(name="exact_cap", batch=2, n_q=300, q_start=900, kv_len=1200, kv_cap=1300,
+                         k=256, mode="exact", key_dtype=key_dtype)
+    q, wt = synth.indexer_queries(w, "cuda", 0)
+    keys, scale = synth.indexer_keys(w, "cuda", 0)
+    poison = torch.full_like(keys[:, w.kv_len:], 0)
+    if key_dtype == "bf16":
+        poison = torch.full(poison.shape, 8.0, dtype=torch.bfloat16, device="cuda")
+    else:
+        poison = torch.full(poison.shape, 8.0, device="cuda").to(torch.float8_e4m3fn).view(torch.uint8)
+    keys[:, w.kv_len:] = poison
+    inputs, got = _run(ix, w, path, inputs=(q, wt, keys, scale))
+    valid_idx_rows(got, w.q_start, w.k)
+    rows = [0, 1, 150, 298, 299]
+    np.testing.assert_array_equal(got[:, rows], _oracle(w, inputs, rows))
