@@ -19,13 +19,15 @@ namespace ix {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 1024 keys per wave
+constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 20 tiles of 64 keys per wave
 constexpr int kWavesPerWG = 4;
-constexpr int kDepth = 4;                   // tiles per wave in registers: 1 in use, 3 in flight
 
 template <int HT, int KS, bool FP8>
 __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(ScoreArgs a) {
   constexpr int d = KS * 16;
+  // tiles per wave held in registers (one in use, the rest in flight): fp8
+  // tiles are half the bytes of bf16 ones
+  constexpr int kDepth = FP8 ? 5 : 3;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 31, hf = l >> 5;
   const int row = blockIdx.y;                 // b * n_q + t
