@@ -228,3 +228,29 @@ def group_forward(roles: str, indexer_layers, attn_layers, q_start: int, kv_len:
         outs.append(o)
         lses.append(lse)
     return {"O": outs, "lse": lses, "idx": idx_list, "used": used, "n_indexer_runs": runs}
+
+
+# ------------------------------------------------------------- diagnostics --
+def index_overlap(idx_a, idx_b) -> np.ndarray:
+    """Per row, the number of positions selected in both index rows.
+
+    "IndexShare" (LLM Architecture Gallery), section "Why Reusing Indices Can
+    Work": reuse pays off because the top-k sets of adjacent layers overlap
+    heavily; this is that count, |{valid a} & {valid b}| for each row, with
+    negative slots (the -1 padding) ignored.  idx_a, idx_b: integer arrays of
+    the same shape [..., k]; returns int64 [...].
+    """
+    a = np.asarray(idx_a)
+    b = np.asarray(idx_b)
+    if a.shape != b.shape:
+        raise ValueError("index buffers must have the same shape")
+    lead = a.shape[:-1]
+    a2 = a.reshape(-1, a.shape[-1])
+    b2 = b.reshape(-1, b.shape[-1])
+    out = np.empty(a2.shape[0], dtype=np.int64)
+    for r in range(a2.shape[0]):
+        sa = set(int(x) for x in a2[r] if x >= 0)
+        sb = set(int(x) for x in b2[r] if x >= 0)
+        out[r] = len(sa & sb)
+    return out.reshape(lead)
+

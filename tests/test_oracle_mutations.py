@@ -60,6 +60,17 @@ def _attn_no_scale(q_row, kv, sel, sm_scale, d_v):
     return ATTN(q_row, kv, sel, 1.0, d_v)
 
 
+def _overlap_counts_padding(idx_a, idx_b):
+    a, b = np.asarray(idx_a), np.asarray(idx_b)
+    return np.array([len(set(x.tolist()) & set(y.tolist())) for x, y in
+                     zip(a.reshape(-1, a.shape[-1]), b.reshape(-1, b.shape[-1]))]).reshape(a.shape[:-1])
+
+
+def _overlap_slotwise(idx_a, idx_b):
+    a, b = np.asarray(idx_a), np.asarray(idx_b)
+    return ((a == b) & (a >= 0)).sum(axis=-1)
+
+
 ATTN = O.attention_row
 INDEXER = O.indexer_topk
 
@@ -74,6 +85,9 @@ MUTATIONS = [
     ("e4m3_bias", "decode_e4m3fn", _e4m3_bias8, P.test_e4m3fn_decode_matches_torch_for_all_256_codes),
     ("wrong_v_slice", "attention_row", _attn_wrong_v, P.test_hand_worked_attention),
     ("no_sm_scale", "attention_row", _attn_no_scale, P.test_attention_with_full_prefix_equals_dense_causal_sdpa),
+    ("overlap_counts_padding", "index_overlap", _overlap_counts_padding,
+     P.test_overlap_ignores_padding_and_is_symmetric),
+    ("overlap_slotwise", "index_overlap", _overlap_slotwise, P.test_overlap_shifted_ranges_closed_form),
 ]
 
 

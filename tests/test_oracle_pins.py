@@ -352,3 +352,43 @@ def test_row_form_agrees_with_batch_form():
     rows = [0, 7, 29]
     part = O.indexer_topk_rows(q[0, rows], w[0, rows], keys[0], "bf16", None, [60 + r for r in rows], n, k)
     np.testing.assert_array_equal(part, full[0, rows])
+
+
+# ------------------------------------------------------------ index overlap --
+def _row(vals, k):
+    r = np.full(k, -1, dtype=np.int32)
+    r[:len(vals)] = sorted(vals)
+    return r
+
+
+def test_overlap_identical_rows_count_valid_slots():
+    """Closed form: a row overlaps itself in exactly its valid slots."""
+    rng = np.random.default_rng(3)
+    rows = [_row(rng.choice(5000, size=n, replace=False), 64) for n in (0, 1, 17, 64)]
+    a = np.stack(rows)
+    np.testing.assert_array_equal(O.index_overlap(a, a), [0, 1, 17, 64])
+
+
+def test_overlap_shifted_ranges_closed_form():
+    """[0, n) against [m, m + n): max(0, n - m) common positions."""
+    k = 32
+    for n, m in ((32, 0), (32, 5), (20, 19), (20, 20), (20, 31), (7, 3)):
+        a = _row(range(n), k)[None]
+        b = _row(range(m, m + n), k)[None]
+        assert O.index_overlap(a, b)[0] == max(0, n - m)
+
+
+def test_overlap_ignores_padding_and_is_symmetric():
+    """-1 padding never counts even when both rows are padded in the same
+    slots; the count is symmetric in its arguments."""
+    a = np.array([[2, 5, 9, -1, -1], [-1, -1, -1, -1, -1]], dtype=np.int32)
+    b = np.array([[5, 9, 11, -1, -1], [-1, -1, -1, -1, -1]], dtype=np.int32)
+    np.testing.assert_array_equal(O.index_overlap(a, b), [2, 0])
+    np.testing.assert_array_equal(O.index_overlap(b, a), [2, 0])
+
+
+def test_overlap_keeps_leading_shape():
+    a = np.zeros((2, 3, 4), dtype=np.int32)
+    assert O.index_overlap(a, a).shape == (2, 3)
+    with pytest.raises(ValueError):
+        O.index_overlap(a, a[:, :2])
