@@ -318,6 +318,17 @@ def main(argv=None):
     tk_bytes = dk.batch * (4 * dk.kv_len + 4 * dk.k)
     del tk_scores
 
+    # overlap of the two full layers' index buffers (the adjacent-layer
+    # overlap that makes reuse work), when the workload has two full layers
+    overlap = None
+    if inp.idx_fs.shape[0] >= 2:
+        cnt = ix.ix_index_overlap(inp.idx_fs[0], inp.idx_fs[1])
+        ov_ms = event_time(torch, lambda: ix.ix_index_overlap(inp.idx_fs[0], inp.idx_fs[1], cnt), 5)
+        valid = (inp.idx_fs[0] >= 0).sum(dim=-1).clamp(min=1)
+        overlap = {"layers": "first vs second full layer", "mean_fraction": float((cnt.float() / valid).mean()),
+                   "us": ov_ms * 1e3, "rows_per_s": w.batch * w.n_q / (ov_ms / 1e3),
+                   "note": "independent synthetic layers: about k / candidates expected"}
+
     allf_ms = None
     if not args.no_all_full:
         log("all-full baseline")
@@ -368,6 +379,7 @@ def main(argv=None):
         "topk_standalone": {"workload": "32 rows x 200,001 fp32 scores, k=2048", "us": tk_ms * 1e3,
                             "rows_per_s": dk.batch / (tk_ms / 1e3),
                             "frac_hbm_peak": tk_bytes / (tk_ms / 1e3) / 1e9 / PEAK_HBM_GBPS},
+        "index_overlap": overlap,
         "group": {"ms_fsss": ms_step / n_groups, "ms_all_full": None if allf_ms is None else allf_ms / n_groups,
                   "speedup_vs_all_full": None if allf_ms is None else allf_ms / ms_step},
         "cpu_baseline": result_cpu,

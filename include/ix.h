@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 1
+#define IX_ABI_VERSION 2
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -171,6 +171,19 @@ int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_ma
  * NULL) bytes; other calls need none (ws may be NULL). */
 int32_t ix_topk_scores(const ix_problem* prob, const float* scores, int64_t ld, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Per-row overlap of two index buffers: counts[b*n_q + t] = the number of
+ * positions present in both idx_a[b][t][:] and idx_b[b][t][:], negative slots
+ * ignored.  It measures the adjacent-layer overlap that makes index reuse
+ * work ("IndexShare", LLM Architecture Gallery, section "Why Reusing Indices
+ * Can Work").  idx_a, idx_b: int32 [B][n_q][k] in the layout ix_indexer_topk
+ * writes (ascending valid positions, then -1; another layout gives an
+ * unspecified count but no access outside the rows); counts: int32 [B][n_q].
+ * Only batch, n_q and k of prob are used (prob is still validated).  Needs no
+ * workspace; IX_E_NULL on a NULL pointer, IX_E_SHAPE on misaligned idx
+ * buffers. */
+int32_t ix_index_overlap(const ix_problem* prob, const int32_t* idx_a, const int32_t* idx_b,
+                         int32_t* counts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
-    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "lib_path", "load",
+    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "lib_path", "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
 
@@ -100,6 +100,8 @@ def load():
     lib.ix_topk_scores.restype = c_int32
     lib.ix_topk_scores.argtypes = [POINTER(Problem), c_void_p, c_int64, c_void_p, c_void_p,
                                    c_size_t, c_void_p]
+    lib.ix_index_overlap.restype = c_int32
+    lib.ix_index_overlap.argtypes = [POINTER(Problem), c_void_p, c_void_p, c_void_p, c_void_p]
     _lib = lib
     return lib
 
@@ -275,3 +277,22 @@ def ix_topk_scores(scores, idx, *, q_start=0, kv_len=None, stream=None):
     ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_TOPK_SCORES, None), scores.device)
     _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), _ptr(ws), nb,
                               _stream(stream)), "ix_topk_scores")
+
+
+def ix_index_overlap(idx_a, idx_b, counts=None, *, stream=None):
+    """Per-row count of positions present in both index buffers [B, n_q, k]
+    (negative slots ignored) into ``counts`` int32 [B, n_q] (see ix.h)."""
+    lib = load()
+    _dev(idx_a, "idx_a"), _dev(idx_b, "idx_b")
+    _need(idx_a.dtype == torch.int32 and idx_a.dim() == 3 and idx_b.shape == idx_a.shape
+          and idx_b.dtype == torch.int32, "idx_a, idx_b must be int32 [B, n_q, k] of one shape")
+    B, n_q, k = idx_a.shape
+    if counts is None:
+        counts = torch.empty((B, n_q), dtype=torch.int32, device=idx_a.device)
+    _dev(counts, "counts")
+    _need(counts.dtype == torch.int32 and tuple(counts.shape) == (B, n_q), "counts must be int32 [B, n_q]")
+    prob = _problem(B, n_q, 0, n_q, n_q, k)
+    _check(lib.ix_index_overlap(ctypes.byref(prob), _ptr(idx_a), _ptr(idx_b), _ptr(counts),
+                                _stream(stream)), "ix_index_overlap")
+    return counts
+

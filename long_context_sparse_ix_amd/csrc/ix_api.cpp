@@ -373,4 +373,16 @@ int32_t ix_topk_scores(const ix_problem* p, const float* scores, int64_t ld, int
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
+int32_t ix_index_overlap(const ix_problem* p, const int32_t* idx_a, const int32_t* idx_b, int32_t* counts,
+                         void* stream) {
+  int32_t st = check_problem(p);
+  if (st != IX_OK) return st;
+  if (!idx_a || !idx_b || !counts) return IX_E_NULL;
+  if (!aligned16(idx_a) || !aligned16(idx_b) || (reinterpret_cast<uintptr_t>(counts) & 3u) != 0)
+    return IX_E_SHAPE;
+  hipError_t e = ix::launch_index_overlap(idx_a, idx_b, counts, (int64_t)p->batch * p->n_q, p->k,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
 }  // extern "C"

@@ -67,6 +67,10 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
                             int64_t q_start, int k, void* ws, hipStream_t s,
                             const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0);
 
+// Per-row overlap count of two [rows][k] index buffers (k <= 2048).
+hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int32_t* counts, int64_t rows, int k,
+                                hipStream_t s);
+
 // Sparse gather attention.
 struct AttnArgs {
   const uint16_t* q;      // [B][n_q][Hq][D]

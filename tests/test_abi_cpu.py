@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     ensure_lib()
     names = declared_functions()
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
-            "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error"} <= set(names)
+            "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
+            "ix_index_overlap"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -173,4 +174,15 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 1
+    assert ix.ix_abi_version() == 2
+
+
+def test_index_overlap_validation():
+    lib = ensure_lib()
+    p = _prob()
+    assert lib.ix_index_overlap(ctypes.byref(p), None, DUMMY, DUMMY, None) == ix.IX_E_NULL
+    assert lib.ix_index_overlap(ctypes.byref(p), DUMMY, DUMMY, None, None) == ix.IX_E_NULL
+    assert lib.ix_index_overlap(ctypes.byref(p), DUMMY + 4, DUMMY, DUMMY, None) == ix.IX_E_SHAPE
+    bad = _prob(k=0)
+    assert lib.ix_index_overlap(ctypes.byref(bad), DUMMY, DUMMY, DUMMY, None) == ix.IX_E_SHAPE
+
