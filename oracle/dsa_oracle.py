@@ -80,6 +80,51 @@ def key_matrix(keys, key_dtype: str, scale=None) -> np.ndarray:
     raise ValueError(f"unknown key dtype {key_dtype!r}")
 
 
+# ---------------------------------------------------------- key quantizing --
+E4M3FN_MAX = 448.0
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """float values -> OCP FP8 E4M3FN codes (uint8), round to nearest with ties
+    to the code whose last bit is 0, saturating at +-448 (no NaN input).
+
+    Written as a plain nearest-value search over the 253 finite codes'
+    decoded values, not as bit arithmetic."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode_e4m3fn(codes)
+    finite = ~np.isnan(vals) & ~((codes == 0x80))          # keep one zero (+0)
+    cand_codes = codes[finite]
+    cand_vals = vals[finite]
+    a = np.clip(np.asarray(x, dtype=np.float64), -E4M3FN_MAX, E4M3FN_MAX)
+    flat = a.reshape(-1)
+    out = np.empty(flat.shape[0], dtype=np.uint8)
+    for i, v in enumerate(flat):
+        d = np.abs(cand_vals - v)
+        best = np.flatnonzero(d == d.min())
+        if best.shape[0] > 1:                               # a tie: the even code
+            best = best[(cand_codes[best] & 1) == 0]
+        c = cand_codes[best[0]]
+        if c == 0 and v < 0:                                # a negative value rounding to zero keeps its sign
+            c = np.uint8(0x80)
+        out[i] = c
+    return out.reshape(a.shape)
+
+
+def quantize_key_rows(k_rows):
+    """New indexer key rows (fp32 [..., d]) -> (e4m3fn codes [..., d], fp32
+    scales [...]) in the cache format.
+
+    IndexCache notes, section 1: the indexer keys are stored in FP8.  Reading
+    of the per-row scaling (the pages give none): scale = max_j |k_j| / 448,
+    or 1 for an all-zero row, and code_j = e4m3fn(k_j / scale); the scale and
+    the division are single-precision operations, as the stored format is."""
+    k = np.asarray(k_rows, dtype=np.float32)
+    amax = np.abs(k).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+    y = (k / scale[..., None]).astype(np.float32)
+    return encode_e4m3fn(y), scale
+
+
 # ----------------------------------------------------------------- indexer --
 def indexer_scores(q_row: np.ndarray, w_row: np.ndarray, keys: np.ndarray) -> np.ndarray:
     """score[s] = sum_h w[h] * max(0, q[h, :] . keys[s, :]) in float64.

@@ -71,6 +71,27 @@ def _overlap_slotwise(idx_a, idx_b):
     return ((a == b) & (a >= 0)).sum(axis=-1)
 
 
+def _encode_ties_away(x):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.decode_e4m3fn(codes)
+    keep = ~np.isnan(vals)
+    cv, cc = vals[keep], codes[keep]
+    a = np.clip(np.asarray(x, dtype=np.float64), -448.0, 448.0).reshape(-1)
+    out = np.empty(a.shape[0], dtype=np.uint8)
+    for i, v in enumerate(a):
+        d = np.abs(cv - v)
+        best = np.flatnonzero(d == d.min())
+        out[i] = cc[best[np.argmax(np.abs(cv[best]))]]      # ties away from zero
+    return out.reshape(np.shape(x))
+
+
+def _quantize_fnuz_max(k_rows):
+    k = np.asarray(k_rows, dtype=np.float32)
+    amax = np.abs(k).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(240.0), np.float32(1.0)).astype(np.float32)
+    return O.encode_e4m3fn((k / scale[..., None]).astype(np.float32)), scale
+
+
 ATTN = O.attention_row
 INDEXER = O.indexer_topk
 
@@ -88,6 +109,8 @@ MUTATIONS = [
     ("overlap_counts_padding", "index_overlap", _overlap_counts_padding,
      P.test_overlap_ignores_padding_and_is_symmetric),
     ("overlap_slotwise", "index_overlap", _overlap_slotwise, P.test_overlap_shifted_ranges_closed_form),
+    ("e4m3_ties_away", "encode_e4m3fn", _encode_ties_away, P.test_e4m3fn_encode_matches_torch_on_grid_and_midpoints),
+    ("quantize_fnuz_range", "quantize_key_rows", _quantize_fnuz_max, P.test_quantize_rows_closed_forms),
 ]
 
 

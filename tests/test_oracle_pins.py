@@ -392,3 +392,50 @@ def test_overlap_keeps_leading_shape():
     assert O.index_overlap(a, a).shape == (2, 3)
     with pytest.raises(ValueError):
         O.index_overlap(a, a[:, :2])
+
+
+# ------------------------------------------------------------ key quantizing --
+def test_e4m3fn_encode_matches_torch_on_grid_and_midpoints():
+    """The encoder agrees with torch's float8_e4m3fn conversion (a library
+    routine) on every code value, on the exact midpoints between neighbouring
+    codes (ties to the even code), just beside them, on subnormals, and
+    saturates like torch after clamping to +-448."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.decode_e4m3fn(codes)
+    fin = np.sort(np.unique(vals[~np.isnan(vals)]))
+    mids = (fin[:-1] + fin[1:]) / 2
+    eps = np.abs(mids) * 1e-6 + 1e-12
+    xs = np.concatenate([fin, mids, mids + eps, mids - eps, [500.0, -1e6, 448.001, -448.001, 1e-9, -1e-9]])
+    xs = xs.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(np.clip(xs, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+    ref = ref.view(torch.uint8).numpy()
+    got = O.encode_e4m3fn(xs)
+    # the two zeros decode alike; compare values where the sign of zero differs
+    np.testing.assert_array_equal(O.decode_e4m3fn(got), O.decode_e4m3fn(ref))
+
+
+def test_quantize_rows_closed_forms():
+    """A row of one repeated magnitude v maps to +-448 codes with scale v/448;
+    an all-zero row gets scale 1 and zero codes; the largest magnitude of any
+    row always lands exactly on +-448."""
+    rows = np.array([[3.0, -3.0, 3.0, 3.0], [0.0, 0.0, 0.0, 0.0], [28.0, -14.0, 7.0, 3.5]], dtype=np.float32)
+    codes, scale = O.quantize_key_rows(rows)
+    assert scale[0] == np.float32(3.0) / np.float32(448.0)
+    np.testing.assert_array_equal(O.decode_e4m3fn(codes[0]), [448.0, -448.0, 448.0, 448.0])
+    assert scale[1] == 1.0 and np.all(O.decode_e4m3fn(codes[1]) == 0.0)
+    assert O.decode_e4m3fn(codes[2])[0] == 448.0
+    # amax 28 gives the power-of-two scale 1/16: decoded codes times it
+    # reproduce the row exactly
+    np.testing.assert_array_equal(O.decode_e4m3fn(codes[2]) * scale[2], rows[2].astype(np.float64))
+
+
+def test_quantize_rows_error_bound():
+    """Each decoded value is within half a code step (relative 2^-4 for
+    normals) of the scaled input: e4m3fn has 3 mantissa bits."""
+    rng = np.random.default_rng(11)
+    rows = rng.standard_normal((64, 128)).astype(np.float32)
+    codes, scale = O.quantize_key_rows(rows)
+    y = rows / scale[:, None].astype(np.float64)
+    back = O.decode_e4m3fn(codes)
+    tol = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(back - y) <= tol)
