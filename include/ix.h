@@ -185,6 +185,22 @@ int32_t ix_topk_scores(const ix_problem* prob, const float* scores, int64_t ld, 
 int32_t ix_index_overlap(const ix_problem* prob, const int32_t* idx_a, const int32_t* idx_b,
                          int32_t* counts, void* stream);
 
+/* New indexer keys into the fp8 key cache (the cache format ix_indexer_topk
+ * reads with k_dtype IX_DTYPE_FP8_E4M3FN; the pages store indexer keys in FP8,
+ * IndexCache notes, section 1).  For every sequence b and new row r < n_new,
+ * with x = k_new[(b*n_new + r)*dim + j] (fp32):
+ *   scale = max_j |x_j| / 448 (1 for an all-zero row), correctly rounded fp32;
+ *   code_j = e4m3fn(x_j / scale): correctly rounded fp32 quotient, then round
+ *            to nearest with ties to the even code, saturating at +-448;
+ * codes go to k_cache[(b*kv_cap + pos + r)*dim + j] and the scale to
+ * k_scale[b*kv_cap + pos + r].  Other cache rows are untouched.  Uses batch
+ * and kv_cap of prob (prob is still validated).  dim: a multiple of 16 in
+ * 16..128; n_new >= 0; 0 <= pos and pos + n_new <= kv_cap.  k_new 16-byte
+ * aligned, k_scale 4-byte aligned.  No workspace.  IX_E_NULL on a NULL
+ * pointer, IX_E_SHAPE on a bad size or alignment. */
+int32_t ix_append_keys(const ix_problem* prob, int32_t dim, const float* k_new, int32_t n_new, int64_t pos,
+                       uint8_t* k_cache, float* k_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -157,6 +157,13 @@ def indexer_keys(w: Workload, device, layer: int = 0):
     return codes, scale
 
 
+def new_key_rows(w: Workload, device, step: int = 0, layer: int = 0):
+    """fp32 indexer key rows [B, 1, d] of the token a decode step appends
+    (N(0,1), seeded per step)."""
+    g = _gen(device, w.seed, w.name, "ix_knew", layer, step)
+    return torch.randn((w.batch, 1, w.ix_dim), generator=g, device=device, dtype=torch.float32)
+
+
 def indexer_queries(w: Workload, device, layer: int = 0, step: int = 0):
     """Indexer queries [B, n_q, H, d] bf16 and head weights [B, n_q, H] fp32."""
     g = _gen(device, w.seed, w.name, "ix_q", layer, step)

@@ -23,7 +23,8 @@ import torch
 
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
-    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "lib_path", "load",
+    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys", "lib_path",
+    "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
 
@@ -100,6 +101,9 @@ def load():
     lib.ix_topk_scores.restype = c_int32
     lib.ix_topk_scores.argtypes = [POINTER(Problem), c_void_p, c_int64, c_void_p, c_void_p,
                                    c_size_t, c_void_p]
+    lib.ix_append_keys.restype = c_int32
+    lib.ix_append_keys.argtypes = [POINTER(Problem), c_int32, c_void_p, c_int32, c_int64, c_void_p, c_void_p,
+                                   c_void_p]
     lib.ix_index_overlap.restype = c_int32
     lib.ix_index_overlap.argtypes = [POINTER(Problem), c_void_p, c_void_p, c_void_p, c_void_p]
     _lib = lib
@@ -295,4 +299,23 @@ def ix_index_overlap(idx_a, idx_b, counts=None, *, stream=None):
     _check(lib.ix_index_overlap(ctypes.byref(prob), _ptr(idx_a), _ptr(idx_b), _ptr(counts),
                                 _stream(stream)), "ix_index_overlap")
     return counts
+
+
+def ix_append_keys(k_new, k_cache, k_scale, pos, *, stream=None):
+    """Quantize new fp32 key rows ``k_new`` [B, n_new, d] into the fp8 key
+    cache ``k_cache`` (uint8 e4m3fn codes [B, kv_cap, d]) and ``k_scale``
+    (fp32 [B, kv_cap]) at rows [pos, pos + n_new) (see ix.h)."""
+    lib = load()
+    _dev(k_new, "k_new"), _dev(k_cache, "k_cache"), _dev(k_scale, "k_scale")
+    _need(k_new.dtype == torch.float32 and k_new.dim() == 3, "k_new must be fp32 [B, n_new, d]")
+    kc = k_cache.view(torch.uint8) if k_cache.dtype == torch.float8_e4m3fn else k_cache
+    _need(kc.dtype == torch.uint8 and kc.dim() == 3 and kc.shape[0] == k_new.shape[0]
+          and kc.shape[2] == k_new.shape[2], "k_cache must be e4m3fn codes [B, kv_cap, d]")
+    _need(k_scale.dtype == torch.float32 and tuple(k_scale.shape) == tuple(kc.shape[:2]),
+          "k_scale must be fp32 [B, kv_cap]")
+    B, n_new, d = k_new.shape
+    cap = kc.shape[1]
+    prob = _problem(B, 1, 0, cap, cap, 1)
+    _check(lib.ix_append_keys(ctypes.byref(prob), d, _ptr(k_new), n_new, int(pos), _ptr(kc), _ptr(k_scale),
+                              _stream(stream)), "ix_append_keys")
 

@@ -1,0 +1,76 @@
+// New indexer keys into the fp8 key cache.
+//
+// The indexer keys are stored in FP8 (IndexCache notes, section 1: "few
+// heads, low-rank, FP8").  Per-row scaling (the library's reading; the pages
+// give none): scale = max_j |k_j| / 448, or 1 for an all-zero row, and
+// code_j = e4m3fn(k_j / scale), rounded to nearest with ties to the even code
+// and saturating at +-448; both divisions are correctly rounded fp32.  One
+// wave per new row; every lane encodes two neighbouring elements in software
+// (exact power-of-two rescaling and rintf), so the codes do not depend on a
+// conversion instruction's rounding or saturation mode.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ix {
+
+namespace {
+
+constexpr int kRowsPerWG = 4;
+constexpr float kE4M3Max = 448.0f;
+
+// e4m3fn code of y, |y| <= 448 (round to nearest even; a negative value that
+// rounds to zero keeps its sign bit, -0.0 and +0.0 give +0)
+__device__ __forceinline__ uint32_t e4m3fn_code(float y) {
+  const uint32_t sign = y < 0.0f ? 0x80u : 0u;
+  const float a = fminf(fabsf(y), kE4M3Max);
+  if (a < 0.015625f) {                           // below the smallest normal 2^-6: m * 2^-9
+    const uint32_t m = (uint32_t)rintf(a * 512.0f);   // exact scaling; m == 8 is the smallest normal
+    return sign | m;
+  }
+  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;      // a is a normal fp32 here
+  const float frac = ldexpf(a, -e);                              // exact, in [1, 2)
+  uint32_t m = (uint32_t)rintf((frac - 1.0f) * 8.0f);            // exact operands, one rounding
+  if (m == 8u) {
+    m = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | m;
+}
+
+__global__ __launch_bounds__(kRowsPerWG * kWave) void append_keys_kernel(const float* __restrict__ k_new,
+                                                                         uint8_t* __restrict__ k_cache,
+                                                                         float* __restrict__ k_scale, int n_new,
+                                                                         int64_t rows, int64_t pos, int64_t kv_cap,
+                                                                         int dim) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWG + wave;   // b * n_new + r
+  if (row >= rows) return;
+  const int64_t b = row / n_new, r = row % n_new;
+  const bool on = 2 * l < dim;
+  float2 x = make_float2(0.0f, 0.0f);
+  if (on) x = *reinterpret_cast<const float2*>(k_new + row * dim + 2 * l);
+  float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float scale = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+  const int64_t dst = b * kv_cap + pos + r;
+  if (on) {
+    const uint32_t c0 = e4m3fn_code(__fdiv_rn(x.x, scale));
+    const uint32_t c1 = e4m3fn_code(__fdiv_rn(x.y, scale));
+    *reinterpret_cast<uint16_t*>(k_cache + dst * dim + 2 * l) = (uint16_t)(c0 | (c1 << 8));
+  }
+  if (l == 0) k_scale[dst] = scale;
+}
+
+}  // namespace
+
+hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_scale, int B, int n_new, int64_t pos,
+                              int64_t kv_cap, int dim, hipStream_t s) {
+  const int64_t rows = (int64_t)B * n_new;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_keys_kernel, dim3((unsigned)((rows + kRowsPerWG - 1) / kRowsPerWG)),
+                     dim3(kRowsPerWG * kWave), 0, s, k_new, k_cache, k_scale, n_new, rows, pos, kv_cap, dim);
+  return hipGetLastError();
+}
+
+}  // namespace ix

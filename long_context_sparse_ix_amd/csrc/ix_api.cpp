@@ -385,4 +385,18 @@ int32_t ix_index_overlap(const ix_problem* p, const int32_t* idx_a, const int32_
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
+int32_t ix_append_keys(const ix_problem* p, int32_t dim, const float* k_new, int32_t n_new, int64_t pos,
+                       uint8_t* k_cache, float* k_scale, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != IX_OK) return st;
+  if (!k_new || !k_cache || !k_scale) return IX_E_NULL;
+  if (dim < 16 || dim > 128 || dim % 16 != 0 || n_new < 0 || pos < 0 || pos + n_new > p->kv_cap)
+    return IX_E_SHAPE;
+  if (!aligned16(k_new) || !aligned16(k_cache) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0)
+    return IX_E_SHAPE;
+  hipError_t e = ix::launch_append_keys(k_new, k_cache, k_scale, p->batch, n_new, pos, p->kv_cap, dim,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
 }  // extern "C"

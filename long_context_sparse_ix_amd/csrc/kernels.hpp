@@ -67,6 +67,11 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
                             int64_t q_start, int k, void* ws, hipStream_t s,
                             const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0);
 
+// New fp32 key rows [B][n_new][dim] -> e4m3fn codes and fp32 scales at cache
+// rows [pos, pos + n_new) of every sequence (dim a multiple of 16, <= 128).
+hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_scale, int B, int n_new, int64_t pos,
+                              int64_t kv_cap, int dim, hipStream_t s);
+
 // Per-row overlap count of two [rows][k] index buffers (k <= 2048).
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int32_t* counts, int64_t rows, int k,
                                 hipStream_t s);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
             "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
-            "ix_index_overlap"} <= set(names)
+            "ix_index_overlap", "ix_append_keys"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -185,4 +185,20 @@ def test_index_overlap_validation():
     assert lib.ix_index_overlap(ctypes.byref(p), DUMMY + 4, DUMMY, DUMMY, None) == ix.IX_E_SHAPE
     bad = _prob(k=0)
     assert lib.ix_index_overlap(ctypes.byref(bad), DUMMY, DUMMY, DUMMY, None) == ix.IX_E_SHAPE
+
+
+def test_append_keys_validation():
+    lib = ensure_lib()
+    p = _prob()                                    # kv_cap 8
+    call = lambda dim=32, n=1, pos=0, kn=DUMMY, kc=DUMMY, ks=DUMMY: lib.ix_append_keys(
+        ctypes.byref(p), dim, kn, n, pos, kc, ks, None)
+    assert call(kn=None) == ix.IX_E_NULL
+    assert call(ks=None) == ix.IX_E_NULL
+    assert call(dim=24) == ix.IX_E_SHAPE
+    assert call(dim=144) == ix.IX_E_SHAPE
+    assert call(n=-1) == ix.IX_E_SHAPE
+    assert call(pos=-1) == ix.IX_E_SHAPE
+    assert call(n=3, pos=6) == ix.IX_E_SHAPE         # past kv_cap
+    assert call(kn=DUMMY + 8) == ix.IX_E_SHAPE
+    assert call(ks=DUMMY + 2) == ix.IX_E_SHAPE
 
