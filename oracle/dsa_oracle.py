@@ -32,7 +32,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
 * attention over the selected rows: o = softmax(sm_scale * Q K^T) V with K the
   whole latent row and V its first d_v dims; slots holding -1 (or any value
   outside [0, kv_len)) are ignored; a row with no valid slot gives o = 0 and
-  lse = -inf.
+  lse = -inf;
+* sequences of different lengths in one batch: row t of sequence b sits at
+  its own start q_start[b] + t, with the same candidate rule;
+* MTP draft steps after the first attend over the first step's positions in
+  the first step's KV cache, so no position a later step adds is selected.
 """
 from __future__ import annotations
 
@@ -41,6 +45,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "key_matrix", "indexer_scores", "select_topk",
     "indexer_topk", "indexer_topk_rows", "attention_row", "sparse_attention", "group_forward",
+    "mtp_draft", "index_overlap", "encode_e4m3fn", "quantize_key_rows",
 ]
 
 
@@ -149,25 +154,32 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
-def indexer_topk(q, w, keys, key_dtype, scale, q_start: int, kv_len: int, k: int,
+def indexer_topk(q, w, keys, key_dtype, scale, q_start, kv_len: int, k: int,
                  rows=None) -> np.ndarray:
     """Full-layer indexer + top-k for every (sequence, query row).
 
     q: bf16 bits [B, n_q, H, d]; w: fp32 [B, n_q, H]; keys: [B, cap, d] bf16
-    bits or e4m3fn codes; scale: [B, cap] fp32 (fp8 only).  ``rows`` limits
-    the work to the listed query rows (the result then has len(rows) rows).
-    Returns int32 [B, len(rows), k].
+    bits or e4m3fn codes; scale: [B, cap] fp32 (fp8 only).  q_start: the
+    position of query row 0, one int for every sequence or one per sequence
+    (a batch of sequences of different lengths: row t of sequence b sits at
+    q_start[b] + t and may select the keys up to there, as any query does).
+    ``rows`` limits the work to the listed query rows (the result then has
+    len(rows) rows).  Returns int32 [B, len(rows), k].
     """
     q = np.asarray(q)
     B, n_q = q.shape[0], q.shape[1]
+    starts = ([int(q_start)] * B if np.ndim(q_start) == 0
+              else [int(x) for x in np.asarray(q_start).reshape(-1)])
+    if len(starts) != B:
+        raise ValueError("q_start needs one entry per sequence")
     rows = list(range(n_q)) if rows is None else list(rows)
     out = np.full((B, len(rows), k), -1, dtype=np.int32)
     for b in range(B):
-        p_max = min(q_start + max(rows), kv_len - 1)
+        p_max = min(starts[b] + max(rows), kv_len - 1)
         sc = None if scale is None else np.asarray(scale)[b, : p_max + 1]
         kmat = key_matrix(np.asarray(keys)[b, : p_max + 1], key_dtype, sc)
         for i, t in enumerate(rows):
-            p = q_start + t
+            p = starts[b] + t
             n = min(p, kv_len - 1) + 1
             s = indexer_scores(decode_bf16(q[b, t]), np.asarray(w[b, t], np.float64),
                                kmat[:n])
@@ -241,14 +253,15 @@ def sparse_attention(Q, KV, idx, kv_len: int, sm_scale: float, d_v: int, rows=No
 
 
 # ---------------------------------------------------------------- schedule --
-def group_forward(roles: str, indexer_layers, attn_layers, q_start: int, kv_len: int,
+def group_forward(roles: str, indexer_layers, attn_layers, q_start, kv_len: int,
                   k: int, sm_scale: float, d_v: int, rows=None):
     """Walk one IndexShare layer group.
 
     roles: one letter per layer, "F" (runs indexer + top-k and stores the
     positions) or "S" (reuses the most recent F layer's positions untouched).
     indexer_layers[l] = (q, w, keys, key_dtype, scale) — read for F layers
-    only; attn_layers[l] = (Q, KV).  Returns a dict with per-layer outputs
+    only; attn_layers[l] = (Q, KV).  q_start as in indexer_topk (one int, or
+    one per sequence).  Returns a dict with per-layer outputs
     "O"/"lse", the list "idx" of index buffers (one per F layer), "used" (for
     each layer, which F buffer it attended over) and "n_indexer_runs".
     """
@@ -273,6 +286,32 @@ def group_forward(roles: str, indexer_layers, attn_layers, q_start: int, kv_len:
         outs.append(o)
         lses.append(lse)
     return {"O": outs, "lse": lses, "idx": idx_list, "used": used, "n_indexer_runs": runs}
+
+
+def mtp_draft(indexer_in, draft_q, kv, q_start, kv_len: int, k: int, sm_scale: float, d_v: int,
+              rows=None):
+    """Draft steps of the multi-token-prediction (MTP) layer with index reuse.
+
+    "GLM-5.2 and IndexShare for Long-Context Sparse Attention", section "Reuse
+    in the MTP layer": the first draft step runs the indexer and keeps its
+    positions; every later draft step attends over those same positions in
+    the same, earlier KV cache (nothing the later steps add is selected).
+    indexer_in = (q, w, keys, key_dtype, scale) of the first step's query rows
+    (positions q_start + t); draft_q: one bf16-bit Q [B, n_q, Hq, D] per draft
+    step; kv: the MTP layer's latent cache [B, cap, D], shared by all steps.
+    Returns dict(idx, O: list per step, lse: list per step, n_indexer_runs).
+    """
+    if len(draft_q) < 1:
+        raise ValueError("at least one draft step")
+    q, w, keys, kd, sc = indexer_in
+    idx = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows)
+    outs, lses = [], []
+    for Q in draft_q:
+        o, lse = sparse_attention(Q, kv, idx, kv_len, sm_scale, d_v, rows=rows,
+                                  idx_rows=range(idx.shape[1]))
+        outs.append(o)
+        lses.append(lse)
+    return {"idx": idx, "O": outs, "lse": lses, "n_indexer_runs": 1}
 
 
 # ------------------------------------------------------------- diagnostics --

@@ -122,6 +122,36 @@ def test_pins_catch_planted_mistake(monkeypatch, name, attr, fn, check):
         check()
 
 
+def test_pins_catch_varlen_sharing_one_start(monkeypatch):
+    """Giving every sequence the largest start (the per-sequence starts
+    ignored) fails the brute-force batch pin."""
+    def one_start(q, w, keys, key_dtype, scale, q_start, kv_len, k, rows=None):
+        return INDEXER(q, w, keys, key_dtype, scale, int(np.max(q_start)), kv_len, k, rows)
+    P.test_varlen_batch_brute_force_tiny()
+    monkeypatch.setattr(O, "indexer_topk", one_start)
+    with pytest.raises(AssertionError):
+        P.test_varlen_batch_brute_force_tiny()
+
+
+def test_pins_catch_mtp_steps_selecting_again(monkeypatch):
+    """Later draft steps that rerun the selection at their own positions (and
+    so see the rows the cache holds past the first step) fail the MTP pin."""
+    def reselect(indexer_in, draft_q, kv, q_start, kv_len, k, sm_scale, d_v, rows=None):
+        q, w, keys, kd, sc = indexer_in
+        outs, lses = [], []
+        for j, Q in enumerate(draft_q):
+            idx = INDEXER(q, w, keys, kd, sc, q_start + j, kv_len, k, rows=rows)
+            o, lse = O.sparse_attention(Q, kv, idx, kv_len, sm_scale, d_v, rows=rows,
+                                        idx_rows=range(idx.shape[1]))
+            outs.append(o)
+            lses.append(lse)
+        return {"idx": idx, "O": outs, "lse": lses, "n_indexer_runs": 1}
+    P.test_mtp_draft_later_steps_attend_over_the_first_steps_prefix()
+    monkeypatch.setattr(O, "mtp_draft", reselect)
+    with pytest.raises(AssertionError):
+        P.test_mtp_draft_later_steps_attend_over_the_first_steps_prefix()
+
+
 def test_pins_catch_self_excluded_causality(monkeypatch):
     """A query that may not select its own position changes the hand-worked
     p=4, k=5 row (position 4 would be missing)."""

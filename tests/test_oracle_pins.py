@@ -139,6 +139,41 @@ def test_indexer_topk_brute_force_tiny_end_to_end():
         assert got[0, 0].tolist() == _brute_topk(ref, k)
 
 
+def _loop_scores(qv, wv, kv, n):
+    """score[s] for s < n by explicit loops (qv [H, d], wv [H], kv [>=n, d])."""
+    ref = []
+    for s in range(n):
+        tot = 0.0
+        for h in range(qv.shape[0]):
+            dot = sum(float(qv[h, j]) * float(kv[s, j]) for j in range(qv.shape[1]))
+            tot += float(wv[h]) * (dot if dot > 0 else 0.0)
+        ref.append(tot)
+    return ref
+
+
+def test_varlen_batch_brute_force_tiny():
+    """Sequences of different lengths in one batch: row t of sequence b sits
+    at its own start + t and selects among that many + 1 keys of its own
+    sequence; checked row by row against loop-summed scores and the
+    subset-enumeration selection."""
+    rng = np.random.default_rng(3)
+    for _ in range(8):
+        B, n_q, H, d = int(rng.integers(2, 4)), int(rng.integers(1, 3)), 2, 3
+        starts = [int(x) for x in rng.integers(0, 6, size=B)]
+        kv_len = max(starts) + n_q
+        qv = rng.integers(-3, 4, size=(B, n_q, H, d)).astype(np.float32)
+        kv = rng.integers(-3, 4, size=(B, kv_len, d)).astype(np.float32)
+        wv = rng.choice([-1.0, 1.0, 2.0], size=(B, n_q, H)).astype(np.float32)
+        k = int(rng.integers(1, 6))
+        got = O.indexer_topk(bf16_bits(qv), wv, bf16_bits(kv), "bf16", None, q_start=starts,
+                             kv_len=kv_len, k=k)
+        for b in range(B):
+            for t in range(n_q):
+                p = starts[b] + t
+                ref = _loop_scores(qv[b, t], wv[b, t], kv[b], p + 1)
+                assert got[b, t].tolist() == _brute_topk(ref, k), (starts, b, t)
+
+
 # ------------------------------------------------------------ closed forms --
 def _ix(q, w, keys, q_start, kv_len, k, kd="bf16", scale=None):
     return O.indexer_topk(q, w, keys, kd, scale, q_start, kv_len, k)
@@ -333,6 +368,33 @@ def test_schedule_rejects_leading_shared_layer():
     ixl, atl = _group_inputs(rng, "SFSS")
     with pytest.raises(ValueError):
         O.group_forward("SFSS", ixl, atl, 0, 24, 5, 0.35, 6)
+
+
+def test_mtp_draft_later_steps_attend_over_the_first_steps_prefix():
+    """MTP draft steps: the first step selects with k >= its candidate count,
+    so it keeps the whole prefix 0..pos; the cache already holds the rows of
+    the later draft tokens (kv_len = pos + steps), yet every step must equal
+    dense attention over rows 0..pos only (torch's scaled_dot_product_attention
+    in float64), and the indexer runs once."""
+    rng = np.random.default_rng(16)
+    pos, steps, Hq, D, Dv, H, d = 9, 4, 2, 8, 6, 2, 4
+    kv_len = pos + steps
+    q = bf16_bits(rng.integers(-8, 9, (1, 1, H, d)))
+    w = rng.choice([1.0, 2.0], (1, 1, H)).astype(np.float32)
+    keys = bf16_bits(rng.integers(-8, 9, (1, kv_len, d)))
+    KV = _rand_bf16(rng, (1, kv_len, D))
+    drafts = [_rand_bf16(rng, (1, 1, Hq, D)) for _ in range(steps)]
+    sm = 0.4
+    r = O.mtp_draft((q, w, keys, "bf16", None), drafts, KV, pos, kv_len, 16, sm, Dv)
+    assert r["n_indexer_runs"] == 1 and len(r["O"]) == steps
+    assert r["idx"][0, 0].tolist() == list(range(pos + 1)) + [-1] * (16 - pos - 1)
+    kvt = torch.from_numpy(O.decode_bf16(KV[0, : pos + 1]))
+    for j in range(steps):
+        qq = torch.from_numpy(O.decode_bf16(drafts[j][0, 0]))[None, :, None, :]     # [1,Hq,1,D]
+        kk = kvt[None, None].expand(1, Hq, pos + 1, D)
+        vv = kvt[None, None, :, :Dv].expand(1, Hq, pos + 1, Dv)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=sm)
+        np.testing.assert_allclose(r["O"][j][0, 0], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
 
 
 def test_oracle_exports():
