@@ -22,6 +22,12 @@
  *   - Query row t of a sequence sits at absolute position p = q_start + t and
  *     may select any key position s with 0 <= s <= p (itself included).
  *     q_start + n_q <= kv_len <= kv_cap is required.
+ *   - Sequences of different lengths (serving batches): with
+ *     ix_problem.seq_q_start set, row t of sequence b sits at
+ *     p = seq_q_start[b] + t instead, and q_start is the largest start, which
+ *     sizes the launches and the workspace.  A sequence's keys past its own
+ *     last row are never read, so its valid length needs no array of its own;
+ *     kv_len stays the common bound.
  *   - All pointers except the problem/descriptor structs are DEVICE pointers
  *     (HBM of the current HIP device) and must be 16-byte aligned.  The
  *     caller allocates and owns every buffer, including the workspace; the
@@ -46,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 2
+#define IX_ABI_VERSION 3
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -86,6 +92,15 @@ typedef struct ix_problem {
   int64_t kv_cap;   /* allocated rows per sequence (row stride), >= kv_len     */
   int32_t k;        /* positions kept per query row, 1 <= k <= 2048            */
   int32_t reserved; /* must be 0                                               */
+  /* NULL (every sequence starts at q_start), or a DEVICE array int64 [batch]
+   * (8-byte aligned) of per-sequence starts, each in [0, q_start]; q_start is
+   * then their maximum or any larger value that keeps q_start + n_q <= kv_len.
+   * The values are read by the kernels, not by the host: an entry outside
+   * [0, q_start] is clamped into it (its sequence's result is then that of the
+   * clamped start; memory accesses stay inside the buffers either way).  Used
+   * by ix_indexer_topk, ix_group_forward (full layers), ix_topk_scores and
+   * ix_append_keys; attention reads positions from idx only. */
+  const int64_t* seq_q_start;
 } ix_problem;
 
 /* Inputs of one full layer's indexer.
@@ -164,7 +179,7 @@ int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_ma
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Top-k over caller-provided fp32 score rows: scores[(b*n_q + t)*ld + s] for
- * s <= p = q_start + t (entries beyond p are ignored).  Same selection rule
+ * s <= p = q_start + t, or seq_q_start[b] + t (entries beyond p are ignored).  Same selection rule
  * and output layout as ix_indexer_topk.  ld >= kv_len.  Scores must not be
  * NaN.  Calls with few long rows (B*n_q < 1024 and q_start + n_q > k) keep
  * their select state in ws, of ix_workspace_bytes(prob, IX_OP_TOPK_SCORES,
@@ -192,12 +207,17 @@ int32_t ix_index_overlap(const ix_problem* prob, const int32_t* idx_a, const int
  *   scale = max_j |x_j| / 448 (1 for an all-zero row), correctly rounded fp32;
  *   code_j = e4m3fn(x_j / scale): correctly rounded fp32 quotient, then round
  *            to nearest with ties to the even code, saturating at +-448;
- * codes go to k_cache[(b*kv_cap + pos + r)*dim + j] and the scale to
- * k_scale[b*kv_cap + pos + r].  Other cache rows are untouched.  Uses batch
- * and kv_cap of prob (prob is still validated).  dim: a multiple of 16 in
- * 16..128; n_new >= 0; 0 <= pos and pos + n_new <= kv_cap.  k_new 16-byte
- * aligned, k_scale 4-byte aligned.  No workspace.  IX_E_NULL on a NULL
- * pointer, IX_E_SHAPE on a bad size or alignment. */
+ * codes go to k_cache[(b*kv_cap + pos_b + r)*dim + j] and the scale to
+ * k_scale[b*kv_cap + pos_b + r], where pos_b = pos, or, with
+ * prob->seq_q_start set, pos_b = pos - q_start + seq_q_start[b] (the entry
+ * clamped into [0, q_start] as everywhere): each sequence's rows move down by
+ * its distance below the largest start, so pos = q_start appends the new
+ * token of a decode step at every sequence's own position.  Other cache rows
+ * are untouched.  Uses batch, q_start, seq_q_start and kv_cap of prob (prob
+ * is still validated).  dim: a multiple of 16 in 16..128; n_new >= 0;
+ * 0 <= pos and pos + n_new <= kv_cap, and pos >= q_start when seq_q_start is
+ * set.  k_new 16-byte aligned, k_scale 4-byte aligned.  No workspace.
+ * IX_E_NULL on a NULL pointer, IX_E_SHAPE on a bad size or alignment. */
 int32_t ix_append_keys(const ix_problem* prob, int32_t dim, const float* k_new, int32_t n_new, int64_t pos,
                        uint8_t* k_cache, float* k_scale, void* stream);
 

@@ -30,6 +30,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
+ABI_VERSION = 3
 IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
 IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
 IX_PATH_AUTO, IX_PATH_FUSED, IX_PATH_MATERIALIZED = 0, 1, 2
@@ -38,7 +39,7 @@ IX_OP_INDEXER_TOPK, IX_OP_SPARSE_ATTN, IX_OP_GROUP_FORWARD, IX_OP_TOPK_SCORES = 
 
 class Problem(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("n_q", c_int32), ("q_start", c_int64), ("kv_len", c_int64),
-                ("kv_cap", c_int64), ("k", c_int32), ("reserved", c_int32)]
+                ("kv_cap", c_int64), ("k", c_int32), ("reserved", c_int32), ("seq_q_start", c_void_p)]
 
 
 class IndexerIn(ctypes.Structure):
@@ -106,6 +107,8 @@ def load():
                                    c_void_p]
     lib.ix_index_overlap.restype = c_int32
     lib.ix_index_overlap.argtypes = [POINTER(Problem), c_void_p, c_void_p, c_void_p, c_void_p]
+    if lib.ix_abi_version() != ABI_VERSION:   # the structs above follow this version of ix.h
+        raise ImportError(f"{LIB_PATH} has ABI {lib.ix_abi_version()}, this binding needs {ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 
@@ -153,8 +156,19 @@ def _workspace(nbytes: int, device):
     return buf, nbytes
 
 
-def _problem(batch, n_q, q_start, kv_len, kv_cap, k):
-    return Problem(batch, n_q, int(q_start), int(kv_len), int(kv_cap), int(k), 0)
+def _problem(batch, n_q, q_start, kv_len, kv_cap, k, seq_q_start=None):
+    return Problem(batch, n_q, int(q_start), int(kv_len), int(kv_cap), int(k), 0, _ptr(seq_q_start))
+
+
+def _starts(seq_q_start, q_start, batch):
+    """Checks a per-sequence start array and returns the common bound: the
+    given q_start, or (None) the array's maximum, which costs a device sync."""
+    if seq_q_start is None:
+        return 0 if q_start is None else int(q_start)
+    _dev(seq_q_start, "seq_q_start")
+    _need(seq_q_start.dtype == torch.int64 and tuple(seq_q_start.shape) == (batch,),
+          "seq_q_start must be int64 [B] on the device")
+    return int(seq_q_start.max().item()) if q_start is None else int(q_start)
 
 
 def _key_dtype(keys):
@@ -208,14 +222,19 @@ def ix_workspace_bytes(prob: Problem, op: int, desc) -> int:
     return load().ix_workspace_bytes(ctypes.byref(prob), op, ref)
 
 
-def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=0, kv_len=None, path=IX_PATH_AUTO,
-                    stream=None):
-    """Full-layer indexer + top-k into ``idx`` int32 [B, n_q, k] (see ix.h)."""
+def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=None, kv_len=None, path=IX_PATH_AUTO,
+                    seq_q_start=None, stream=None):
+    """Full-layer indexer + top-k into ``idx`` int32 [B, n_q, k] (see ix.h).
+
+    ``seq_q_start`` (int64 [B] on the device, optional): per-sequence position
+    of row 0; ``q_start`` is then their bound (default: their maximum)."""
     lib = load()
     _dev(idx, "idx")
     _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(q.shape[:2]), "idx must be int32 [B, n_q, k]")
     cap = keys.shape[1]
-    prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2])
+    q_start = _starts(seq_q_start, q_start, q.shape[0])
+    prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2],
+                    seq_q_start)
     desc = _indexer_in(q, w, keys, k_scale, path)
     ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, desc), q.device)
     _check(lib.ix_indexer_topk(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
@@ -236,13 +255,14 @@ def ix_sparse_attn(q, kv, idx, out, *, lse=None, q_start=0, kv_len=None, sm_scal
                               _stream(stream)), "ix_sparse_attn")
 
 
-def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=0, kv_len=None,
-                     sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, stream=None):
+def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=None, kv_len=None,
+                     sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, seq_q_start=None, stream=None):
     """One IndexShare layer group (see ix.h).
 
     indexer_layers[l]: dict(q=, w=, keys=, k_scale=) for full layers (None for
     shared ones); attn_layers[l]: dict(q=, kv=, out=, lse=).  Bit l of f_mask
-    marks layer l full.  idx: int32 [n_full, B, n_q, k]."""
+    marks layer l full.  idx: int32 [n_full, B, n_q, k].  ``seq_q_start`` as
+    in ix_indexer_topk."""
     lib = load()
     n = len(attn_layers)
     _need(len(indexer_layers) == n, "one indexer entry per layer (None for shared layers)")
@@ -251,7 +271,8 @@ def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=0
     a0 = attn_layers[0]
     B, n_q = a0["q"].shape[0], a0["q"].shape[1]
     cap = a0["kv"].shape[1]
-    prob = _problem(B, n_q, q_start, cap if kv_len is None else kv_len, cap, idx.shape[3])
+    q_start = _starts(seq_q_start, q_start, B)
+    prob = _problem(B, n_q, q_start, cap if kv_len is None else kv_len, cap, idx.shape[3], seq_q_start)
     ixr = (IndexerIn * n)()
     att = (AttnIn * n)()
     for l in range(n):
@@ -269,15 +290,17 @@ def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=0
                                 _stream(stream)), "ix_group_forward")
 
 
-def ix_topk_scores(scores, idx, *, q_start=0, kv_len=None, stream=None):
-    """Top-k over fp32 score rows ``scores`` [B, n_q, ld] into idx [B, n_q, k]."""
+def ix_topk_scores(scores, idx, *, q_start=None, kv_len=None, seq_q_start=None, stream=None):
+    """Top-k over fp32 score rows ``scores`` [B, n_q, ld] into idx [B, n_q, k]
+    (``seq_q_start`` as in ix_indexer_topk)."""
     lib = load()
     _dev(scores, "scores"), _dev(idx, "idx")
     _need(scores.dtype == torch.float32 and scores.dim() == 3, "scores must be fp32 [B, n_q, ld]")
     _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(scores.shape[:2]), "idx must be int32 [B, n_q, k]")
     ld = scores.shape[2]
+    q_start = _starts(seq_q_start, q_start, scores.shape[0])
     prob = _problem(scores.shape[0], scores.shape[1], q_start, ld if kv_len is None else kv_len,
-                    ld if kv_len is None else kv_len, idx.shape[2])
+                    ld if kv_len is None else kv_len, idx.shape[2], seq_q_start)
     ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_TOPK_SCORES, None), scores.device)
     _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), _ptr(ws), nb,
                               _stream(stream)), "ix_topk_scores")
@@ -301,10 +324,13 @@ def ix_index_overlap(idx_a, idx_b, counts=None, *, stream=None):
     return counts
 
 
-def ix_append_keys(k_new, k_cache, k_scale, pos, *, stream=None):
+def ix_append_keys(k_new, k_cache, k_scale, pos=None, *, seq_pos=None, stream=None):
     """Quantize new fp32 key rows ``k_new`` [B, n_new, d] into the fp8 key
     cache ``k_cache`` (uint8 e4m3fn codes [B, kv_cap, d]) and ``k_scale``
-    (fp32 [B, kv_cap]) at rows [pos, pos + n_new) (see ix.h)."""
+    (fp32 [B, kv_cap]) at rows [pos, pos + n_new) (see ix.h).
+
+    ``seq_pos`` (int64 [B] on the device, optional): each sequence's own first
+    row instead; ``pos`` is then their bound (default: their maximum)."""
     lib = load()
     _dev(k_new, "k_new"), _dev(k_cache, "k_cache"), _dev(k_scale, "k_scale")
     _need(k_new.dtype == torch.float32 and k_new.dim() == 3, "k_new must be fp32 [B, n_new, d]")
@@ -315,7 +341,11 @@ def ix_append_keys(k_new, k_cache, k_scale, pos, *, stream=None):
           "k_scale must be fp32 [B, kv_cap]")
     B, n_new, d = k_new.shape
     cap = kc.shape[1]
-    prob = _problem(B, 1, 0, cap, cap, 1)
+    _need(pos is not None or seq_pos is not None, "give pos or seq_pos")
+    pos = _starts(seq_pos, pos, B)
+    # with per-sequence rows the bound pos is the problem's q_start, so row
+    # pos_b = pos - q_start + seq_pos[b] = seq_pos[b]
+    prob = _problem(B, 1, 0 if seq_pos is None else pos, cap, cap, 1, seq_pos)
     _check(lib.ix_append_keys(ctypes.byref(prob), d, _ptr(k_new), n_new, int(pos), _ptr(kc), _ptr(k_scale),
                               _stream(stream)), "ix_append_keys")
 

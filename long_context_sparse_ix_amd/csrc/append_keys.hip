@@ -40,8 +40,9 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float y) {
 __global__ __launch_bounds__(kRowsPerWG * kWave) void append_keys_kernel(const float* __restrict__ k_new,
                                                                          uint8_t* __restrict__ k_cache,
                                                                          float* __restrict__ k_scale, int n_new,
-                                                                         int64_t rows, int64_t pos, int64_t kv_cap,
-                                                                         int dim) {
+                                                                         int64_t rows, int64_t pos,
+                                                                         const int64_t* __restrict__ seq_shift,
+                                                                         int64_t shift_bound, int64_t kv_cap, int dim) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerWG + wave;   // b * n_new + r
   if (row >= rows) return;
@@ -53,7 +54,9 @@ __global__ __launch_bounds__(kRowsPerWG * kWave) void append_keys_kernel(const f
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
   const float scale = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
-  const int64_t dst = b * kv_cap + pos + r;
+  // per-sequence rows: shifted back by the sequence's distance below the bound
+  const int64_t pos_b = seq_shift ? pos - shift_bound + seq_start(seq_shift, (int)b, shift_bound) : pos;
+  const int64_t dst = b * kv_cap + pos_b + r;
   if (on) {
     const uint32_t c0 = e4m3fn_code(__fdiv_rn(x.x, scale));
     const uint32_t c1 = e4m3fn_code(__fdiv_rn(x.y, scale));
@@ -65,11 +68,13 @@ __global__ __launch_bounds__(kRowsPerWG * kWave) void append_keys_kernel(const f
 }  // namespace
 
 hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_scale, int B, int n_new, int64_t pos,
-                              int64_t kv_cap, int dim, hipStream_t s) {
+                              const int64_t* seq_shift, int64_t shift_bound, int64_t kv_cap, int dim,
+                              hipStream_t s) {
   const int64_t rows = (int64_t)B * n_new;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(append_keys_kernel, dim3((unsigned)((rows + kRowsPerWG - 1) / kRowsPerWG)),
-                     dim3(kRowsPerWG * kWave), 0, s, k_new, k_cache, k_scale, n_new, rows, pos, kv_cap, dim);
+                     dim3(kRowsPerWG * kWave), 0, s, k_new, k_cache, k_scale, n_new, rows, pos, seq_shift,
+                     shift_bound, kv_cap, dim);
   return hipGetLastError();
 }
 

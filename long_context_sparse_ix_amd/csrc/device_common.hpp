@@ -75,6 +75,16 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   return v;
 }
 
+// Position of query row 0 of sequence b: the sequence's own start when a
+// per-sequence array is given (clamped into [0, bound], so a bad entry can
+// never move a read past the keys every launch is sized for), else the common
+// start `bound`.
+__device__ __forceinline__ int64_t seq_start(const int64_t* seq, int b, int64_t bound) {
+  if (!seq) return bound;
+  const int64_t v = seq[b];
+  return v < 0 ? 0 : (v > bound ? bound : v);
+}
+
 // max(x, 0) as one v_med3_f32 (x clamped to [0, +inf]).  fmaxf would add a
 // NaN-quieting max in front; the callers' inputs (MFMA dot products of finite
 // bf16 values) are never NaN.

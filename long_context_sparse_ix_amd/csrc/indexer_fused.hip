@@ -370,9 +370,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   const int row0 = (gridDim.x - 1 - blockIdx.x) * kRowsPerWG;
   const int t = row0 + wave;
   const bool row_ok = t < a.n_q;
-  const int p = (int)a.q_start + (row_ok ? t : 0);              // positions fit in int32
+  const int qs = uniform((int)seq_start(a.seq_q_start, b, a.q_start));   // positions fit in int32
+  const int p = qs + (row_ok ? t : 0);
   const int last_row = min(row0 + kRowsPerWG - 1, a.n_q - 1);
-  const int n_keys = (int)a.q_start + last_row + 1;
+  const int n_keys = qs + last_row + 1;
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
   const int C = a.C;
   const Cand cand{a.cand + ((int64_t)b * a.n_q + (row_ok ? t : 0)) * C};

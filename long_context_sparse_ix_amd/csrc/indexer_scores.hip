@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
   const int m = l & 31, hf = l >> 5;
   const int row = blockIdx.y;                 // b * n_q + t
   const int b = row / a.n_q, t = row % a.n_q;
-  const int64_t p = a.q_start + t;
+  const int64_t p = seq_start(a.seq_q_start, b, a.q_start) + t;
   const int64_t s_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kTilesPerWave * kTileKeys;
   if (s_begin > p) return;
   const int n_tiles = (int)min<int64_t>(kTilesPerWave, (p - s_begin) / kTileKeys + 1);

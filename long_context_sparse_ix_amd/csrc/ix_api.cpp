@@ -33,6 +33,7 @@ int32_t check_problem(const ix_problem* p) {
     return IX_E_SHAPE;
   if (p->kv_len < p->q_start + p->n_q || p->kv_cap < p->kv_len) return IX_E_SHAPE;
   if (p->kv_len > (int64_t)INT32_MAX) return IX_E_SHAPE;   // positions are int32
+  if ((reinterpret_cast<uintptr_t>(p->seq_q_start) & 7u) != 0) return IX_E_SHAPE;
   return IX_OK;
 }
 
@@ -156,6 +157,7 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
     a.w = in->w;
     a.idx = idx;
     a.q_start = p->q_start;
+    a.seq_q_start = p->seq_q_start;
     a.n_q = p->n_q;
     a.H = in->heads;
     a.k = p->k;
@@ -186,13 +188,14 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
   a.scale_bstride = p->kv_cap;
   a.ld = score_ld(p);
   a.q_start = p->q_start;
+  a.seq_q_start = p->seq_q_start;
   a.n_q = p->n_q;
   a.H = in->heads;
   a.rng = reinterpret_cast<float2*>(static_cast<char*>(ws) + score_bytes(p));
   a.rng_stride = rng_stride(p);
   hipError_t e = ix::launch_indexer_scores(a, p->batch, in->dim, fp8, p->kv_len, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
+  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->seq_q_start, p->k,
                            static_cast<char*>(ws) + score_bytes(p) + rng_bytes(p), s, a.rng, ix::kScoreSpan,
                            a.rng_stride);
   return e == hipSuccess ? IX_OK : hip_fail(e);
@@ -368,8 +371,8 @@ int32_t ix_topk_scores(const ix_problem* p, const float* scores, int64_t ld, int
   if (ld < p->kv_len || !aligned16(scores) || !aligned16(idx)) return IX_E_SHAPE;
   st = check_ws(topk_ws(p), ws, ws_bytes);
   if (st != IX_OK) return st;
-  hipError_t e = ix::launch_topk_rows(scores, ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->k,
-                                      ws, static_cast<hipStream_t>(stream));
+  hipError_t e = ix::launch_topk_rows(scores, ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->seq_q_start,
+                                      p->k, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
@@ -392,10 +395,11 @@ int32_t ix_append_keys(const ix_problem* p, int32_t dim, const float* k_new, int
   if (!k_new || !k_cache || !k_scale) return IX_E_NULL;
   if (dim < 16 || dim > 128 || dim % 16 != 0 || n_new < 0 || pos < 0 || pos + n_new > p->kv_cap)
     return IX_E_SHAPE;
+  if (p->seq_q_start && pos < p->q_start) return IX_E_SHAPE;   // keeps every shifted row >= 0
   if (!aligned16(k_new) || !aligned16(k_cache) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0)
     return IX_E_SHAPE;
-  hipError_t e = ix::launch_append_keys(k_new, k_cache, k_scale, p->batch, n_new, pos, p->kv_cap, dim,
-                                        static_cast<hipStream_t>(stream));
+  hipError_t e = ix::launch_append_keys(k_new, k_cache, k_scale, p->batch, n_new, pos, p->seq_q_start,
+                                        p->q_start, p->kv_cap, dim, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 

@@ -17,7 +17,8 @@ struct FusedArgs {
   float2* cand;           // workspace: [B][n_q][C] (score, position bits) candidate buffers
   int64_t key_bstride;    // elements
   int64_t scale_bstride;  // elements
-  int64_t q_start;
+  int64_t q_start;        // row 0's position (with seq_q_start: the largest start)
+  const int64_t* seq_q_start;   // nullable: per-sequence start of row 0 [B]
   int n_q, H, k, C;       // C: candidate slots per row (>= k + 64)
 };
 size_t fused_lds_bytes(int d);
@@ -46,7 +47,8 @@ struct ScoreArgs {
   int64_t key_bstride;    // elements
   int64_t scale_bstride;
   int64_t ld;
-  int64_t q_start;
+  int64_t q_start;        // row 0's position (with seq_q_start: the largest start)
+  const int64_t* seq_q_start;   // nullable: per-sequence start of row 0 [B]
   int n_q, H;
   float2* rng;            // nullable: per-wave (min, max) of the written scores,
                           // [rows][rng_stride], one entry per kScoreSpan keys
@@ -63,14 +65,19 @@ hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int
 // rng_span scores, rng_stride entries per row; without it the select measures
 // the ranges itself.
 size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k);
+// Row r = b * n_q + t holds the candidates 0 .. start_b + t, start_b the
+// per-sequence start seq_q_start[b] (clamped into [0, q_start]) or q_start.
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, void* ws, hipStream_t s,
+                            int64_t q_start, const int64_t* seq_q_start, int k, void* ws, hipStream_t s,
                             const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0);
 
 // New fp32 key rows [B][n_new][dim] -> e4m3fn codes and fp32 scales at cache
-// rows [pos, pos + n_new) of every sequence (dim a multiple of 16, <= 128).
+// rows [pos_b, pos_b + n_new) of sequence b (dim a multiple of 16, <= 128):
+// pos_b = pos, or with seq_shift, pos - shift_bound + seq_shift[b] (the entry
+// clamped into [0, shift_bound]; the caller keeps pos >= shift_bound).
 hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_scale, int B, int n_new, int64_t pos,
-                              int64_t kv_cap, int dim, hipStream_t s);
+                              const int64_t* seq_shift, int64_t shift_bound, int64_t kv_cap, int dim,
+                              hipStream_t s);
 
 // Per-row overlap count of two [rows][k] index buffers (k <= 2048).
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int32_t* counts, int64_t rows, int k,

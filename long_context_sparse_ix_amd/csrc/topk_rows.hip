@@ -52,8 +52,9 @@ struct RowSel {
 constexpr int kFallback = -1;            // too many candidates: whole-row select
 constexpr int kTrivial = -2;             // p + 1 <= k: keep every position
 
-__device__ __forceinline__ int row_len(int row, int n_q, int64_t q_start) {
-  return (int)(q_start + row % n_q + 1);
+// Candidates of row `row` (= b * n_q + t): positions 0 .. start_b + t.
+__device__ __forceinline__ int row_len(int row, int n_q, int64_t q_start, const int64_t* seq) {
+  return (int)(seq_start(seq, row / n_q, q_start) + row % n_q + 1);
 }
 
 __device__ __forceinline__ int vbin(float s, float lo, float inv, int nbins) {
@@ -246,9 +247,10 @@ __device__ void write_trivial(int32_t* dst, int n, int k) {
 
 __global__ __launch_bounds__(kFT) void topk_rows_single_kernel(const float* __restrict__ scores, int64_t ld,
                                                                int32_t* __restrict__ idx, int n_q,
-                                                               int64_t q_start, int k) {
+                                                               int64_t q_start, const int64_t* seq,
+                                                               int k) {
   const int row = blockIdx.x;
-  const int n = row_len(row, n_q, q_start);
+  const int n = row_len(row, n_q, q_start, seq);
   int32_t* dst = idx + (int64_t)row * k;
   if (n <= k) {
     write_trivial(dst, n, k);
@@ -264,6 +266,7 @@ struct ChunkArgs {
   int64_t ld;
   int n_q;
   int64_t q_start;
+  const int64_t* seq;   // nullable: per-sequence start of row 0
   int k;
   int G;           // chunks per row (of the longest row)
   int vec;         // rows are 16-byte aligned: load float4
@@ -312,7 +315,7 @@ __device__ __forceinline__ void row_binning(const float2* rng, int G, float* red
 __global__ __launch_bounds__(kCT) void tk_range_kernel(ChunkArgs a) {
   __shared__ float red[kCT / kWave];
   const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
-  const int n = row_len(row, a.n_q, a.q_start);
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
   const int base = g * kChunk;
   if (n <= a.k || base >= n) return;
   const int i0 = base + threadIdx.x * kPT;
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(kCT) void tk_hist_kernel(ChunkArgs a) {
   __shared__ uint32_t h[kVB];
   __shared__ float red[kCT / kWave];
   const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
-  const int n = row_len(row, a.n_q, a.q_start);
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
   const int base = g * kChunk;
   if (n <= a.k || base >= n) return;
   const int i0 = base + threadIdx.x * kPT;
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
   __shared__ int sh_vb, sh_above, sh_h;
   __shared__ int cnt[kST];                       // per-chunk counts, kST at a time
   const int row = blockIdx.x, tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
-  const int n = row_len(row, a.n_q, a.q_start);
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
   if (n <= a.k) {
     if (tid == 0) a.sel[row] = RowSel{0.0f, 0.0f, 0, kTrivial, 0, {}};
     return;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kST) void tk_select_kernel(ChunkArgs a) {
 __global__ __launch_bounds__(kCT) void tk_collect_kernel(ChunkArgs a) {
   __shared__ int redi[kCT / kWave];
   const int row = blockIdx.x / a.G, g = blockIdx.x % a.G;
-  const int n = row_len(row, a.n_q, a.q_start);
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
   const int base = g * kChunk;
   if (n <= a.k || base >= n) return;
   const RowSel rs = a.sel[row];
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
   __shared__ int redi[kFT / kWave];
   __shared__ int sel_bin, sel_above;
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int n = row_len(row, a.n_q, a.q_start);
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
   int32_t* dst = idx + (int64_t)row * a.k;
   const RowSel rs = a.sel[row];
   if (rs.m == kTrivial) {
@@ -539,12 +542,12 @@ size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k) {
 }
 
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
-                            int64_t q_start, int k, void* ws, hipStream_t s, const float2* rng,
-                            int rng_span, int rng_stride) {
+                            int64_t q_start, const int64_t* seq_q_start, int k, void* ws, hipStream_t s,
+                            const float2* rng, int rng_span, int rng_stride) {
   const int64_t max_n = q_start + n_q;
   if (topk_rows_ws_bytes(rows, max_n, k) == 0) {
     hipLaunchKernelGGL(topk_rows_single_kernel, dim3(rows), dim3(kFT), 0, s, scores, ld, idx, n_q,
-                       q_start, k);
+                       q_start, seq_q_start, k);
     return hipGetLastError();
   }
   if (ws == nullptr) return hipErrorInvalidValue;
@@ -553,6 +556,7 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
   a.ld = ld;
   a.n_q = n_q;
   a.q_start = q_start;
+  a.seq = seq_q_start;
   a.k = k;
   a.G = (int)chunks_per_row(max_n);
   a.vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0) ? 1 : 0;

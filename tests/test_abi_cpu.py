@@ -48,7 +48,7 @@ def test_struct_layout_matches_header():
 int main(void) {
   printf("ix_problem %zu\nix_indexer_in %zu\nix_attn_in %zu\nix_group_desc %zu\n",
          sizeof(ix_problem), sizeof(ix_indexer_in), sizeof(ix_attn_in), sizeof(ix_group_desc));
-  F(ix_problem, q_start) F(ix_problem, kv_cap) F(ix_problem, k)
+  F(ix_problem, q_start) F(ix_problem, kv_cap) F(ix_problem, k) F(ix_problem, seq_q_start)
   F(ix_indexer_in, q) F(ix_indexer_in, k_scale) F(ix_indexer_in, path)
   F(ix_attn_in, sm_scale) F(ix_attn_in, kv_splits) F(ix_attn_in, q) F(ix_attn_in, lse)
   F(ix_group_desc, f_mask) F(ix_group_desc, ixr) F(ix_group_desc, attn)
@@ -104,6 +104,7 @@ def _call_att(p, d, idx=DUMMY, ws=None, nb=0):
     (dict(k=0), ix.IX_E_SHAPE), (dict(k=4096), ix.IX_E_SHAPE), (dict(batch=0), ix.IX_E_SHAPE),
     (dict(kv_len=7), ix.IX_E_SHAPE), (dict(kv_cap=7), ix.IX_E_SHAPE),
     (dict(q_start=-1), ix.IX_E_SHAPE), (dict(reserved=1), ix.IX_E_SHAPE),
+    (dict(seq_q_start=DUMMY + 4), ix.IX_E_SHAPE),  # per-sequence starts: int64, 8-byte aligned
 ])
 def test_problem_validation(kw, status):
     assert _call_ix(_prob(**kw), _ixr()) == status
@@ -174,7 +175,7 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 2
+    assert ix.ix_abi_version() == 3
 
 
 def test_index_overlap_validation():
@@ -202,3 +203,13 @@ def test_append_keys_validation():
     assert call(kn=DUMMY + 8) == ix.IX_E_SHAPE
     assert call(ks=DUMMY + 2) == ix.IX_E_SHAPE
 
+
+
+def test_append_keys_per_sequence_rows_need_pos_at_the_bound():
+    """With per-sequence starts each sequence's rows move down by its distance
+    below q_start, so pos < q_start (a negative row) is rejected."""
+    lib = ensure_lib()
+    p = _prob(n_q=1, q_start=5, kv_len=8, seq_q_start=DUMMY)
+    call = lambda pos, n=1: lib.ix_append_keys(ctypes.byref(p), 32, DUMMY, n, pos, DUMMY, DUMMY, None)
+    assert call(4) == ix.IX_E_SHAPE
+    assert call(8) == ix.IX_E_SHAPE                  # past kv_cap
