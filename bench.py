@@ -442,6 +442,39 @@ def bench_decode(args, w, torch, synth, ix):
     allf = event_time(torch, lambda: run(args.warmup, mask=0xF), 2)
     key_bytes = w.batch * (w.kv_len + args.warmup) * (w.ix_dim + 4)
     app_ms = event_time(torch, lambda: ix.ix_append_keys(new_keys[0], keys, scale, w.q_start), 20)
+
+    # sequences of different lengths: the same group step with contexts spread
+    # evenly over [context/2, context] (per-sequence starts read on the device)
+    lo = w.q_start // 2
+    starts = torch.linspace(lo, w.q_start, w.batch, device=dev).round().to(torch.int64)
+    ixl0, att0 = steps[args.warmup]
+    varlen_ms = event_time(torch, lambda: ix.ix_group_forward(ixl0, att0, 1, idx, q_start=w.q_start, kv_len=w.kv_len,
+                                                              seq_q_start=starts), 5)
+    varlen = {"contexts": f"{w.batch} sequences, {lo + 1:,}..{w.q_start + 1:,} keys evenly spaced",
+              "ms_fsss": varlen_ms, "tokens_per_s": w.batch / (varlen_ms / 1e3)}
+
+    # MTP draft steps on one layer: the first step selects, the later steps
+    # attend over its positions in the same cache; against every step
+    # selecting anew at its own position
+    n_draft = 5
+    e = ixl0[0]
+    kv0 = kvs[0]
+    dq = [steps[args.warmup + (j % args.steps)][1][0]["q"] for j in range(n_draft)]
+    d_out = torch.empty((w.batch, 1, w.q_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    d_idx = torch.empty((w.batch, 1, w.k), dtype=torch.int32, device=dev)
+
+    def draft(reuse):
+        for j in range(n_draft):
+            if j == 0 or not reuse:
+                ix.ix_indexer_topk(e["q"], e["w"], keys, d_idx, k_scale=scale, q_start=w.q_start + j,
+                                   kv_len=w.kv_len + j)
+            ix.ix_sparse_attn(dq[j], kv0, d_idx, d_out, q_start=w.q_start, kv_len=w.kv_len + n_draft)
+
+    reuse_ms = event_time(torch, lambda: draft(True), 5)
+    reselect_ms = event_time(torch, lambda: draft(False), 5)
+    mtp = {"draft_steps": n_draft, "ms_reuse": reuse_ms, "ms_reselect_every_step": reselect_ms,
+           "speedup": reselect_ms / reuse_ms,
+           "note": "one MTP layer, B sequences: the indexer + top-k once, then attention per step"}
     out = {"metric": "decode tokens/s (B=32, 200K context, one F,S,S,S group per step)",
            "value": w.batch / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -450,6 +483,7 @@ def bench_decode(args, w, torch, synth, ix):
            "step": "quantize+append the new token's indexer key into the fp8 cache, then the F,S,S,S group",
            "append_keys_us": app_ms * 1e3,
            "group": {"ms_fsss": ms, "ms_all_full": allf, "speedup_vs_all_full": allf / ms},
+           "varlen": varlen, "mtp_draft": mtp,
            "indexer_key_GBps_lower_bound": key_bytes / (ms / 1e3) / 1e9}
     print(json.dumps(out))
     return 0
