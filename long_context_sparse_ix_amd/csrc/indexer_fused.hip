@@ -47,7 +47,8 @@ constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 4;
 constexpr int kThreads = kRowsPerWG * kWave;
 constexpr int kRing = 4;        // LDS tile buffers: a pair of tiles being read, the next pair landing
-constexpr int kUnroll = 8;      // candidate entries per lane in flight in buffer passes
+constexpr int kUnroll = 8;      // (score, position) entries per lane in flight in buffer passes
+constexpr int kUnrollS = 16;    // scores per lane in flight in score-only passes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -94,10 +95,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Candidate buffer of one row: float2 entries (score, position bits).
+// Candidate buffer of one row: `cap` scores, then the `cap` positions (two
+// arrays, so passes that need only the scores read contiguous words).  Passes
+// load from indices clamped into the buffer and mask the values afterwards:
+// unconditional loads let one wait cover a whole batch of them.
 struct Cand {
-  float2* e;
-  __device__ __forceinline__ float score(int i) const { return e[i].x; }
+  float* s;
+  int32_t* p;
+  int cap;
+  __device__ __forceinline__ int at(int i) const { return min(i, cap - 1); }
 };
 
 // Bin holding the kk-th largest entry of a 256-bin LDS histogram (lane l owns
@@ -137,15 +143,12 @@ __device__ __forceinline__ int range_bits8(uint32_t range) {   // bit length rou
 __device__ Thresh select_kth(Cand c, int cnt, int k, uint32_t* hist) {
   const int l = lane_id();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int base = 0; base < cnt; base += kWave * kUnroll) {
-    float v[kUnroll];
+  for (int base = 0; base < cnt; base += kWave * kUnrollS) {
+    float v[kUnrollS];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = base + u * kWave + l;
-      v[u] = i < cnt ? c.score(i) : 0.0f;
-    }
+    for (int u = 0; u < kUnrollS; ++u) v[u] = c.s[c.at(base + u * kWave + l)];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kUnrollS; ++u)
       if (base + u * kWave + l < cnt) {
         const uint32_t key = order_key(v[u]);
         lo = min(lo, key);
@@ -158,15 +161,12 @@ __device__ Thresh select_kth(Cand c, int cnt, int k, uint32_t* hist) {
   int kk = k;
   for (int shift = range_bits8(hi - lo) - 8; shift >= 0; shift -= 8) {
     clear_hist(hist);
-    for (int base = 0; base < cnt; base += kWave * kUnroll) {
-      float v[kUnroll];
+    for (int base = 0; base < cnt; base += kWave * kUnrollS) {
+      float v[kUnrollS];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = base + u * kWave + l;
-        v[u] = i < cnt ? c.score(i) : 0.0f;
-      }
+      for (int u = 0; u < kUnrollS; ++u) v[u] = c.s[c.at(base + u * kWave + l)];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollS; ++u) {
         const uint32_t rel = order_key(v[u]) - lo;
         if (base + u * kWave + l < cnt && (rel & pmask) == prefix)
           atomicAdd(&hist[(rel >> shift) & 255u], 1u);
@@ -192,24 +192,30 @@ __device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
   const int l = lane_id();
   int out = 0, eq_seen = 0;
   for (int base = 0; base < cnt; base += kWave * kUnroll) {
-    float2 v[kUnroll];
+    float v[kUnroll];
+    int32_t pos[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int i = base + u * kWave + l;
-      v[u] = i < cnt ? c.e[i] : make_float2(0.0f, 0.0f);
+      const int i = c.at(base + u * kWave + l);
+      v[u] = c.s[i];
+      pos[u] = c.p[i];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const bool in = base + u * kWave + l < cnt;
-      const uint32_t key = order_key(v[u].x);
+      const uint32_t key = order_key(v[u]);
       const bool eq = in && key == t.v;
       const uint64_t em = __ballot(eq);
       const bool keep = (in && key > t.v) || (eq && eq_seen + wave_prefix(em) < t.need);
       const uint64_t km = __ballot(keep);
       if (keep) {
         const int o = out + wave_prefix(km);
-        if constexpr (EMIT) dst[o] = __float_as_int(v[u].y);
-        else c.e[o] = v[u];
+        if constexpr (EMIT) {
+          dst[o] = pos[u];
+        } else {
+          c.s[o] = v[u];
+          c.p[o] = pos[u];
+        }
       }
       out += __popcll(km);
       eq_seen += __popcll(em);
@@ -226,37 +232,23 @@ __device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
 // later key equal to s* loses the position tie, so tau = s* keeps the strict
 // filter exact.  A crowded bin (ties, or a range too wide to split) falls back
 // to the exact select.
-__device__ __forceinline__ void shrink(Cand c, int& cnt, float& tau, float hi_lane, int k, int keep_max, uint32_t* hist) {
+__device__ __forceinline__ void shrink(Cand c, int& cnt, float& tau, float hi_lane, float lo_lane, int k,
+                                       int keep_max, uint32_t* hist) {
   const int l = lane_id();
   wait_vmcnt<0>();                               // this wave's appends are visible
   const float hi = wave_max_f(hi_lane);
-  float lo = tau;
-  if (lo == -INFINITY) {                         // first shrink: entries may be anything
-    float a = INFINITY;
-    for (int base = 0; base < cnt; base += kWave * kUnroll) {
-      float v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = base + u * kWave + l;
-        v[u] = i < cnt ? c.score(i) : INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) a = fminf(a, v[u]);
-    }
-    lo = wave_min_f(a);
-  }
+  // every entry is above tau once a shrink has set it; before that the
+  // buffer holds exactly the appends, whose minimum each lane tracked
+  const float lo = tau == -INFINITY ? wave_min_f(lo_lane) : tau;
   const float inv = 256.0f / (hi - lo);
   if (hi > lo && inv > 0.0f && inv < INFINITY) {
     clear_hist(hist);
-    for (int base = 0; base < cnt; base += kWave * kUnroll) {
-      float v[kUnroll];
+    for (int base = 0; base < cnt; base += kWave * kUnrollS) {
+      float v[kUnrollS];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = base + u * kWave + l;
-        v[u] = i < cnt ? c.score(i) : lo;
-      }
+      for (int u = 0; u < kUnrollS; ++u) v[u] = c.s[c.at(base + u * kWave + l)];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnrollS; ++u)
         if (base + u * kWave + l < cnt) atomicAdd(&hist[min(255, max(0, (int)((v[u] - lo) * inv)))], 1u);
     }
     wave_lds_sync();
@@ -266,19 +258,23 @@ __device__ __forceinline__ void shrink(Cand c, int& cnt, float& tau, float hi_la
       int out = 0;
       float smin = INFINITY;
       for (int base = 0; base < cnt; base += kWave * kUnroll) {
-        float2 v[kUnroll];
+        float v[kUnroll];
+        int32_t pos[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          const int i = base + u * kWave + l;
-          v[u] = i < cnt ? c.e[i] : make_float2(0.0f, 0.0f);
+          const int i = c.at(base + u * kWave + l);
+          v[u] = c.s[i];
+          pos[u] = c.p[i];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          const bool keep = base + u * kWave + l < cnt && min(255, max(0, (int)((v[u].x - lo) * inv))) >= b;
+          const bool keep = base + u * kWave + l < cnt && min(255, max(0, (int)((v[u] - lo) * inv))) >= b;
           const uint64_t km = __ballot(keep);
           if (keep) {
-            c.e[out + wave_prefix(km)] = v[u];
-            smin = fminf(smin, v[u].x);
+            const int o = out + wave_prefix(km);
+            c.s[o] = v[u];
+            c.p[o] = pos[u];
+            smin = fminf(smin, v[u]);
           }
           out += __popcll(km);
         }
@@ -363,6 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   unsigned char* key_lds0 = smem;                                                   // [3][tile]
   float* scale_lds = reinterpret_cast<float*>(smem + kRing * G::tile_bytes);       // [3][64]
   uint32_t* hist = reinterpret_cast<uint32_t*>(scale_lds + kRing * kTileKeys);     // [4][256]
+  int* fill_lds = reinterpret_cast<int*>(hist + kRowsPerWG * 256);                 // [2][4] buffer fills
 
   const int tid = threadIdx.x, wave = uniform(tid >> 6), l = tid & 63;
   const int m = l & 31, hf = l >> 5;
@@ -376,7 +373,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   const int n_keys = qs + last_row + 1;
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
   const int C = a.C;
-  const Cand cand{a.cand + ((int64_t)b * a.n_q + (row_ok ? t : 0)) * C};
+  float* const cand_base = reinterpret_cast<float*>(a.cand) + ((int64_t)b * a.n_q + (row_ok ? t : 0)) * 2 * C;
+  const Cand cand{cand_base, reinterpret_cast<int32_t*>(cand_base + C), C};
   uint32_t* my_hist = hist + wave * 256;
 
   // Query slice (A operand): lane (m, hf) holds head ht*32+m, elements
@@ -438,9 +436,17 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     }
   };
 
-  float tau = -INFINITY, vmax = -INFINITY;
+  float tau = -INFINITY, vmax = -INFINITY, vmin = INFINITY;
   int cnt = 0;
-  const int keep_max = C - 2 * kWave;          // after a shrink the next trigger is >= 64 appends away
+  // Shrinks happen at pair boundaries, together: a pair appends at most 128
+  // entries per row, so a row needs one when it holds more than C - 128; then
+  // every row of the workgroup past `join` shrinks in the same step.  The rows
+  // fill at similar rates, and the barrier makes the others wait for a
+  // shrinking row anyway, so shrinking together turns the workgroup's stalls
+  // from the sum of its rows' shrinks into about their maximum.  A shrink
+  // keeps at most keep_max entries, so the next one is >= 128 appends away.
+  const int keep_max = C - 4 * kWave;
+  const int join = a.k + (C - a.k) / 2;
   float sc_prev = 1.0f;
   float part0 = 0.0f;                           // key-half-0 partial score of the tile being finished
 
@@ -486,24 +492,30 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       const uint64_t pm = __ballot(pass);
       if (pm) {
         if (pass) {
-          cand.e[cnt + wave_prefix(pm)] = make_float2(score, __int_as_float(s));
+          const int o = cnt + wave_prefix(pm);
+          cand.s[o] = score;
+          cand.p[o] = s;
           vmax = fmaxf(vmax, score);              // per lane; reduced when a shrink needs it
+          vmin = fminf(vmin, score);
         }
         cnt += __popcll(pm);
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
     if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, bfr, acc1, acc0);
-    // keep room for the next tile's up to 64 appends (here, where no B
-    // fragments are live)
-    if (cnt > C - kWave) shrink(cand, cnt, tau, vmax, a.k, keep_max, my_hist);
     sc_prev = sc_cur;
   };
-  for (int it = 0; it <= n_tiles; it += 2) {
+  for (int it = 0, parity = 0; it <= n_tiles; it += 2, parity ^= 1) {
     step(it, true);
     if (it + 1 <= n_tiles) step(it + 1, false);
+    // post this row's fill; the slots alternate by pair so that a wave
+    // already in the next pair cannot overwrite a fill still being read
+    if (l == 0) fill_lds[parity * kRowsPerWG + wave] = cnt;
     wait_vmcnt<0>();                             // the next pair landed
     lds_barrier();
+    const int4 f = *reinterpret_cast<const int4*>(fill_lds + parity * kRowsPerWG);
+    const int fullest = max(max(f.x, f.y), max(f.z, f.w));
+    if (fullest > C - 2 * kWave && cnt > join) shrink(cand, cnt, tau, vmax, vmin, a.k, keep_max, my_hist);
   }
 
   if (row_ok) {
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       keep_pass<true>(cand, cnt, th, dst);
       written = a.k;
     } else {
-      for (int i = l; i < cnt; i += kWave) dst[i] = __float_as_int(cand.e[i].y);
+      for (int i = l; i < cnt; i += kWave) dst[i] = cand.p[i];
       written = cnt;
     }
     for (int i = written + l; i < a.k; i += kWave) dst[i] = -1;
@@ -580,7 +592,7 @@ int fused_candidates(int k) {
 
 size_t fused_lds_bytes(int d) {
   return (size_t)kRing * kTileKeys * 2 * d + kRing * kTileKeys * sizeof(float) +
-         kRowsPerWG * 256 * sizeof(uint32_t);
+         kRowsPerWG * 256 * sizeof(uint32_t) + 2 * kRowsPerWG * sizeof(int);
 }
 
 bool fused_dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }

@@ -14,7 +14,7 @@ struct FusedArgs {
   const uint16_t* keys;   // bf16 rows, row stride d, sequence stride key_bstride
   const float* scale;     // per-key fp32 scale, or nullptr
   int32_t* idx;           // [B][n_q][k]
-  float2* cand;           // workspace: [B][n_q][C] (score, position bits) candidate buffers
+  float2* cand;           // workspace: per row C fp32 scores then C int32 positions (C float2 of room)
   int64_t key_bstride;    // elements
   int64_t scale_bstride;  // elements
   int64_t q_start;        // row 0's position (with seq_q_start: the largest start)
