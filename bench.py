@@ -7,6 +7,10 @@ default (headline) workload that is L = 131072 query rows through 8 layers
 arranged as two full+shared+shared+shared groups -- the indexer + streaming
 top-k on the 2 full layers and sparse attention on all 8.  Inputs are
 generated on the device before timing starts.  Prints one JSON line.
+
+    python bench.py --op indexer|attention [--steps K] [--warmup W]
+
+times one op of the workload's first layer alone (for profilers).
 """
 from __future__ import annotations
 
@@ -237,6 +241,8 @@ def main(argv=None):
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the attention traffic summary from two rocprofv3 --pmc output dirs")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
+    ap.add_argument("--op", choices=["indexer", "attention"],
+                    help="time one op of the workload's first layer alone (warmup + steps launches), for profiling")
     args = ap.parse_args(argv)
     if args.write_traffic:
         write_traffic(*args.write_traffic, args.traffic_command)
@@ -260,6 +266,8 @@ def main(argv=None):
     ix.load()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[CONFIGS[args.config]]
+    if args.op:
+        return bench_op(args, w, torch, synth, ix)
     if w.decode_steps:
         return bench_decode(args, w, torch, synth, ix)
 
@@ -393,6 +401,31 @@ def main(argv=None):
         for _ in range(4):
             dst.copy_(src)
         torch.cuda.synchronize()
+    return 0
+
+
+def bench_op(args, w, torch, synth, ix):
+    """One op of the first layer, launched warmup + steps times: the indexer
+    (+ fused top-k) or the sparse attention over that indexer's positions."""
+    dev = "cuda"
+    q, wt = synth.indexer_queries(w, dev, 0)
+    keys, scale = synth.indexer_keys(w, dev, 0)
+    idx = torch.empty((w.batch, w.n_q, w.k), dtype=torch.int32, device=dev)
+    run_ix = lambda: ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len)
+    fn = run_ix
+    if args.op == "attention":
+        run_ix()
+        del q, wt, keys, scale
+        aq = synth.attn_queries(w, dev, 0)
+        kv = synth.latent_kv(w, dev, 0)
+        out = torch.empty((w.batch, w.n_q, w.q_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+        fn = lambda: ix.ix_sparse_attn(aq, kv, idx, out, q_start=w.q_start, kv_len=w.kv_len)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
+    print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
+                      "ms_per_launch": ms}), flush=True)
     return 0
 
 
