@@ -105,9 +105,10 @@ typedef struct ix_problem {
 
 /* Inputs of one full layer's indexer.
  * score(t, s) = sum_h w[t,h] * max(0, q[t,h,:] . key[s,:]), where key[s,:] is
- * the bf16 row, or the e4m3fn codes of row s times k_scale[s].  The pages name
- * the indexer only as "few heads, low-rank, FP8" (IndexCache notes, section
- * 1); this weighted-ReLU form is the library's stated reading. */
+ * the bf16 row, or the e4m3fn codes of row s times k_scale[s].  The pages
+ * describe the indexer only as a small low-rank FP8 module with few heads
+ * (IndexCache notes, section 1); this weighted-ReLU form is the library's
+ * stated reading. */
 typedef struct ix_indexer_in {
   int32_t heads;    /* H, 1..64                                                */
   int32_t dim;      /* d, a multiple of 16 in 16..128                          */

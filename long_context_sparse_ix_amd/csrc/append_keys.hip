@@ -1,7 +1,7 @@
 // New indexer keys into the fp8 key cache.
 //
-// The indexer keys are stored in FP8 (IndexCache notes, section 1: "few
-// heads, low-rank, FP8").  Per-row scaling (the library's reading; the pages
+// The indexer keys are stored in FP8 (IndexCache notes, section 1, which
+// describes the indexer as a small, low-rank, FP8 module).  Per-row scaling (the library's reading; the pages
 // give none): scale = max_j |k_j| / 448, or 1 for an all-zero row, and
 // code_j = e4m3fn(k_j / scale), rounded to nearest with ties to the even code
 // and saturating at +-448; both divisions are correctly rounded fp32.  One

@@ -1,8 +1,8 @@
 // Per-row top-k over materialised fp32 score rows.
 //
 // Selection rule ("IndexShare", LLM Architecture Gallery, section "How
-// IndexShare Works": the full layer performs the top-k operation and stores the
-// selected positions): keep the min(k, p+1) best positions of row p under
+// IndexShare Works": a full layer runs the top-k itself and keeps the chosen
+// positions for the shared layers): keep the min(k, p+1) best positions of row p under
 // (score desc, position asc); emit them in ascending position order, then -1.
 //
 // Few long rows (decode: 32 rows of ~200K scores) cannot fill the chip with one

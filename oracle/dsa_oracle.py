@@ -22,8 +22,8 @@ with plain NumPy, following the definitions on the pages:
 
 Readings taken where the pages are silent (each also listed in the design doc):
 * indexer score: score(t, s) = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :]),
-  one key vector per token shared by all indexer heads (the pages only say
-  "few heads, low-rank, FP8");
+  one key vector per token shared by all indexer heads (the pages describe
+  the indexer only as a small, low-rank module with few heads, in FP8);
 * a query at absolute position p may select any s with 0 <= s <= p (itself
   included), and s < kv_len;
 * order: larger score first, equal scores -> lower position first; the row is
