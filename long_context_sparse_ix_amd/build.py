@@ -26,6 +26,10 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMAs accumulate in VGPRs; the default AGPR form made the attention
+          # kernel copy its 128-register output accumulator between the two
+          # register files on every 16-slot step
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 

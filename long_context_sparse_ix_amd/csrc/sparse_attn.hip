@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kWavesPerWG = 4;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kSlack = 8.0f;   // how far the softmax reference may trail the max (log2 units)
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
@@ -65,7 +66,7 @@ struct AttnLds {
 
 template <int KS, int MT, int WPI>
 __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(AttnArgs a) {
-  constexpr int D = 32 * KS, QD = 8 * KS, Dv = 16 * MT;
+  constexpr int D = 32 * KS, Dv = 16 * MT;
   using V = VTile<MT>;
   static_assert(WPI == 1 || WPI == kWavesPerWG, "a (row, split) has one wave or the whole workgroup");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -77,14 +78,19 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   const int b = r / a.n_q;
   uint16_t* vl = reinterpret_cast<uint16_t*>(smem + wave * V::bytes);
 
-  // Query slice as the B operand: head n16, elements [g*QD + 8ks, +8).
+  // Query slice as the B operand: head n16, elements [32ks + 8g, +8) -- the
+  // MFMA's k-group g of step ks.  The gathered latent rows use the same
+  // split, so in every gather instruction the four lanes of a row read 64
+  // contiguous bytes: 16 cache lines per instruction instead of 64 (a split
+  // into one contiguous run per lane spreads each instruction over 4 lines per
+  // row, and the vector L1's line rate, not memory, then bounds the kernel).
   const bool hq_ok = n16 < a.Hq;
   bf16x8 qf[KS];
   {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + g * QD;
+    const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * ks) : bf16x8{};
+      qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks) : bf16x8{};
   }
 
   int j0 = sp * a.slots_per_split;
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     j1 = min(j1, j0 + per);
   }
   const int32_t* irow = a.idx + (int64_t)r * a.k;
-  const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride + g * QD;
+  const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride + 8 * g;
 
   f32x4 oacc[MT];
 #pragma unroll
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     const bool valid = rid >= 0 && (int64_t)rid < a.kv_len;
     const uint16_t* src = kvb + (int64_t)(valid ? rid : 0) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
     return valid;
   };
 
@@ -130,9 +136,9 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     for (int ks = 0; ks < KS; ++ks)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
     // park the value part of row n16 for the transposed read
+    static_assert(Dv % 32 == 0, "the value part is whole k-steps");
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      if (g * QD + 8 * ks < Dv) *reinterpret_cast<bf16x8*>(vl + n16 * V::stride + g * QD + 8 * ks) = kf[ks];
+    for (int ks = 0; ks < Dv / 32; ++ks) *reinterpret_cast<bf16x8*>(vl + n16 * V::stride + 32 * ks + 8 * g) = kf[ks];
 
     float z[4];
     float cmax = -INFINITY;
@@ -143,9 +149,15 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     }
     cmax = wave_max_xor(cmax, 16);
     cmax = wave_max_xor(cmax, 32);
-    const float m_new = fmaxf(m_run, cmax);
-    if (__ballot(m_new > m_run)) {
-      const float alpha = m_new > m_run ? exp2f(m_run - m_new) : 1.0f;
+    // The reference m_run may trail the running max by up to kSlack (log2
+    // units): every p = 2^(z - m_run) then stays below 2^kSlack, far inside
+    // the fp32 and bf16 ranges, and the normalised softmax does not depend on
+    // the reference.  The accumulators are rescaled only when a head's max
+    // jumps further, which after the first step is rare.
+    const bool jump = cmax > m_run + kSlack;     // always true on a head's first valid step
+    if (__builtin_expect(__ballot(jump) != 0, 0)) {
+      const float m_new = jump ? cmax : m_run;
+      const float alpha = jump ? exp2f(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
@@ -168,18 +180,20 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     // transposed read: lane (n16, g) supplies 4 value dims of key 4g + n16/4
     // and receives value dim 16mt + n16 of keys 4g .. 4g+3
     const uint16_t* vrow = vl + (4 * g + (n16 >> 2)) * V::stride + 4 * (n16 & 3);
+    v4s_t vt[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const v4s_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
-      const i16x4 av = __builtin_bit_cast(i16x4, t);
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, oacc[mt], 0, 0, 0);
-    }
+    for (int mt = 0; mt < MT; ++mt) vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[mt]), pb, oacc[mt], 0, 0, 0);
     wave_lds_sync();
   };
 
   // Two named buffers in turn (unrolled by 2): the step on one runs while the
   // other's gathers are in flight.  A loop-carried copy of the buffer would
-  // make the compiler wait for those gathers at every step.
+  // make the compiler wait for those gathers at every step.  (A third buffer,
+  // two steps of lookahead, measured no faster: the gathers are bound by the
+  // rate at which the CUs take in scattered 64-byte pieces, not by latency.)
   bf16x8 kA[KS], kB[KS];
   bool vA = fetch(slot_row(j0), kA), vB = false;
   int rid_after = slot_row(j0 + 16);             // -1 past the range
