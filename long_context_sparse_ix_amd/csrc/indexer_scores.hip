@@ -23,11 +23,14 @@ constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 20 tiles of 64 keys p
 constexpr int kWavesPerWG = 4;
 
 template <int HT, int KS, bool FP8>
-__global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scores_kernel(ScoreArgs a) {
   constexpr int d = KS * 16;
-  // tiles per wave held in registers (one in use, the rest in flight): fp8
-  // tiles are half the bytes of bf16 ones
-  constexpr int kDepth = FP8 ? 5 : 3;
+  // tiles per wave held in registers (one in use, the rest in flight).  fp8
+  // keys: one tile ahead, which leaves room for two waves per SIMD (one
+  // computes while the other waits on its keys; measured faster than one
+  // wave with four tiles ahead); bf16 tiles are twice the bytes, so one wave
+  // per SIMD with two tiles ahead.
+  constexpr int kDepth = FP8 ? 2 : 3;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int m = l & 31, hf = l >> 5;
   const int row = blockIdx.y;                 // b * n_q + t
@@ -59,29 +62,26 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
     }
     if constexpr (FP8) scl = scale_b[min<int64_t>(s0 + l, p)];
   };
-  auto widen = [&](const piece_t (&rw)[2][RAW], bf16x8 (&bfr)[2][KS]) {
+  auto widen = [&](const piece_t (&rw)[RAW], bf16x8 (&bfr)[KS]) {
+    if constexpr (FP8 && KS % 2 == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if constexpr (FP8 && KS % 2 == 0) {
-#pragma unroll
-        for (int c = 0; c < KS / 2; ++c) {
-          const u32x4 v = rw[nt][c];
-          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-          const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
-          bfr[nt][2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
-          bfr[nt][2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
-        }
-      } else if constexpr (FP8) {
-#pragma unroll
-        for (int c = 0; c < KS; ++c) {
-          const u32x2 v = rw[nt][c];
-          const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
-          bfr[nt][c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bfr[nt][ks] = __builtin_bit_cast(bf16x8, rw[nt][ks]);
+      for (int c = 0; c < KS / 2; ++c) {
+        const u32x4 v = rw[c];
+        const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+        const u32x2 r2 = e4m3x4_to_bf16x4(v.z), r3 = e4m3x4_to_bf16x4(v.w);
+        bfr[2 * c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+        bfr[2 * c + 1] = __builtin_bit_cast(bf16x8, u32x4{r2.x, r2.y, r3.x, r3.y});
       }
+    } else if constexpr (FP8) {
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const u32x2 v = rw[c];
+        const u32x2 r0 = e4m3x4_to_bf16x4(v.x), r1 = e4m3x4_to_bf16x4(v.y);
+        bfr[c] = __builtin_bit_cast(bf16x8, u32x4{r0.x, r0.y, r1.x, r1.y});
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bfr[ks] = __builtin_bit_cast(bf16x8, rw[ks]);
     }
   };
 
@@ -119,25 +119,26 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void indexer_scores_kernel(
         const int jn = j + kDepth - 1;
         load_raw(s_begin + (int64_t)jn * kTileKeys, raw[(u + kDepth - 1) % kDepth], sc[(u + kDepth - 1) % kDepth]);
         const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
-        bf16x8 bfr[2][KS];
-        widen(raw[u], bfr);
-        f32x16 acc[2][HT];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-              acc[nt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[nt][ks],
-                                                                    ks == 0 ? f32x16{} : acc[nt][ht], 0, 0, 0);
+        // the two 32-key halves one after the other: only one half's B
+        // fragments and accumulators are live, which leaves room for two
+        // waves per SIMD (one computes while the other waits on its keys)
         float part[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
+          bf16x8 bfr[KS];
+          widen(raw[u][nt], bfr);
+          f32x16 acc[HT];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+              acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[ks], ks == 0 ? f32x16{} : acc[ht],
+                                                                0, 0, 0);
           float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], relu(acc[nt][ht][r]), sacc[r & 3]);
+            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], relu(acc[ht][r]), sacc[r & 3]);
           part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
