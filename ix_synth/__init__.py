@@ -73,7 +73,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads the method is measured on (shapes from the benchmark spec;
+# The five workloads the method is measured on (the benchmark configurations;
 # k=2048 and the 1M context follow the pages).
 TINY_L1K = Workload("tiny_l1k_exact", 1, 1024, 0, 1024, 64, "FSSS", 4, 32, "bf16",
                     8, 128, 96, mode="exact")

@@ -20,7 +20,7 @@ with plain NumPy, following the definitions on the pages:
   F layers compute fresh top-k, S layers reuse the nearest preceding F layer's
   result, and the first layer is always F.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 * indexer score: score(t, s) = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :]),
   one key vector per token shared by all indexer heads (the pages describe
   the indexer only as a small, low-rank module with few heads, in FP8);
