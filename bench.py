@@ -426,6 +426,12 @@ def bench_op(args, w, torch, synth, ix):
     ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
     print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
                       "ms_per_launch": ms}), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     return 0
 
 
