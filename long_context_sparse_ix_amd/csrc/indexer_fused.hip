@@ -16,9 +16,9 @@
 //     waits overlap the other's MFMAs); row blocks are issued longest-first so
 //     the causal triangle drains evenly;
 //   * keys stream HBM -> LDS with direct loads (global_load_lds_dwordx4, no
-//     VGPR staging) into a 3-deep ring of 64-key bf16 tiles shared by the 4
-//     rows, rows XOR-swizzled so B-operand reads are bank-conflict free; one
-//     barrier per tile;
+//     VGPR staging) into a 4-slot ring of 64-key bf16 tiles shared by the 4
+//     rows, rows XOR-swizzled so B-operand reads are bank-conflict free; tiles
+//     are consumed in pairs, one LDS-only barrier per pair;
 //   * each wave keeps its row's heads x d query slice in registers as the MFMA
 //     A operand (M = heads) and reads 32-key halves of a tile as the B operand
 //     (N = keys): v_mfma_f32_32x32x16_bf16, output lane l holds key l%32 and 16
@@ -28,8 +28,9 @@
 //     leaves lane l with the score of key tile_start + l;
 //   * streaming top-k per row: a strict "score > tau" filter appends survivors
 //     to the row's candidate buffer in the workspace (L2-resident, ascending
-//     position order).  When it nears capacity, one histogram pass over the
-//     score range picks the bin holding the k-th best and everything below
+//     position order).  At pair boundaries, when any row of the workgroup
+//     nears capacity, the fuller rows shrink together: one histogram pass over
+//     the score range picks the bin holding the k-th best and everything below
 //     that bin is dropped; tau becomes the smallest kept score.  Because keys
 //     arrive in ascending position, a later key tying tau always loses the
 //     tie, so the strict filter is exact.  A crowded bin (ties) falls back to

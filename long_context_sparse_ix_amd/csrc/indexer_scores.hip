@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
 
   // Loads are unconditional (keys past p are clamped to p, their scores are
   // masked): exec-masked load branches make the compiler's memory-counter
-  // waits drain every load in flight, tiles three steps ahead included.
+  // waits drain every load in flight, the prefetched tiles included.
 #pragma unroll
   for (int j = 0; j < kDepth - 1; ++j) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
 
