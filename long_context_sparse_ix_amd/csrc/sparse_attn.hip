@@ -12,9 +12,10 @@
 // Layout of the work
 //   * one wave = one (query row, slot range); all Hq <= 16 heads of the row
 //     share every gathered latent row, so each gathered byte feeds 16 heads;
-//   * 16 slots per step: lane (key n16 = l%16, quarter g = l/16) loads its
-//     quarter of latent row idx[n16] straight from HBM into the MFMA A operand
-//     (16 B per load, prefetched one step ahead, index words two steps ahead);
+//   * 16 slots per step: lane (key n16 = l%16, group g = l/16) loads 16-byte
+//     pieces 4ks + g of latent row idx[n16] straight from HBM into the MFMA A
+//     operand (k-group g of step ks; 64 contiguous bytes per row and load),
+//     prefetched one step ahead, index words two steps ahead;
 //   * S^T = KV . Q^T with v_mfma_f32_16x16x32_bf16 (M = keys, N = heads, the
 //     query slice stays in VGPRs), so lane l ends with 4 logits of head l%16
 //     -- exactly the B-operand layout of the P.V product below;
@@ -22,8 +23,9 @@
 //     read back transposed by ds_read_b64_tr_b16 (lane (dv, key group) gets 4
 //     keys of one value dim) as the A operand of O^T = V^T . P^T
 //     (v_mfma_f32_16x16x16_bf16);
-//   * online softmax in base 2, rescaling the accumulators only when some
-//     head's running max grows;
+//   * online softmax in base 2 against a reference max that may trail the
+//     running max by up to 2^8, so the accumulators are rescaled only when a
+//     head's max jumps further (rarely);
 //   * few rows (decode): the four waves of a workgroup share one (row, split),
 //     each taking a quarter of its slots, and merge their (o, m, l) through
 //     LDS; with several splits per row the merged partials go to the
