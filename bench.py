@@ -142,7 +142,9 @@ def write_traffic(fetch_dir, write_dir, command):
            "calibration": {"copy_bytes": CAL_BYTES, "fetch_kib": fc, "write_kib": wc,
                            "fetch_factor": f_fac, "write_factor": w_fac},
            "hbm_bytes_per_launch": fa * 1024 * f_fac + wa * 1024 * w_fac,
-           "source_sha256": source_sha(ATTN_SOURCE), "command": command}
+           "source_sha256": source_sha(ATTN_SOURCE),
+           "source_sha256_of": "sparse_attn.hip with comments and blank space removed (the code the counters were taken on)",
+           "command": command}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
