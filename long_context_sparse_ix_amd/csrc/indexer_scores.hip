@@ -19,7 +19,7 @@ namespace ix {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 20 tiles of 64 keys per wave
+constexpr int kTilesPerWave = kScoreSpan / kTileKeys;   // 10 tiles of 64 keys per wave
 constexpr int kWavesPerWG = 4;
 
 template <int HT, int KS, bool FP8>

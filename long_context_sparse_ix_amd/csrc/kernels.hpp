@@ -54,7 +54,7 @@ struct ScoreArgs {
                           // [rows][rng_stride], one entry per kScoreSpan keys
   int rng_stride;
 };
-constexpr int kScoreSpan = 1280;   // keys per wave of the score kernel (20 tiles of 64)
+constexpr int kScoreSpan = 640;    // keys per wave of the score kernel (10 tiles of 64)
 hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
                                  hipStream_t s);
 
