@@ -8,11 +8,16 @@
 // row is split over many waves instead and each wave streams its own keys
 // straight from HBM into MFMA B operands (no LDS).  fp8 e4m3fn keys are
 // widened to bf16 in registers (exact) and the per-key scale is applied to the
-// finished score.  The rows are then reduced by the per-row top-k kernel.
+// finished score.  The rows are then reduced by the per-row top-k: for rows of
+// at most 512 waves' spans, each wave first keeps the best of its own 640
+// scores for the row's candidate list (the top-k's wave-local stage, run here
+// as the epilogue on the scores just written), so the top-k itself is one
+// merge pass.
 #include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "topk_local.hpp"
 
 namespace ix {
 
@@ -111,7 +116,12 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   for (int j = 0; j < kDepth - 1; ++j) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
 
   float smin = INFINITY, smax = -INFINITY;     // range of this wave's scores
-  for (int j0 = 0; j0 < n_tiles; j0 += kDepth) {   // a partial last group computes masked tiles
+  float kept[kTilesPerWave] = {};               // this lane's score of every tile (top-k stage)
+  // fully unrolled, so `kept` stays in registers; a partial last group
+  // computes masked tiles
+#pragma unroll
+  for (int j0 = 0; j0 < kTilesPerWave; j0 += kDepth) {
+    if (j0 >= n_tiles) break;
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int j = j0 + u;
@@ -145,6 +155,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
                                                          __float_as_uint(part[1]), false, false);
         float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const int64_t s = s0 + l;
+        if (j < kTilesPerWave) kept[j < kTilesPerWave ? j : 0] = FP8 ? score * sc[u] : score;
         if (s <= p) {
           if constexpr (FP8) score *= sc[u];
           out[s] = score;
@@ -154,7 +165,23 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
       }
     }
   }
-  if (a.rng) {
+  if (a.local) {
+    // wave-local top-k stage over this wave's scores (entries past p, and
+    // tiles past the last, are masked)
+    const int piece = blockIdx.x * kWavesPerWG + wave;
+    const int P = (int)((p + kScoreSpan) / kScoreSpan);       // waves that score this row
+    uint64_t valid[kTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave; ++j) {
+      const int64_t c = p + 1 - (s_begin + (int64_t)j * kTileKeys);
+      valid[j] = c >= kWave ? ~0ull : (c <= 0 ? 0ull : (1ull << c) - 1ull);
+    }
+    const int cap = kLocalCap / P;
+    __shared__ uint32_t hist[kWavesPerWG][kLocalBins];
+    const uint4 r = wave_keep_top<kTilesPerWave>(kept, valid, (int)s_begin, cap, hist[wave],
+                                                 a.cand + (int64_t)row * kLocalCap + (int64_t)piece * cap);
+    if (l == 0) a.local[(int64_t)row * a.rng_stride + piece] = r;
+  } else if (a.rng) {
 #pragma unroll
     for (int dd = 32; dd >= 1; dd >>= 1) {
       smin = fminf(smin, __shfl_xor(smin, dd));

@@ -90,10 +90,11 @@ size_t score_bytes(const ix_problem* p) {
 size_t topk_ws(const ix_problem* p) {
   return round_up(ix::topk_rows_ws_bytes(p->batch * p->n_q, p->q_start + p->n_q, p->k));
 }
-// per-wave score ranges written by the score kernel for the row select
+// per-wave records of the score kernel for the row select: a (min, max) score
+// range, or the wave-local top-k stage's 16-byte record
 int rng_stride(const ix_problem* p) { return (int)((p->q_start + p->n_q + ix::kScoreSpan - 1) / ix::kScoreSpan); }
 size_t rng_bytes(const ix_problem* p) {
-  return round_up((size_t)p->batch * p->n_q * rng_stride(p) * 8);
+  return round_up((size_t)p->batch * p->n_q * rng_stride(p) * 16);
 }
 
 size_t stage_key_bytes(const ix_problem* p, const ix_indexer_in* in) {
@@ -191,13 +192,21 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
   a.seq_q_start = p->seq_q_start;
   a.n_q = p->n_q;
   a.H = in->heads;
-  a.rng = reinterpret_cast<float2*>(static_cast<char*>(ws) + score_bytes(p));
+  // per-wave records after the scores: (min, max) ranges for the chunked
+  // row select, or the wave-local top-k stage's records when it applies
+  const int rows = p->batch * p->n_q;
+  const int64_t max_n = p->q_start + p->n_q;
+  void* per_wave = static_cast<char*>(ws) + score_bytes(p);
+  void* tws = static_cast<char*>(ws) + score_bytes(p) + rng_bytes(p);
+  const bool local = ix::topk_rows_local_fits(rows, max_n, p->k, ix::kScoreSpan);
+  a.rng = local ? nullptr : static_cast<float2*>(per_wave);
+  a.local = local ? static_cast<uint4*>(per_wave) : nullptr;
+  a.cand = local ? ix::topk_rows_cand(tws, rows, max_n) : nullptr;
   a.rng_stride = rng_stride(p);
   hipError_t e = ix::launch_indexer_scores(a, p->batch, in->dim, fp8, p->kv_len, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = ix::launch_topk_rows(a.scores, a.ld, idx, p->batch * p->n_q, p->n_q, p->q_start, p->seq_q_start, p->k,
-                           static_cast<char*>(ws) + score_bytes(p) + rng_bytes(p), s, a.rng, ix::kScoreSpan,
-                           a.rng_stride);
+  e = ix::launch_topk_rows(a.scores, a.ld, idx, rows, p->n_q, p->q_start, p->seq_q_start, p->k, tws, s, a.rng,
+                           ix::kScoreSpan, a.rng_stride, a.local, ix::kScoreSpan, a.rng_stride);
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 

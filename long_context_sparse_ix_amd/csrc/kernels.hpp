@@ -52,24 +52,37 @@ struct ScoreArgs {
   int n_q, H;
   float2* rng;            // nullable: per-wave (min, max) of the written scores,
                           // [rows][rng_stride], one entry per kScoreSpan keys
+  uint4* local;           // nullable (then rng is unused): the wave-local top-k stage runs
+                          // as the epilogue, records [rows][rng_stride], kept entries
+                          // into cand [rows][8192] (the row top-k's candidate list)
+  uint2* cand;
   int rng_stride;
 };
 constexpr int kScoreSpan = 640;    // keys per wave of the score kernel (10 tiles of 64)
 hipError_t launch_indexer_scores(const ScoreArgs& a, int B, int d, bool fp8, int64_t kv_len,
                                  hipStream_t s);
 
-// Per-row top-k over materialised fp32 score rows.  Few rows use a chunked
-// multi-workgroup select whose state lives in a workspace of
-// topk_rows_ws_bytes(rows, q_start + n_q, k) bytes (0: none needed).
-// `rng` (nullable) holds per-row (min, max) partials over consecutive spans of
+// Per-row top-k over materialised fp32 score rows.  Few rows use
+// multi-workgroup selects whose state lives in a workspace of
+// topk_rows_ws_bytes(rows, q_start + n_q, k) bytes (0: none needed): a
+// wave-local keep stage over pieces of the row plus a per-row merge when a row
+// has at most 512 pieces, else five chunked passes.  `rng` (nullable, five-pass
+// select only) holds per-row (min, max) partials over consecutive spans of
 // rng_span scores, rng_stride entries per row; without it the select measures
-// the ranges itself.
+// the ranges itself.  `pre_local` (nullable) says the wave-local stage already
+// ran over pieces of pre_span positions (the score kernel's epilogue): its
+// per-piece records are [rows][pre_stride] and its kept entries are in the
+// workspace's candidate list (topk_rows_cand), so only the merge runs.
 size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k);
+// true when the wave-local stage applies to pieces of `span` positions
+bool topk_rows_local_fits(int rows, int64_t max_n, int k, int span);
+uint2* topk_rows_cand(void* ws, int rows, int64_t max_n);
 // Row r = b * n_q + t holds the candidates 0 .. start_b + t, start_b the
 // per-sequence start seq_q_start[b] (clamped into [0, q_start]) or q_start.
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
                             int64_t q_start, const int64_t* seq_q_start, int k, void* ws, hipStream_t s,
-                            const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0);
+                            const float2* rng = nullptr, int rng_span = 0, int rng_stride = 0,
+                            const uint4* pre_local = nullptr, int pre_span = 0, int pre_stride = 0);
 
 // New fp32 key rows [B][n_new][dim] -> e4m3fn codes and fp32 scales at cache
 // rows [pos_b, pos_b + n_new) of sequence b (dim a multiple of 16, <= 128):

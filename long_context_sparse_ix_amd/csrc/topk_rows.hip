@@ -7,7 +7,25 @@
 //
 // Few long rows (decode: 32 rows of ~200K scores) cannot fill the chip with one
 // workgroup per row, so a row is cut into 8192-score chunks, each with its own
-// workgroup, and the select runs as five short passes:
+// workgroup.  Rows of up to 128 chunks (about 1M scores) take two passes:
+//   L  local:  a chunk of a row with G chunks keeps at most cap = 8192 / G
+//              entries: a 1024-bin value histogram over the chunk's [min, max]
+//              gives the bin holding its (cap+1)-th best, and every entry in a
+//              higher bin is kept, in position order, at slots [g*cap, ...) of
+//              the row's candidate list.  The chunk records how many it kept
+//              and the largest order key it dropped;
+//   M  merge:  per row, the kept entries of all chunks (at most 8192, in
+//              position order) go to LDS and an exact radix select finds the
+//              k-th best v among them.  If v is above every dropped key, no
+//              dropped entry can rank among the k best, so the row's top k is
+//              the top k of the kept entries and a stable pass emits it.
+//              Otherwise (fewer than k kept, or a chunk dropped an entry at or
+//              above v: a ramp that puts the winners in one chunk, a flat row)
+//              the row is finished by a single-workgroup exact select over the
+//              whole row.
+// Random rows keep about 4x what each chunk contributes to the top k (k <=
+// 2048 of 8192 G slots), so the fallback is rare.  Longer rows run five
+// passes:
 //   R  range:   min / max of every chunk;
 //   H  hist:    a 1024-bin value-domain histogram of every chunk over the
 //               row's [min, max] (bins are monotone in the score);
@@ -25,6 +43,7 @@
 // workgroup per row already fills the chip and needs no workspace.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "topk_local.hpp"
 
 namespace ix {
 
@@ -36,7 +55,7 @@ constexpr int kChunk = kCT * kPT;        // 8192 scores per chunk
 constexpr int kVB = 1024;                // value bins of a chunk histogram
 constexpr int kST = 256;                 // threads of the select pass (4 bins each)
 constexpr int kFT = 1024;                // threads of the finish / single-row select
-constexpr int kCap = 8192;               // candidate capacity per row
+constexpr int kCap = kLocalCap;          // candidate capacity per row
 constexpr int kMultiRowLimit = 1024;     // rows below this use the chunked select
 
 constexpr int kSingleBins = 2048;        // value bins of the single-workgroup select
@@ -167,6 +186,37 @@ __device__ uint32_t radix_kth(int n, int kk, uint32_t kmin, uint32_t kmax, KeyF 
   return kmin + prefix;
 }
 
+// The kk-th largest order key among entries i in [0, n) with pred(i), whose
+// keys lie in [kmin, kmax]: a kSingleBins value histogram over that range
+// gives the bin holding it (the bins spread a tail of scores thinly, where the
+// top 8 bits of the keys would pile most of them into a few bins and
+// serialise the LDS atomics), then the exact radix select runs over that
+// bin's entries only.  hist holds >= kSingleBins words of LDS.
+template <int NT, typename KeyF, typename PredF>
+__device__ uint32_t select_binned(int n, int kk, uint32_t kmin, uint32_t kmax, KeyF key, PredF pred,
+                                  uint32_t* hist, uint32_t* redu, int* sel_bin, int* sel_above, int* need) {
+  const float lo = key_value(kmin);
+  const float inv = bin_scale(lo, key_value(kmax), kSingleBins);
+  for (int i = threadIdx.x; i < kSingleBins; i += NT) hist[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += NT)
+    if (pred(i)) atomicAdd(&hist[vbin(key_value(key(i)), lo, inv, kSingleBins)], 1u);
+  __syncthreads();
+  pick_from_top(hist, kSingleBins, kk, sel_bin, sel_above);
+  const int vb = *sel_bin;
+  const int kb = kk - *sel_above;
+  const auto in_vb = [&](int i) { return pred(i) && vbin(key_value(key(i)), lo, inv, kSingleBins) == vb; };
+  uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+  for (int i = threadIdx.x; i < n; i += NT)
+    if (in_vb(i)) {
+      bmin = min(bmin, key(i));
+      bmax = max(bmax, key(i));
+    }
+  bmin = block_reduce<NT>(bmin, redu, UMinOp{});
+  bmax = block_reduce<NT>(bmax, redu, UMaxOp{});
+  return radix_kth<NT>(n, kb, bmin, bmax, key, in_vb, hist, sel_bin, sel_above, need);
+}
+
 // ---- single-workgroup select of one whole row (kFT threads) ----
 //   1. min / max of the row;  2. a 2048-bin value histogram gives the bin
 //   holding the k-th best;  3. exact radix select on the order keys of that
@@ -273,6 +323,9 @@ struct ChunkArgs {
   const float2* rng;  // range partials: [rows][rng_stride], one per rng_span scores
   int rng_span, rng_stride;
   float2* rng_own;    // [rows][G], written by the range pass when no partials are given
+  uint4* local;       // [rows][local_stride] per piece: kept count, largest dropped order key,
+                      // smallest and largest kept order key
+  int local_stride, local_span;   // pieces of local_span positions
   uint32_t* hist;  // [rows][G][kVB]
   int32_t* off;    // [rows][G]
   RowSel* sel;     // [rows]
@@ -466,9 +519,41 @@ __global__ __launch_bounds__(kCT) void tk_collect_kernel(ChunkArgs a) {
     if ((take & (1u << j)) && o < rs.m) dst[o++] = make_uint2(order_key(v[j]), (uint32_t)(i0 + j));
 }
 
+// Candidate lists in LDS are stored with one pad word after every 8 entries:
+// the stable emission gives each thread a run of up to 8 consecutive entries,
+// and with the pad the 64 lanes of a wave read 64 different banks instead of
+// 8 lanes per bank.
+constexpr int kCapPadded = kCap + kCap / 8;
+__device__ __forceinline__ int lds_at(int i) { return i + (i >> 3); }
+
+// Stable emission of a position-ordered candidate list (keys ck, positions
+// cp, m entries in LDS at lds_at(i)): every entry with key > v and the first
+// `need` with key == v, in list order.  Thread t owns entries [t*P, t*P + P):
+// one pass counts them, two scans place them, a second pass writes.
+__device__ __forceinline__ void emit_stable(const uint32_t* ck, const int* cp, int m, uint32_t v, int need,
+                                            int k, int32_t* __restrict__ dst, int* redi) {
+  const int tid = threadIdx.x;
+  const int P = (m + kFT - 1) / kFT;
+  const int e0 = min(m, tid * P), e1 = min(m, e0 + P);
+  int gt = 0, eq = 0;
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t key = ck[lds_at(i)];
+    gt += key > v;
+    eq += key == v;
+  }
+  int tot;
+  int eq_rank = block_excl_scan<kFT>(eq, redi, &tot);
+  const int take_eq = min(eq, max(0, need - eq_rank));
+  int out = block_excl_scan<kFT>(gt + take_eq, redi, &tot);
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t key = ck[lds_at(i)];
+    if ((key > v || (key == v && eq_rank++ < need)) && out < k) dst[out++] = cp[lds_at(i)];
+  }
+}
+
 __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __restrict__ idx) {
-  __shared__ uint32_t ck[kCap];
-  __shared__ int cp[kCap];
+  __shared__ uint32_t ck[kCapPadded];
+  __shared__ int cp[kCapPadded];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t redu[kFT / kWave];
   __shared__ int redi[kFT / kWave];
@@ -493,8 +578,8 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < m; i += kFT) {
     const uint2 e = src[i];
-    ck[i] = e.x;
-    cp[i] = (int)e.y;
+    ck[lds_at(i)] = e.x;
+    cp[lds_at(i)] = (int)e.y;
     if (in_vb(e.x)) {
       kmin = min(kmin, e.x);
       kmax = max(kmax, e.x);
@@ -504,46 +589,202 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
   kmax = block_reduce<kFT>(kmax, redu, UMaxOp{});   // its barriers publish ck / cp
   int need = 0;
   const uint32_t v = radix_kth<kFT>(
-      m, a.k - rs.above, kmin, kmax, [&](int i) { return ck[i]; }, [&](int i) { return in_vb(ck[i]); }, hist,
+      m, a.k - rs.above, kmin, kmax, [&](int i) { return ck[lds_at(i)]; }, [&](int i) { return in_vb(ck[lds_at(i)]); }, hist,
       &sel_bin, &sel_above, &need);
 
-  // stable emission: thread t owns list entries [t*P, t*P + P)
-  const int P = (m + kFT - 1) / kFT;
-  const int e0 = min(m, tid * P), e1 = min(m, e0 + P);
-  int eq = 0;
-  for (int i = e0; i < e1; ++i) eq += ck[i] == v;
-  int tot;
-  int eq_rank = block_excl_scan<kFT>(eq, redi, &tot);
-  int keep = 0;
-  for (int i = e0; i < e1; ++i) {
-    const uint32_t key = ck[i];
-    keep += key > v || (key == v && eq_rank++ < need);
+  emit_stable(ck, cp, m, v, need, a.k, dst, redi);
+}
+
+// ---- wave-local keep + merge (rows of at most kLocalMaxPieces pieces) ----
+
+constexpr int kLocalNV = 16;                    // scores per lane of a standalone piece
+constexpr int kLocalSpan = kLocalNV * kWave;    // 1024 positions per piece
+
+__global__ __launch_bounds__(256) void tk_wave_local_kernel(ChunkArgs a) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row = blockIdx.y, piece = blockIdx.x * 4 + wave;
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
+  if (n <= a.k) return;
+  const int P = (n + kLocalSpan - 1) / kLocalSpan;
+  if (piece >= P) return;
+  const int pos0 = piece * kLocalSpan;
+  const float* src = a.scores + (int64_t)row * a.ld;
+  float v[kLocalNV];
+  uint64_t valid[kLocalNV];
+#pragma unroll
+  for (int j = 0; j < kLocalNV; ++j) {
+    const int c = n - (pos0 + kWave * j);     // valid lanes of value j
+    valid[j] = c >= kWave ? ~0ull : (c <= 0 ? 0ull : (1ull << c) - 1ull);
+    v[j] = src[min(pos0 + kWave * j + l, n - 1)];
   }
-  int out = block_excl_scan<kFT>(keep, redi, &tot);
-  eq_rank -= eq;
-  for (int i = e0; i < e1; ++i) {
-    const uint32_t key = ck[i];
-    if ((key > v || (key == v && eq_rank++ < need)) && out < a.k) dst[out++] = cp[i];
+  const int cap = kLocalCap / P;
+  __shared__ uint32_t hist[4][kLocalBins];
+  const uint4 r = wave_keep_top<kLocalNV>(v, valid, pos0, cap, hist[wave],
+                                          a.cand + (int64_t)row * kLocalCap + (int64_t)piece * cap);
+  if (l == 0) a.local[(int64_t)row * a.local_stride + piece] = r;
+}
+
+// Per row: the pieces' kept entries (piece c at slots [c*cap, c*cap + kept_c)
+// of the candidate list) gathered in position order into LDS.  Entries at or
+// below the largest dropped key D rank below some dropped entry; if at least
+// k entries lie above D, the row's k-th best is among them and every dropped
+// entry ranks below it, so the k-th best of the entries above D and a stable
+// emission give the row's top k.  Otherwise the whole-row select runs.
+//   pass 1: load the entries into LDS; those above D also go into a
+//           kSingleBins value histogram over (D, largest kept];
+//   the bin vb holding the k-th best, then pass 2 copies vb's entries to a
+//   short list on which the exact radix select runs (all of vb's entries are
+//   above D, so ties at the k-th key are all there);
+//   passes 3 and 4: stable emission.
+constexpr int kShort = 1024;     // short-list capacity (else the radix runs over the whole list)
+
+__global__ __launch_bounds__(kFT) void tk_merge_kernel(ChunkArgs a, int32_t* __restrict__ idx) {
+  __shared__ uint32_t ck[kCapPadded];
+  __shared__ int cp[kCapPadded];
+  __shared__ uint32_t hist[kSingleBins];
+  __shared__ uint32_t sk[kShort];
+  __shared__ uint32_t redu[kFT / kWave];
+  __shared__ int redi[kFT / kWave];
+  __shared__ int offs[kLocalMaxPieces + 1];
+  __shared__ int sel_bin, sel_above, sh_short;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = row_len(row, a.n_q, a.q_start, a.seq);
+  int32_t* dst = idx + (int64_t)row * a.k;
+  if (n <= a.k) {
+    write_trivial(dst, n, a.k);
+    return;
   }
+  for (int i = tid; i < kSingleBins; i += kFT) hist[i] = 0u;
+  if (tid == 0) sh_short = 0;
+  const int P = (n + a.local_span - 1) / a.local_span;     // <= kLocalMaxPieces
+  const int cap = kLocalCap / P;
+  const uint4 e = tid < P ? a.local[(int64_t)row * a.local_stride + tid] : make_uint4(0u, 0u, 0xFFFFFFFFu, 0u);
+  int m;
+  const int ex = block_excl_scan<kFT>((int)e.x, redi, &m);
+  if (tid < P) offs[tid] = ex;
+  if (tid == 0) offs[P] = m;
+  const uint32_t dmax = block_reduce<kFT>(e.y, redu, UMaxOp{});   // its barriers publish offs
+  const uint32_t gmin = block_reduce<kFT>(e.z, redu, UMinOp{});
+  const uint32_t gmax = block_reduce<kFT>(e.w, redu, UMaxOp{});
+  if (m >= a.k) {
+    const float lo = key_value(max(dmax + 1u, gmin));
+    const float inv = bin_scale(lo, key_value(gmax), kSingleBins);
+    const uint2* src = a.cand + (int64_t)row * kLocalCap;
+    const int slots = P * cap;
+    constexpr int kB = 8;                     // loads per thread in flight
+    int above = 0;
+    for (int i0 = tid; i0 < slots; i0 += kFT * kB) {
+      uint2 x[kB];
+      int o[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = min(i0 + u * kFT, slots - 1);
+        x[u] = src[i];
+        const int c = i / cap;
+        const int at = offs[c] + (i - c * cap);
+        o[u] = (i0 + u * kFT < slots && at < offs[c + 1]) ? at : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (o[u] >= 0) {
+          ck[lds_at(o[u])] = x[u].x;
+          cp[lds_at(o[u])] = (int)x[u].y;
+          if (x[u].x > dmax) {
+            ++above;
+            atomicAdd(&hist[vbin(key_value(x[u].x), lo, inv, kSingleBins)], 1u);
+          }
+        }
+    }
+    int n_above;
+    block_excl_scan<kFT>(above, redi, &n_above);     // its barriers publish ck, cp and hist
+    if (n_above >= a.k) {
+      pick_from_top(hist, kSingleBins, a.k, &sel_bin, &sel_above);
+      const int vb = sel_bin, kb = a.k - sel_above;
+      const auto in_vb = [&](uint32_t key) { return key > dmax && vbin(key_value(key), lo, inv, kSingleBins) == vb; };
+      uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+      for (int i = tid; i < m; i += kFT) {
+        const uint32_t key = ck[lds_at(i)];
+        if (in_vb(key)) {
+          const int j = atomicAdd(&sh_short, 1);
+          if (j < kShort) sk[j] = key;
+          bmin = min(bmin, key);
+          bmax = max(bmax, key);
+        }
+      }
+      bmin = block_reduce<kFT>(bmin, redu, UMinOp{});   // its barriers publish sk and sh_short
+      bmax = block_reduce<kFT>(bmax, redu, UMaxOp{});
+      const int ns = sh_short;
+      int need = 0;
+      uint32_t v;
+      if (ns <= kShort)
+        v = radix_kth<kFT>(ns, kb, bmin, bmax, [&](int i) { return sk[i]; }, [&](int) { return true; }, hist,
+                           &sel_bin, &sel_above, &need);
+      else
+        v = radix_kth<kFT>(m, kb, bmin, bmax, [&](int i) { return ck[lds_at(i)]; },
+                           [&](int i) { return in_vb(ck[lds_at(i)]); }, hist, &sel_bin, &sel_above, &need);
+      emit_stable(ck, cp, m, v, need, a.k, dst, redi);
+      return;
+    }
+  }
+  select_row_single(a.scores + (int64_t)row * a.ld, n, a.k, dst);
 }
 
 int64_t chunks_per_row(int64_t max_n) { return (max_n + kChunk - 1) / kChunk; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace of the few-rows select: the five-pass state (range partials,
+// chunk histograms, chunk offsets, row records), the candidate list and the
+// standalone pieces' records.
+struct TopkLayout {
+  float2* rng_own;
+  uint32_t* hist;
+  int32_t* off;
+  RowSel* sel;
+  uint2* cand;
+  uint4* local;
+  int G, PL;
+  size_t bytes;
+};
+
+TopkLayout topk_layout(void* ws, int rows, int64_t max_n) {
+  TopkLayout t{};
+  t.G = (int)chunks_per_row(max_n);
+  t.PL = (int)((max_n + kLocalSpan - 1) / kLocalSpan);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const uintptr_t at = base + o;
+    o += align256(bytes);
+    return at;
+  };
+  t.rng_own = reinterpret_cast<float2*>(take((size_t)rows * t.G * sizeof(float2)));
+  t.hist = reinterpret_cast<uint32_t*>(take((size_t)rows * t.G * kVB * 4));
+  t.off = reinterpret_cast<int32_t*>(take((size_t)rows * t.G * 4));
+  t.sel = reinterpret_cast<RowSel*>(take((size_t)rows * sizeof(RowSel)));
+  t.cand = reinterpret_cast<uint2*>(take((size_t)rows * kCap * sizeof(uint2)));
+  t.local = reinterpret_cast<uint4*>(take((size_t)rows * t.PL * sizeof(uint4)));
+  t.bytes = o;
+  return t;
+}
+
 }  // namespace
 
 size_t topk_rows_ws_bytes(int rows, int64_t max_n, int k) {
   if (rows >= kMultiRowLimit || max_n <= k) return 0;
-  const size_t G = (size_t)chunks_per_row(max_n);
-  return align256((size_t)rows * G * sizeof(float2)) + align256((size_t)rows * G * kVB * 4) +
-         align256((size_t)rows * G * 4) + align256((size_t)rows * sizeof(RowSel)) +
-         align256((size_t)rows * kCap * sizeof(uint2));
+  return topk_layout(nullptr, rows, max_n).bytes;
 }
+
+bool topk_rows_local_fits(int rows, int64_t max_n, int k, int span) {
+  return topk_rows_ws_bytes(rows, max_n, k) != 0 && (max_n + span - 1) / span <= kLocalMaxPieces;
+}
+
+uint2* topk_rows_cand(void* ws, int rows, int64_t max_n) { return topk_layout(ws, rows, max_n).cand; }
 
 hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int rows, int n_q,
                             int64_t q_start, const int64_t* seq_q_start, int k, void* ws, hipStream_t s,
-                            const float2* rng, int rng_span, int rng_stride) {
+                            const float2* rng, int rng_span, int rng_stride, const uint4* pre_local,
+                            int pre_span, int pre_stride) {
   const int64_t max_n = q_start + n_q;
   if (topk_rows_ws_bytes(rows, max_n, k) == 0) {
     hipLaunchKernelGGL(topk_rows_single_kernel, dim3(rows), dim3(kFT), 0, s, scores, ld, idx, n_q,
@@ -551,6 +792,7 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
     return hipGetLastError();
   }
   if (ws == nullptr) return hipErrorInvalidValue;
+  const TopkLayout t = topk_layout(ws, rows, max_n);
   ChunkArgs a{};
   a.scores = scores;
   a.ld = ld;
@@ -558,10 +800,9 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
   a.q_start = q_start;
   a.seq = seq_q_start;
   a.k = k;
-  a.G = (int)chunks_per_row(max_n);
+  a.G = t.G;
   a.vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0) ? 1 : 0;
-  char* p = static_cast<char*>(ws);
-  a.rng_own = reinterpret_cast<float2*>(p);
+  a.rng_own = t.rng_own;
   if (rng) {
     a.rng = rng;
     a.rng_span = rng_span;
@@ -571,14 +812,27 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int32_t* idx, int r
     a.rng_span = kChunk;
     a.rng_stride = a.G;
   }
-  p += align256((size_t)rows * a.G * sizeof(float2));
-  a.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * a.G * kVB * 4);
-  a.off = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)rows * a.G * 4);
-  a.sel = reinterpret_cast<RowSel*>(p);
-  p += align256((size_t)rows * sizeof(RowSel));
-  a.cand = reinterpret_cast<uint2*>(p);
+  a.hist = t.hist;
+  a.off = t.off;
+  a.sel = t.sel;
+  a.cand = t.cand;
+  if (pre_local) {                      // the score kernel ran the wave-local stage
+    if ((max_n + pre_span - 1) / pre_span > kLocalMaxPieces) return hipErrorInvalidValue;
+    a.local = const_cast<uint4*>(pre_local);
+    a.local_span = pre_span;
+    a.local_stride = pre_stride;
+    hipLaunchKernelGGL(tk_merge_kernel, dim3(rows), dim3(kFT), 0, s, a, idx);
+    return hipGetLastError();
+  }
+  if (t.PL <= kLocalMaxPieces) {
+    a.local = t.local;
+    a.local_span = kLocalSpan;
+    a.local_stride = t.PL;
+    hipLaunchKernelGGL(tk_wave_local_kernel, dim3((unsigned)((t.PL + 3) / 4), (unsigned)rows), dim3(256), 0, s,
+                       a);
+    hipLaunchKernelGGL(tk_merge_kernel, dim3(rows), dim3(kFT), 0, s, a, idx);
+    return hipGetLastError();
+  }
   const dim3 chunk_grid((unsigned)((int64_t)rows * a.G));
   if (!rng) hipLaunchKernelGGL(tk_range_kernel, chunk_grid, dim3(kCT), 0, s, a);
   hipLaunchKernelGGL(tk_hist_kernel, chunk_grid, dim3(kCT), 0, s, a);

@@ -1,6 +1,9 @@
 """Row top-k over caller-provided fp32 scores (ix_topk_scores), on every
-select path: the chunked multi-workgroup select for few long rows (with its
-whole-row fallback when the k-th best sits in an over-full value bin), the
+select path: for few long rows the chunk-local keep + per-row merge (rows of
+up to 128 chunks of 8192 scores, with its whole-row fallback when a chunk
+dropped an entry that could rank among the k best, as on monotone ramps, or
+too few were kept) and the five-pass chunked select for longer rows (with its
+fallback when the k-th best sits in an over-full value bin); the
 single-workgroup select for many rows, unaligned row strides and rows short
 enough to keep every position.  Compared with the oracle's stable sort,
 element for element."""
@@ -70,6 +73,35 @@ def test_chunked_fallback_flat_rows(ix):
     signed_zero[0, 0, ::3] = -0.0
     for s in (flat, outlier, signed_zero):
         _check(ix, s, 2048, L - 1, L)
+
+
+def test_chunked_monotone_ramps_fall_back(ix):
+    """The k best all sit in the last (increasing) or first (decreasing)
+    chunk: that chunk keeps only 8192 / chunks of them, so its dropped keys
+    outrank the merged k-th best and the row takes the whole-row select."""
+    L = 200_001
+    up = torch.arange(L, device="cuda", dtype=torch.float32).reshape(1, 1, L)
+    down = torch.flip(up, dims=[2]).contiguous()
+    _check(ix, torch.cat([up, down], dim=0), 2048, L - 1, L)
+
+
+def test_chunked_local_path_at_its_longest_rows(ix):
+    """128 chunks of 8192 (the longest rows of the local + merge passes):
+    each chunk keeps 64 entries."""
+    g = torch.Generator(device="cuda").manual_seed(17)
+    L = 128 * 8192
+    scores = torch.randn((2, 1, L), generator=g, device="cuda")
+    _check(ix, scores, 2048, L - 1, L)
+
+
+def test_chunked_five_pass_path_past_1m(ix):
+    """Rows of more than 128 chunks use the range / histogram / select /
+    collect / finish passes."""
+    g = torch.Generator(device="cuda").manual_seed(18)
+    L = 128 * 8192 + 5001
+    scores = torch.randn((2, 1, L), generator=g, device="cuda")
+    ties = torch.randint(-50, 50, (1, 1, L), generator=g, device="cuda").float()
+    _check(ix, torch.cat([scores, ties], dim=0), 2048, L - 1, L)
 
 
 def test_chunked_ragged_rows_with_short_prefix(ix):
