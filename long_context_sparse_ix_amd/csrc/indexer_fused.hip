@@ -325,6 +325,9 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
                                             const bf16x8 (&bfr)[KS], f32x16 (&acc_mma)[HT],
                                             const f32x16 (&acc_epi)[HT]) {
   if constexpr (MMA) {
+    // a wave issuing MFMAs outranks the other wave of its SIMD while that one
+    // filters or shrinks, so the matrix pipe stays fed (0.7% at L=128K)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -348,6 +351,7 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                          // 4 VALU
     }
   }
+  if constexpr (MMA) __builtin_amdgcn_s_setprio(0);
   return part;
 }
 
