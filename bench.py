@@ -102,15 +102,16 @@ def attention_bytes(w):
     return (gathered_rows(w) * w.d_qk * 2 + rows * w.q_heads * (w.d_qk + w.d_v) * 2 + rows * w.k * 4)
 
 
-def load_traffic():
+def load_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing or was taken on another version of the kernel."""
+    None when it is missing, was taken on another version of the kernel, or
+    on another workload (the counters were taken at one size only)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_sha(ATTN_SOURCE):
+    if t.get("source_sha256") != source_sha(ATTN_SOURCE) or t.get("workload") != workload:
         return None
     return t
 
@@ -241,7 +242,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="l128k", choices=sorted(CONFIGS))
     ap.add_argument("--kernel-reps", type=int, default=3)
-    ap.add_argument("--sample-rows", type=int, default=48)
+    ap.add_argument("--sample-rows", type=int, default=0,
+                    help="rows checked against the oracle and timed on the CPU (0: 48, fewer for "
+                         "rows of more than 512K candidates so the CPU leg stays near half a minute)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-full", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -354,10 +357,13 @@ def main(argv=None):
         run_group(fs_mask, inp.idx_fs)
         torch.cuda.synchronize()
 
-    tr = load_traffic()
+    tr = load_traffic(w.name)
     traffic_bytes = None if tr is None else tr["hbm_bytes_per_launch"]
 
-    rows = synth.sample_rows(w, args.sample_rows)
+    n_sample = args.sample_rows
+    if n_sample <= 0:   # the oracle costs about 2 s per row at 1M candidates
+        n_sample = 48 if w.kv_len <= 512 * 1024 else 12
+    rows = synth.sample_rows(w, n_sample)
     result_cpu, parity = None, None
     if not args.no_cpu_baseline:
         log(f"CPU oracle on {len(rows)} sampled rows")

@@ -111,6 +111,35 @@ def test_increasing_scores_keep_latest_positions(ix, path):
         assert got[0, t, :n].tolist() == list(range(t + 1 - n, t + 1))
 
 
+@pytest.mark.parametrize("increasing", [True, False])
+def test_long_ramp_rows_on_the_few_rows_path(ix, increasing):
+    """Few long rows on the materialised path (score kernel with the top-k's
+    wave-local keep, then the merge): with score(s) = s every row's k best
+    sit in its last waves' pieces, with score(s) = L-1-s in its first ones,
+    so pieces drop winners and the merge must fall back to the whole-row
+    select.  Scores are exact: q = (4096, 64, 1) and the key holds the base-64
+    digits of s (or of L-1-s), all exact in bf16."""
+    L, k, n_q = 150_001, 2048, 3
+    w = synth.L16K.with_(name="long_ramp", batch=2, n_q=n_q, q_start=L - n_q, kv_len=L, k=k, ix_heads=1,
+                         ix_dim=16, mode="exact")
+    s = torch.arange(L, device="cuda")
+    v = s if increasing else (L - 1 - s)
+    keys = torch.zeros((2, L, 16), dtype=torch.float32, device="cuda")
+    keys[:, :, 0] = torch.div(v, 4096, rounding_mode="floor").float()
+    keys[:, :, 1] = (torch.div(v, 64, rounding_mode="floor") % 64).float()
+    keys[:, :, 2] = (v % 64).float()
+    q = torch.zeros((2, n_q, 1, 16), dtype=torch.float32, device="cuda")
+    q[..., 0], q[..., 1], q[..., 2] = 4096.0, 64.0, 1.0
+    inputs = (q.to(torch.bfloat16), torch.ones((2, n_q, 1), device="cuda"), keys.to(torch.bfloat16), None)
+    assert torch.equal(inputs[2].float(), keys)
+    _, got = _run(ix, w, 2, inputs=inputs)
+    for b in range(2):
+        for t in range(n_q):
+            p = w.q_start + t
+            want = list(range(p + 1 - k, p + 1)) if increasing else list(range(k))
+            assert got[b, t].tolist() == want, f"b={b} t={t}"
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_fp8_every_code_orders_like_the_oracle(ix, path):
     """One key per e4m3fn code (NaN codes excluded), scored by a unit query:
