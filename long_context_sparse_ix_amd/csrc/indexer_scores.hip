@@ -155,6 +155,8 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
                                                          __float_as_uint(part[1]), false, false);
         float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const int64_t s = s0 + l;
+        // (a partial last group of bf16's three-tile groups runs past the
+        // wave's ten tiles; those scores are masked and not kept)
         if (j < kTilesPerWave) kept[j < kTilesPerWave ? j : 0] = FP8 ? score * sc[u] : score;
         if (s <= p) {
           if constexpr (FP8) score *= sc[u];
