@@ -140,6 +140,22 @@ def test_long_ramp_rows_on_the_few_rows_path(ix, increasing):
             assert got[b, t].tolist() == want, f"b={b} t={t}"
 
 
+@pytest.mark.parametrize("key_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_len", [327_680, 400_001])
+def test_exact_few_long_rows_both_score_kernel_modes(ix, key_dtype, kv_len):
+    """Few long rows on the materialised path at the edge of the score
+    kernel's two modes: rows of up to 512 waves' spans (327,680 keys) keep
+    each wave's best for the one-pass merge (here 16 slots per wave, the
+    fewest it allows), longer rows get per-wave score ranges for the
+    five-pass select.  Integer-valued inputs: bit-exact against the oracle."""
+    w = synth.DECODE_B32.with_(name=f"exact_long_{kv_len}", batch=2, n_q=2, q_start=kv_len - 2, kv_len=kv_len,
+                               ix_heads=4, ix_dim=32, key_dtype=key_dtype, mode="exact", decode_steps=0,
+                               kv_cap=0)
+    inputs, got = _run(ix, w, 2)
+    valid_idx_rows(got, w.q_start, w.k)
+    np.testing.assert_array_equal(got, _oracle(w, inputs))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_fp8_every_code_orders_like_the_oracle(ix, path):
     """One key per e4m3fn code (NaN codes excluded), scored by a unit query:
