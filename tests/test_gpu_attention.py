@@ -126,3 +126,33 @@ def test_full_prefix_equals_dense_causal(ix):
     rows = list(range(300))
     ref, ref_lse = _oracle(w, Q, KV, idx, rows, sm_scale=0.125)
     _check(got, lse, ref, ref_lse, rows)
+
+
+@pytest.mark.parametrize("n_q", [4, 1024])
+def test_dominant_logit_in_every_key_group(ix, n_q):
+    """One slot per row has logit 256 (natural units) and the others 0, so the
+    output is that slot's value row exactly and lse = 256.  The dominant slot
+    sits in a different one of the four 4-key groups of a 16-slot step (and,
+    with few rows, in a different wave of the four sharing a row) from row to
+    row: a running max that missed a group would leave 2^369 unscaled and
+    overflow.  n_q = 4 runs the four-waves-per-row split, 1024 one wave per
+    row."""
+    k, L = 64, 2048
+    w = synth.TINY_L1K.with_(name="dominant", n_q=n_q, q_start=L - n_q, kv_len=L, k=k, q_heads=8, d_qk=128,
+                             d_v=96)
+    KV = torch.zeros((1, L, w.d_qk), dtype=torch.bfloat16, device="cuda")
+    KV[0, :, 1:] = torch.randn((L, w.d_qk - 1), generator=torch.Generator(device="cuda").manual_seed(3),
+                               device="cuda").to(torch.bfloat16)
+    dom = 1000 + torch.arange(16, device="cuda")
+    KV[0, dom, 0] = 16.0
+    Q = torch.zeros((1, n_q, w.q_heads, w.d_qk), dtype=torch.bfloat16, device="cuda")
+    Q[..., 0] = 16.0
+    r = torch.arange(n_q, device="cuda")
+    idx = torch.arange(k, dtype=torch.int32, device="cuda").repeat(1, n_q, 1)
+    slot = 16 * (r % 4) + 4 * ((r + r // 4) % 4) + (r % 3)       # wave r%4; rows 0..3 cover groups 0..3
+    idx[0, r, slot] = dom[(r % 16)].to(torch.int32)
+    got, lse = _attn(ix, w, Q, KV, idx, sm_scale=1.0)
+    want = KV[0, dom[(r % 16)], : w.d_v].float().cpu().numpy()          # [n_q, Dv]
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+    np.testing.assert_array_equal(got[0], np.broadcast_to(want[:, None, :], got[0].shape))
+    np.testing.assert_allclose(lse[0], 256.0, rtol=0, atol=1e-3)
