@@ -213,3 +213,25 @@ def test_append_keys_per_sequence_rows_need_pos_at_the_bound():
     call = lambda pos, n=1: lib.ix_append_keys(ctypes.byref(p), 32, DUMMY, n, pos, DUMMY, DUMMY, None)
     assert call(4) == ix.IX_E_SHAPE
     assert call(8) == ix.IX_E_SHAPE                  # past kv_cap
+
+
+def test_workspace_sizes_cover_the_row_select_state():
+    """Host-side sizes: the few-long-rows top-k needs at least its 8192-entry
+    candidate list per row plus one 16-byte record per 1024-score piece; the
+    materialised indexer adds the score rows and one 16-byte record per
+    640-key wave of the score kernel; many-row calls and rows no longer than
+    k need no row-select state."""
+    lib = ensure_lib()
+    rows, n = 32, 200_001
+    p = _prob(batch=rows, n_q=1, q_start=n - 1, kv_len=n, kv_cap=n, k=2048)
+    topk = lib.ix_workspace_bytes(ctypes.byref(p), ix.IX_OP_TOPK_SCORES, None)
+    pieces = -(-n // 1024)
+    assert topk >= rows * 8192 * 8 + rows * pieces * 16
+    d = _ixr(heads=64, dim=128, k_dtype=ix.IX_DTYPE_FP8_E4M3FN, path=2, k_scale=DUMMY)
+    mat = lib.ix_workspace_bytes(ctypes.byref(p), ix.IX_OP_INDEXER_TOPK, ctypes.byref(d))
+    ld = (n + 3) // 4 * 4
+    assert mat >= rows * ld * 4 + rows * (-(-n // 640)) * 16 + topk
+    many = _prob(batch=1, n_q=1024, q_start=n - 1024, kv_len=n, kv_cap=n, k=2048)
+    assert lib.ix_workspace_bytes(ctypes.byref(many), ix.IX_OP_TOPK_SCORES, None) == 0
+    short = _prob(batch=4, n_q=1, q_start=1000, kv_len=1001, kv_cap=1001, k=2048)
+    assert lib.ix_workspace_bytes(ctypes.byref(short), ix.IX_OP_TOPK_SCORES, None) == 0
