@@ -94,4 +94,42 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// Full-wave reduction with the result in every lane, in registers: DPP moves
+// pair lanes within 16 (xor 1, xor 2, then the 8- and 16-lane mirrors, which
+// pair each already-reduced half with the other), v_permlane16_swap and
+// v_permlane32_swap the 16- and 32-lane halves (with both operands v, the two
+// results hold v of the lane and of its partner).  __shfl_xor would take an
+// LDS round trip (ds_bpermute) per step instead.  op must be associative and
+// commutative (min, max, integer add).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  const auto bits = [](T x) { return __builtin_bit_cast(uint32_t, x); };
+  const auto val = [](uint32_t x) { return __builtin_bit_cast(T, x); };
+  v = op(v, val(dpp_mov<0xB1>(bits(v))));     // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, val(dpp_mov<0x4E>(bits(v))));     // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, val(dpp_mov<0x141>(bits(v))));    // row_half_mirror: 7 - i within 8
+  v = op(v, val(dpp_mov<0x140>(bits(v))));    // row_mirror: 15 - i within 16
+  auto r = __builtin_amdgcn_permlane16_swap(bits(v), bits(v), false, false);
+  v = op(val(r[0]), val(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(bits(v), bits(v), false, false);
+  return op(val(r[0]), val(r[1]));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_min(float v) {
+  return wave_reduce(v, [](float a, float b) { return fminf(a, b); });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
 }  // namespace ix

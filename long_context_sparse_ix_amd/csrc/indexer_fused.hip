@@ -75,26 +75,10 @@ struct Thresh {
   int need;     // how many entries with key == v belong to the top k
 };
 
-__device__ __forceinline__ float wave_min_f(float v) {
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) v = fminf(v, __shfl_xor(v, dd));
-  return v;
-}
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) v = fmaxf(v, __shfl_xor(v, dd));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, dd));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, dd));
-  return v;
-}
+__device__ __forceinline__ float wave_min_f(float v) { return wave_min(v); }
+__device__ __forceinline__ float wave_max_f(float v) { return wave_max(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_min(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_max(v); }
 
 // Candidate buffer of one row: `cap` scores, then the `cap` positions (two
 // arrays, so passes that need only the scores read contiguous words).  Passes

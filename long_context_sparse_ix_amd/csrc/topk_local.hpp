@@ -7,8 +7,9 @@
 // records the largest order key it dropped.  The merge pass then selects the
 // row's k best among the kept entries, which is exact whenever that k-th best
 // is above every dropped key (see topk_rows.hip).  Everything here is one
-// wave: a histogram in the wave's own LDS words, ballots and lane shuffles, no
-// barriers, so the stage can also run as the epilogue of the score kernel.
+// wave: a histogram in the wave's own LDS words, ballots and register-level
+// lane exchanges, no barriers, so the stage can also run as the epilogue of
+// the score kernel.
 #pragma once
 
 #include "device_common.hpp"
@@ -45,11 +46,8 @@ __device__ __forceinline__ uint4 wave_keep_top(const float (&v)[NV], const uint6
         lo = fminf(lo, v[j]);
         hi = fmaxf(hi, v[j]);
       }
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) {
-      lo = fminf(lo, __shfl_xor(lo, dd));
-      hi = fmaxf(hi, __shfl_xor(hi, dd));
-    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
     inv = (float)kLocalBins / (hi - lo);
     if (!(hi > lo) || !(inv > 0.0f) || !(inv < INFINITY)) inv = 0.0f;   // one bin: keep nothing
     *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
@@ -89,13 +87,7 @@ __device__ __forceinline__ uint4 wave_keep_top(const float (&v)[NV], const uint6
     }
     out += __popcll(km);
   }
-#pragma unroll
-  for (int dd = 32; dd >= 1; dd >>= 1) {
-    dropped = max(dropped, (uint32_t)__shfl_xor((int)dropped, dd));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, dd));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, dd));
-  }
-  return make_uint4((uint32_t)out, dropped, kmin, kmax);
+  return make_uint4((uint32_t)out, wave_max(dropped), wave_min(kmin), wave_max(kmax));
 }
 
 }  // namespace ix

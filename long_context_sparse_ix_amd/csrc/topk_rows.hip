@@ -92,8 +92,7 @@ __device__ __forceinline__ float bin_scale(float lo, float hi, int nbins) {
 
 template <int NT, typename T, typename Op>
 __device__ __forceinline__ T block_reduce(T v, T* red, Op op) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = op(v, __shfl_xor(v, d));
+  v = wave_reduce(v, op);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   T r = red[0];
