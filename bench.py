@@ -449,6 +449,58 @@ def bench_op(args, w, torch, synth, ix):
     return 0
 
 
+def decode_oracle_leg(w, torch, keys, scale, kvs, step_inputs, last, j, log, n_seq=12):
+    """The CPU oracle on n_seq sequences of decode step j (indexer over the
+    whole cache, then the four layers' attention over the GPU's positions),
+    timed and extrapolated to the batch; parity of those sequences."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dsa_oracle as O
+
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    seqs = list(range(0, w.batch, max(1, w.batch // n_seq)))[:n_seq]
+    q_start, kv_len = w.q_start + j, w.kv_len + j
+    ixl, att = step_inputs
+    ixe = ixl[0]                                   # the full layer's indexer inputs
+    sel = torch.tensor(seqs, device=keys.device)
+    h_q, h_w = bits(ixe["q"][sel]), ixe["w"][sel].cpu().numpy()
+    h_k, h_s = keys[sel, :kv_len].contiguous().cpu().numpy(), scale[sel, :kv_len].cpu().numpy()
+    gpu_idx = last["idx"][sel]                                      # [S, 1, k]
+    # attention inputs: only the selected latent rows leave the device
+    gidx = gpu_idx.clamp(min=0).long()
+    att_in = []
+    for l in range(4):
+        kvg = torch.stack([kvs[l][b][gidx[i, 0]] for i, b in enumerate(seqs)])   # [S, k, D]
+        att_in.append((bits(att[l]["q"][sel]), bits(kvg)))
+    slot = torch.where(gpu_idx >= 0, torch.arange(w.k, device=keys.device).view(1, 1, -1),
+                       torch.full_like(gpu_idx, -1)).cpu().numpy().astype(np.int32)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    log(f"CPU oracle on {len(seqs)} sequences of decode step {j}")
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        ref_idx = O.indexer_topk(h_q, h_w, h_k, "fp8", h_s, q_start, kv_len, w.k)
+        t_ix = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        ref_o = [O.sparse_attention(qb, kvb, slot, w.k, 1.0 / math.sqrt(w.d_qk), w.d_v)[0] for qb, kvb in att_in]
+        t_at = time.perf_counter() - t0
+    got = gpu_idx.cpu().numpy()
+    inter = tot = 0
+    for g, r in zip(got.reshape(-1, w.k), ref_idx.reshape(-1, w.k)):
+        sr = set(r[r >= 0].tolist())
+        inter += len(set(g[g >= 0].tolist()) & sr)
+        tot += len(sr)
+    ovl = inter / max(tot, 1)
+    err = max(float(np.abs(last["outs"][l][sel].float().cpu().numpy() - ref_o[l]).max()) for l in range(4))
+    step_s = (t_ix + t_at) * w.batch / len(seqs)
+    cpu = {"value": w.batch / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{len(seqs)} of {w.batch} sequences of one decode step (indexer over {kv_len:,} keys, "
+                     f"4 layers of attention) timed {t_ix + t_at:.1f}s, extrapolated to the batch"}
+    parity = {"sequences": len(seqs), "idx_overlap": ovl, "attn_max_abs_err": err,
+              "ok": ovl >= 0.999 and err <= 2e-2}
+    return cpu, parity
+
+
 def bench_decode(args, w, torch, synth, ix):
     """Decode: each step appends one token to each of B sequences and runs one
     full+3 shared layer group for the new query rows."""
@@ -492,6 +544,9 @@ def bench_decode(args, w, torch, synth, ix):
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # the last timed step's results, for the oracle leg below (later runs overwrite them)
+    j_last = total - 1
+    last = dict(idx=idx[0].clone(), outs=[a["out"].clone() for a in steps[j_last][1]])
     allf = event_time(torch, lambda: run(args.warmup, mask=0xF), 2)
     key_bytes = w.batch * (w.kv_len + args.warmup) * (w.ix_dim + 4)
     app_ms = event_time(torch, lambda: ix.ix_append_keys(new_keys[0], keys, scale, w.q_start), 20)
@@ -528,12 +583,30 @@ def bench_decode(args, w, torch, synth, ix):
     mtp = {"draft_steps": n_draft, "ms_reuse": reuse_ms, "ms_reselect_every_step": reselect_ms,
            "speedup": reselect_ms / reuse_ms,
            "note": "one MTP layer, B sequences: the indexer + top-k once, then attention per step"}
+    # dominant op: the full layer's indexer + top-k (score kernel streaming the
+    # fp8 keys, then the one-pass merge), 58-60% of the step
+    ixe = steps[j_last][0][0]
+    ix_idx = torch.empty((w.batch, 1, w.k), dtype=torch.int32, device=dev)
+    ix_ms = event_time(torch, lambda: ix.ix_indexer_topk(ixe["q"], ixe["w"], keys, ix_idx, k_scale=scale,
+                                                         q_start=w.q_start + j_last, kv_len=w.kv_len + j_last), 20)
+    ix_bytes = w.batch * (w.kv_len + j_last) * (w.ix_dim + 4 + 4)
+    ix_gbps = ix_bytes / (ix_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": ix_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ix_gbps / PEAK_HBM_GBPS, "traffic": None,
+                "kernel": "ix_indexer_topk per call (indexer_scores_kernel + tk_merge_kernel): fp8 key codes + "
+                          "scale read and one fp32 score written per (row, key)",
+                "algorithmic_bytes": ix_bytes}
+
+    result_cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        result_cpu, parity = decode_oracle_leg(w, torch, keys, scale, kvs, steps[j_last], last, j_last, log)
     out = {"metric": "decode tokens/s (B=32, 200K context, one F,S,S,S group per step)",
            "value": w.batch / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, on device)",
            "config": {"workload": w.name, "batch": w.batch, "context": w.kv_len, "k": w.k},
            "step": "quantize+append the new token's indexer key into the fp8 cache, then the F,S,S,S group",
+           "roofline": roofline, "cpu_baseline": result_cpu, "parity": parity,
            "append_keys_us": app_ms * 1e3,
            "group": {"ms_fsss": ms, "ms_all_full": allf, "speedup_vs_all_full": allf / ms},
            "varlen": varlen, "mtp_draft": mtp,
