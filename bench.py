@@ -238,8 +238,10 @@ def sampled_parity(w, inp, rows, cb, torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 3; decode: 60, so that with the warmup the 64 decode "
+                         "steps of the workload run)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 1; decode: 4)")
     ap.add_argument("--config", default="l128k", choices=sorted(CONFIGS))
     ap.add_argument("--kernel-reps", type=int, default=3)
     ap.add_argument("--sample-rows", type=int, default=0,
@@ -277,6 +279,11 @@ def main(argv=None):
     ix.load()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[CONFIGS[args.config]]
+    if w.decode_steps and not args.op:
+        args.warmup = 4 if args.warmup is None else args.warmup
+        args.steps = w.decode_steps - args.warmup if args.steps is None else args.steps
+    args.warmup = 1 if args.warmup is None else args.warmup
+    args.steps = 3 if args.steps is None else args.steps
     if args.op:
         return bench_op(args, w, torch, synth, ix)
     if w.decode_steps:
