@@ -175,3 +175,24 @@ def test_append_keys_at_per_sequence_rows(ix):
         keep = np.ones(cap, bool)
         keep[p:p + n_new] = False
         assert np.all(codes[b, keep] == 0x55) and np.all(sc[b, keep] == -3.0)
+
+
+def test_topk_scores_long_rows_of_different_lengths(ix):
+    """Per-sequence starts through the wave-local keep + merge with a
+    different piece count in every row (3 to 489 pieces of 1024 scores, so
+    every piece keeps 2730 down to 16 entries), normal and tied scores."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    L, k = 500_001, 2048
+    starts = [3000, 60_000, 250_000, L - 1]
+    B = len(starts)
+    scores = torch.randn((B, 1, L), generator=g, device="cuda")
+    scores[1] = torch.randint(-2000, 2000, (1, L), generator=g, device="cuda").float()   # ties
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    print(f"[varlen] topk_scores long rows L={L} starts={starts}", flush=True)
+    ix.ix_topk_scores(scores, idx, kv_len=L, seq_q_start=_dev_starts(starts))
+    torch.cuda.synchronize()
+    s, got = host(scores), host(idx)
+    for b in range(B):
+        p = starts[b]
+        np.testing.assert_array_equal(got[b, 0], O.select_topk(s[b, 0, : p + 1].astype(np.float64), k),
+                                      err_msg=f"row b={b}")
