@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 3
+#define IX_ABI_VERSION 4
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -80,7 +80,8 @@ typedef enum ix_op {
   IX_OP_INDEXER_TOPK = 1,   /* op_desc: const ix_indexer_in*  */
   IX_OP_SPARSE_ATTN = 2,    /* op_desc: const ix_attn_in*     */
   IX_OP_GROUP_FORWARD = 3,  /* op_desc: const ix_group_desc*  */
-  IX_OP_TOPK_SCORES = 4     /* op_desc: NULL                  */
+  IX_OP_TOPK_SCORES = 4,    /* op_desc: NULL                  */
+  IX_OP_INDEXER_ARGMAX = 5  /* op_desc: const ix_indexer_in*  */
 } ix_op;
 
 /* Sizes shared by every layer of a call. */
@@ -156,20 +157,60 @@ const char* ix_last_error(void);
 size_t ix_workspace_bytes(const ix_problem* prob, int32_t op, const void* op_desc);
 
 /* Full-layer indexer and top-k (one F layer).
+ * Passages: "IndexShare" (LLM Architecture Gallery), section "Why The Indexer
+ * Becomes Expensive" -- the indexer scores every preceding token of a query
+ * and the top-k positions are kept; "GLM-5.2 and IndexShare for Long-Context
+ * Sparse Attention", section "Where the DSA indexer becomes expensive" --
+ * k = 2,048 per query position; "IndexShare", section "How IndexShare Works"
+ * -- a full layer runs this step and stores the positions.
  * Writes idx int32 [B][n_q][k]: for each query row, the min(k, p+1) positions
  * with the largest scores (equal scores: lower position wins), in ascending
  * position order, then -1 up to k.  The fp32 score matrix is never stored on
- * the fused path (scores stream straight into a per-row candidate set). */
+ * the fused path (scores stream straight into a per-row candidate set).
+ * Workspace: ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, in) bytes, 256-byte
+ * aligned, caller-owned, contents undefined on entry and on return.
+ * Errors: IX_E_NULL / IX_E_SHAPE / IX_E_DTYPE for bad arguments,
+ * IX_E_WORKSPACE when ws_bytes is too small, IX_E_HIP for a failed launch. */
 int32_t ix_indexer_topk(const ix_problem* prob, const ix_indexer_in* in, int32_t* idx,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Top-1 of the same indexer scores: for each query row, the position with the
+ * largest score (equal scores: lower position) into pos int32 [B][n_q] and,
+ * if score is not NULL, that fp32 score into score [B][n_q].  This is
+ * ix_indexer_topk with k = 1 under the same rule ("IndexShare", LLM
+ * Architecture Gallery, section "Why The Indexer Becomes Expensive"), run by
+ * the fused kernel with a running maximum in place of the streaming top-k, so
+ * its time is the score stream's alone.  Fused path only: dim in {16, 32,
+ * 64, 128} and in->path not IX_PATH_MATERIALIZED, else IX_E_SHAPE.  prob->k
+ * is validated but unused.  pos and score 4-byte aligned.  Workspace:
+ * ix_workspace_bytes(prob, IX_OP_INDEXER_ARGMAX, in) bytes (the staged keys). */
+int32_t ix_indexer_argmax(const ix_problem* prob, const ix_indexer_in* in, int32_t* pos, float* score,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Sparse attention of one layer over an index buffer idx int32 [B][n_q][k]
- * (typically written by ix_indexer_topk).  Entries outside [0, kv_len) are
- * ignored; latent rows outside [0, kv_len) are never read. */
+ * (typically written by ix_indexer_topk).
+ * Passages: "IndexShare" (LLM Architecture Gallery), section "Why The Indexer
+ * Becomes Expensive" -- the main attention runs only over the selected
+ * subset; "GLM-5.2 and IndexShare for Long-Context Sparse Attention", section
+ * "What IndexShare reuses" -- every layer, shared or not, computes its own
+ * attention over the shared positions.
+ * Entries outside [0, kv_len) are ignored; latent rows outside [0, kv_len)
+ * are never read.  out (and lse if given) are written for every row; a row
+ * with no valid entry gets o = 0 and lse = -inf.  Workspace:
+ * ix_workspace_bytes(prob, IX_OP_SPARSE_ATTN, in) bytes (0 when rows are many:
+ * split partials only exist for few rows).  Errors as ix_indexer_topk. */
 int32_t ix_sparse_attn(const ix_problem* prob, const ix_attn_in* in, const int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* One IndexShare layer group, layers run in order on `stream`.
+ * Passages: "IndexShare" (LLM Architecture Gallery), section "How IndexShare
+ * Works" -- full layers compute and store positions, shared layers skip the
+ * indexer and top-k and reuse the nearest preceding full layer's integer
+ * positions; "IndexCache: Killing the Indexer's O(NL^2) Bottleneck" notes,
+ * section 2 -- the first layer of a pattern is full; "GLM-5.2 and IndexShare
+ * for Long-Context Sparse Attention", section "What IndexShare reuses" -- the
+ * released pattern repeats full, shared, shared, shared after a few initial
+ * exceptions, which any f_mask expresses.
  * Bit l of f_mask set => layer l is full (F): it runs ix_indexer_topk with
  * ixr[l] into the next slot of idx, then attends; clear => shared (S): it
  * attends over the most recent F layer's slot, byte for byte unchanged.
@@ -179,7 +220,10 @@ int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_ma
                          const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx,
                          void* ws, size_t ws_bytes, void* stream);
 
-/* Top-k over caller-provided fp32 score rows: scores[(b*n_q + t)*ld + s] for
+/* The top-k step alone, over caller-provided fp32 score rows (the selection
+ * of "IndexShare" (LLM Architecture Gallery), section "How IndexShare Works",
+ * with k as in "GLM-5.2 and IndexShare for Long-Context Sparse Attention",
+ * section "Where the DSA indexer becomes expensive"): scores[(b*n_q + t)*ld + s] for
  * s <= p = q_start + t, or seq_q_start[b] + t (entries beyond p are ignored).  Same selection rule
  * and output layout as ix_indexer_topk.  ld >= kv_len.  Scores must not be
  * NaN.  Calls with few long rows (B*n_q < 1024 and q_start + n_q > k) keep

@@ -23,18 +23,19 @@ import torch
 
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
-    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys", "lib_path",
+    "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys",
+    "ix_indexer_argmax", "lib_path",
     "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
 IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
 IX_PATH_AUTO, IX_PATH_FUSED, IX_PATH_MATERIALIZED = 0, 1, 2
-IX_OP_INDEXER_TOPK, IX_OP_SPARSE_ATTN, IX_OP_GROUP_FORWARD, IX_OP_TOPK_SCORES = 1, 2, 3, 4
+IX_OP_INDEXER_TOPK, IX_OP_SPARSE_ATTN, IX_OP_GROUP_FORWARD, IX_OP_TOPK_SCORES, IX_OP_INDEXER_ARGMAX = 1, 2, 3, 4, 5
 
 
 class Problem(ctypes.Structure):
@@ -93,6 +94,9 @@ def load():
     lib.ix_indexer_topk.restype = c_int32
     lib.ix_indexer_topk.argtypes = [POINTER(Problem), POINTER(IndexerIn), c_void_p, c_void_p,
                                     c_size_t, c_void_p]
+    lib.ix_indexer_argmax.restype = c_int32
+    lib.ix_indexer_argmax.argtypes = [POINTER(Problem), POINTER(IndexerIn), c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]
     lib.ix_sparse_attn.restype = c_int32
     lib.ix_sparse_attn.argtypes = [POINTER(Problem), POINTER(AttnIn), c_void_p, c_void_p, c_size_t,
                                    c_void_p]
@@ -145,13 +149,31 @@ def _stream(stream):
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device):
+def _torch_stream(stream, device):
+    """The torch stream object a call enqueues on (current stream by default)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _workspace(nbytes: int, device, stream=None):
+    """A workspace of at least nbytes for calls on (device, stream).  One
+    buffer is cached per (device, stream) and allocated on that stream, so
+    calls on different streams never share bytes, and when a larger request
+    replaces a buffer the caching allocator hands its block out again only
+    after the work already queued on that stream."""
     if nbytes == 0:
         return None, 0
-    key = torch.device(device).index
+    dev = torch.device(device)
+    s = _torch_stream(stream, dev)
+    key = (dev.index, s.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache.pop(key, None)
+        with torch.cuda.stream(s):
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf, nbytes
 
@@ -236,9 +258,29 @@ def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=None, kv_len=None,
     prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2],
                     seq_q_start)
     desc = _indexer_in(q, w, keys, k_scale, path)
-    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, desc), q.device)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, desc), q.device, stream)
     _check(lib.ix_indexer_topk(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
                                _stream(stream)), "ix_indexer_topk")
+
+
+def ix_indexer_argmax(q, w, keys, pos, score=None, *, k_scale=None, q_start=None, kv_len=None,
+                      seq_q_start=None, stream=None):
+    """Top-1 of the indexer scores (see ix.h): ``pos`` int32 [B, n_q] gets each
+    row's best position, ``score`` (fp32 [B, n_q], optional) its score."""
+    lib = load()
+    _dev(pos, "pos")
+    _need(pos.dtype == torch.int32 and tuple(pos.shape) == tuple(q.shape[:2]), "pos must be int32 [B, n_q]")
+    if score is not None:
+        _dev(score, "score")
+        _need(score.dtype == torch.float32 and tuple(score.shape) == tuple(q.shape[:2]),
+              "score must be fp32 [B, n_q]")
+    cap = keys.shape[1]
+    q_start = _starts(seq_q_start, q_start, q.shape[0])
+    prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, 1, seq_q_start)
+    desc = _indexer_in(q, w, keys, k_scale, IX_PATH_AUTO)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_ARGMAX, desc), q.device, stream)
+    _check(lib.ix_indexer_argmax(ctypes.byref(prob), ctypes.byref(desc), _ptr(pos), _ptr(score), _ptr(ws), nb,
+                                 _stream(stream)), "ix_indexer_argmax")
 
 
 def ix_sparse_attn(q, kv, idx, out, *, lse=None, q_start=0, kv_len=None, sm_scale=0.0, kv_splits=0,
@@ -250,7 +292,7 @@ def ix_sparse_attn(q, kv, idx, out, *, lse=None, q_start=0, kv_len=None, sm_scal
     cap = kv.shape[1]
     prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2])
     desc = _attn_in(q, kv, out, lse, sm_scale, kv_splits)
-    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_SPARSE_ATTN, desc), q.device)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_SPARSE_ATTN, desc), q.device, stream)
     _check(lib.ix_sparse_attn(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
                               _stream(stream)), "ix_sparse_attn")
 
@@ -285,7 +327,7 @@ def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=N
         _need(a["q"].shape[:2] == a0["q"].shape[:2] and a["kv"].shape[1] == cap, "layers must share sizes")
         att[l] = _attn_in(a["q"], a["kv"], a["out"], a.get("lse"), sm_scale, kv_splits)
     gd = GroupDesc(n, 0, f_mask, ixr, att)
-    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_GROUP_FORWARD, gd), a0["q"].device)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_GROUP_FORWARD, gd), a0["q"].device, stream)
     _check(lib.ix_group_forward(ctypes.byref(prob), n, f_mask, ixr, att, _ptr(idx), _ptr(ws), nb,
                                 _stream(stream)), "ix_group_forward")
 
@@ -301,7 +343,7 @@ def ix_topk_scores(scores, idx, *, q_start=None, kv_len=None, seq_q_start=None, 
     q_start = _starts(seq_q_start, q_start, scores.shape[0])
     prob = _problem(scores.shape[0], scores.shape[1], q_start, ld if kv_len is None else kv_len,
                     ld if kv_len is None else kv_len, idx.shape[2], seq_q_start)
-    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_TOPK_SCORES, None), scores.device)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_TOPK_SCORES, None), scores.device, stream)
     _check(lib.ix_topk_scores(ctypes.byref(prob), _ptr(scores), ld, _ptr(idx), _ptr(ws), nb,
                               _stream(stream)), "ix_topk_scores")
 

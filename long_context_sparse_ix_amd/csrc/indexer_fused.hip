@@ -37,6 +37,13 @@
 //     an exact radix select;
 //   * at the end an exact radix select (score desc, position asc) picks the k
 //     winners and a stable pass writes their positions in ascending order.
+//
+// The same kernel with SELECT = false keeps only a running maximum per lane
+// instead of the candidate buffer: the row's best position (equal scores:
+// lower position) and its score, i.e. the top-1 under the same rule.  It
+// streams the same scores through the same tile ring and MFMA pipeline, so
+// its time is the score stream's alone and the difference to the full kernel
+// is what the streaming top-k costs.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -339,7 +346,7 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
   return part;
 }
 
-template <int HT, int KS, bool SCALE>
+template <int HT, int KS, bool SCALE, bool SELECT>
 __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedArgs a) {
   using G = TileGeom<KS>;
   constexpr int d = G::d;
@@ -427,6 +434,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
 
   float tau = -INFINITY, vmax = -INFINITY, vmin = INFINITY;
   int cnt = 0;
+  float best_s = -INFINITY;                     // SELECT == false: this lane's running maximum
+  int best_p = -1;
   // Shrinks happen at pair boundaries, together: a pair appends at most 128
   // entries per row, so a row needs one when it holds more than C - 128; then
   // every row of the workgroup past `join` shrinks in the same step.  The rows
@@ -477,17 +486,22 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       if (SCALE) score *= sc_prev;
       const int s = (it - 1) * kTileKeys + l;
       if (s > p) score = -INFINITY;
-      const bool pass = score > tau;             // room for 64: see the shrink below
-      const uint64_t pm = __ballot(pass);
-      if (pm) {
-        if (pass) {
-          const int o = cnt + wave_prefix(pm);
-          cand.s[o] = score;
-          cand.p[o] = s;
-          vmax = fmaxf(vmax, score);              // per lane; reduced when a shrink needs it
-          vmin = fminf(vmin, score);
+      if constexpr (SELECT) {
+        const bool pass = score > tau;           // room for 64: see the shrink below
+        const uint64_t pm = __ballot(pass);
+        if (pm) {
+          if (pass) {
+            const int o = cnt + wave_prefix(pm);
+            cand.s[o] = score;
+            cand.p[o] = s;
+            vmax = fmaxf(vmax, score);            // per lane; reduced when a shrink needs it
+            vmin = fminf(vmin, score);
+          }
+          cnt += __popcll(pm);
         }
-        cnt += __popcll(pm);
+      } else if (score > best_s) {               // keys arrive in ascending position:
+        best_s = score;                          // strict > keeps the lowest of equal scores
+        best_p = s;
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
@@ -497,16 +511,32 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   for (int it = 0, parity = 0; it <= n_tiles; it += 2, parity ^= 1) {
     step(it, true);
     if (it + 1 <= n_tiles) step(it + 1, false);
-    // post this row's fill; the slots alternate by pair so that a wave
-    // already in the next pair cannot overwrite a fill still being read
-    if (l == 0) fill_lds[parity * kRowsPerWG + wave] = cnt;
+    if constexpr (SELECT) {
+      // post this row's fill; the slots alternate by pair so that a wave
+      // already in the next pair cannot overwrite a fill still being read
+      if (l == 0) fill_lds[parity * kRowsPerWG + wave] = cnt;
+    }
     wait_vmcnt<0>();                             // the next pair landed
     lds_barrier();
-    const int4 f = *reinterpret_cast<const int4*>(fill_lds + parity * kRowsPerWG);
-    const int fullest = max(max(f.x, f.y), max(f.z, f.w));
-    if (fullest > C - 2 * kWave && cnt > join) shrink(cand, cnt, tau, vmax, vmin, a.k, keep_max, my_hist);
+    if constexpr (SELECT) {
+      const int4 f = *reinterpret_cast<const int4*>(fill_lds + parity * kRowsPerWG);
+      const int fullest = max(max(f.x, f.y), max(f.z, f.w));
+      if (fullest > C - 2 * kWave && cnt > join) shrink(cand, cnt, tau, vmax, vmin, a.k, keep_max, my_hist);
+    }
   }
 
+  if constexpr (!SELECT) {
+    // the row's best: the largest lane maximum, the lowest position among
+    // lanes holding it (every row has its own key, so some lane holds one)
+    const float bs = wave_max_f(best_s);
+    const int bp = (int)wave_min_u32(best_s == bs ? (uint32_t)best_p : 0xFFFFFFFFu);
+    if (row_ok && l == 0) {
+      const int64_t r = (int64_t)b * a.n_q + t;
+      a.idx[r] = bp;
+      if (a.best) a.best[r] = bs;
+    }
+    return;
+  }
   if (row_ok) {
     int32_t* dst = a.idx + ((int64_t)b * a.n_q + t) * a.k;
     wait_vmcnt<0>();
@@ -556,20 +586,20 @@ __global__ void stage_keys_kernel(const void* __restrict__ src, int fp8, int64_t
   }
 }
 
-template <int HT, int KS, bool SCALE>
+template <int HT, int KS, bool SCALE, bool SELECT>
 hipError_t launch_fused_s(const FusedArgs& a, int B, hipStream_t s) {
   const size_t lds = fused_lds_bytes(KS * 16);
-  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE>);
+  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE, SELECT>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((a.n_q + kRowsPerWG - 1) / kRowsPerWG, B);
-  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS, SCALE>), grid, dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS, SCALE, SELECT>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int HT, int KS>
+template <int HT, int KS, bool SELECT>
 hipError_t launch_fused_t(const FusedArgs& a, int B, hipStream_t s) {
-  return a.scale ? launch_fused_s<HT, KS, true>(a, B, s) : launch_fused_s<HT, KS, false>(a, B, s);
+  return a.scale ? launch_fused_s<HT, KS, true, SELECT>(a, B, s) : launch_fused_s<HT, KS, false, SELECT>(a, B, s);
 }
 
 }  // namespace
@@ -586,15 +616,24 @@ size_t fused_lds_bytes(int d) {
 
 bool fused_dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s) {
+template <bool SELECT>
+hipError_t launch_fused_sel(const FusedArgs& a, int B, int d, hipStream_t s) {
   const int HT = a.H > 32 ? 2 : 1;
   const int KS = d / 16;
 #define IX_FUSED_CASE(ht, ks) \
-  if (HT == ht && KS == ks) return launch_fused_t<ht, ks>(a, B, s);
+  if (HT == ht && KS == ks) return launch_fused_t<ht, ks, SELECT>(a, B, s);
   IX_FUSED_CASE(1, 1) IX_FUSED_CASE(1, 2) IX_FUSED_CASE(1, 4) IX_FUSED_CASE(1, 8)
   IX_FUSED_CASE(2, 1) IX_FUSED_CASE(2, 2) IX_FUSED_CASE(2, 4) IX_FUSED_CASE(2, 8)
 #undef IX_FUSED_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s) {
+  return launch_fused_sel<true>(a, B, d, s);
+}
+
+hipError_t launch_fused_argmax(const FusedArgs& a, int B, int d, hipStream_t s) {
+  return launch_fused_sel<false>(a, B, d, s);
 }
 
 hipError_t launch_stage_keys(const void* src, bool fp8, int64_t src_bstride, const float* scale,

@@ -105,6 +105,10 @@ size_t stage_scale_bytes(const ix_problem* p, const ix_indexer_in* in) {
                                              : 0;
 }
 
+size_t argmax_ws(const ix_problem* p, const ix_indexer_in* in) {
+  return stage_key_bytes(p, in) + stage_scale_bytes(p, in);
+}
+
 size_t indexer_ws(const ix_problem* p, const ix_indexer_in* in) {
   if (use_fused(p, in)) return fused_cand_bytes(p) + stage_key_bytes(p, in) + stage_scale_bytes(p, in);
   return score_bytes(p) + rng_bytes(p) + topk_ws(p);
@@ -149,33 +153,44 @@ int32_t hip_fail(hipError_t e) {
   return IX_E_HIP;
 }
 
+// Stages the keys (widened to bf16) and fp8 scales into padded copies at
+// `stage` and fills the fused kernel's key fields.
+hipError_t stage_fused_keys(const ix_problem* p, const ix_indexer_in* in, char* stage, ix::FusedArgs& a,
+                            hipStream_t s) {
+  const bool fp8 = in->k_dtype == IX_DTYPE_FP8_E4M3FN;
+  const int64_t rows_pad = p->kv_len + ix::kStagePad;
+  uint16_t* kb = reinterpret_cast<uint16_t*>(stage);
+  float* sb = fp8 ? reinterpret_cast<float*>(stage + stage_key_bytes(p, in)) : nullptr;
+  a.keys = kb;
+  a.key_bstride = rows_pad * in->dim;
+  a.scale = sb;
+  a.scale_bstride = fp8 ? rows_pad : 0;
+  return ix::launch_stage_keys(in->k, fp8, p->kv_cap * in->dim, in->k_scale, p->kv_cap, kb, sb, p->batch,
+                               p->kv_len, rows_pad, in->dim, s);
+}
+
+ix::FusedArgs fused_args(const ix_problem* p, const ix_indexer_in* in, int32_t* idx) {
+  ix::FusedArgs a{};
+  a.q = static_cast<const uint16_t*>(in->q);
+  a.w = in->w;
+  a.idx = idx;
+  a.q_start = p->q_start;
+  a.seq_q_start = p->seq_q_start;
+  a.n_q = p->n_q;
+  a.H = in->heads;
+  a.k = p->k;
+  return a;
+}
+
 int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, void* ws,
                     hipStream_t s) {
   const bool fp8 = in->k_dtype == IX_DTYPE_FP8_E4M3FN;
   if (use_fused(p, in)) {
-    ix::FusedArgs a{};
-    a.q = static_cast<const uint16_t*>(in->q);
-    a.w = in->w;
-    a.idx = idx;
-    a.q_start = p->q_start;
-    a.seq_q_start = p->seq_q_start;
-    a.n_q = p->n_q;
-    a.H = in->heads;
-    a.k = p->k;
+    ix::FusedArgs a = fused_args(p, in, idx);
     a.C = ix::fused_candidates(p->k);
     a.cand = static_cast<float2*>(ws);
-    // keys (widened to bf16) and scales staged into padded workspace copies
-    const int64_t rows_pad = p->kv_len + ix::kStagePad;
-    char* stage = static_cast<char*>(ws) + fused_cand_bytes(p);
-    uint16_t* kb = reinterpret_cast<uint16_t*>(stage);
-    float* sb = fp8 ? reinterpret_cast<float*>(stage + stage_key_bytes(p, in)) : nullptr;
-    hipError_t e = ix::launch_stage_keys(in->k, fp8, p->kv_cap * in->dim, in->k_scale, p->kv_cap, kb, sb,
-                                         p->batch, p->kv_len, rows_pad, in->dim, s);
+    hipError_t e = stage_fused_keys(p, in, static_cast<char*>(ws) + fused_cand_bytes(p), a, s);
     if (e != hipSuccess) return hip_fail(e);
-    a.keys = kb;
-    a.key_bstride = rows_pad * in->dim;
-    a.scale = sb;
-    a.scale_bstride = fp8 ? rows_pad : 0;
     e = ix::launch_fused_indexer(a, p->batch, in->dim, s);
     return e == hipSuccess ? IX_OK : hip_fail(e);
   }
@@ -317,6 +332,10 @@ size_t ix_workspace_bytes(const ix_problem* p, int32_t op, const void* desc) {
     }
     case IX_OP_TOPK_SCORES:
       return topk_ws(p);
+    case IX_OP_INDEXER_ARGMAX: {
+      auto in = static_cast<const ix_indexer_in*>(desc);
+      return check_indexer(p, in) == IX_OK && ix::fused_dim_supported(in->dim) ? argmax_ws(p, in) : 0;
+    }
     default:
       return 0;
   }
@@ -332,6 +351,26 @@ int32_t ix_indexer_topk(const ix_problem* p, const ix_indexer_in* in, int32_t* i
   st = check_ws(indexer_ws(p, in), ws, ws_bytes);
   if (st != IX_OK) return st;
   return run_indexer(p, in, idx, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t ix_indexer_argmax(const ix_problem* p, const ix_indexer_in* in, int32_t* pos, float* score, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st == IX_OK) st = check_indexer(p, in);
+  if (st != IX_OK) return st;
+  if (!pos) return IX_E_NULL;
+  if (!ix::fused_dim_supported(in->dim) || in->path == IX_PATH_MATERIALIZED) return IX_E_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(pos) & 3u) != 0 || (reinterpret_cast<uintptr_t>(score) & 3u) != 0)
+    return IX_E_SHAPE;
+  st = check_ws(argmax_ws(p, in), ws, ws_bytes);
+  if (st != IX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ix::FusedArgs a = fused_args(p, in, pos);
+  a.best = score;
+  hipError_t e = stage_fused_keys(p, in, static_cast<char*>(ws), a, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = ix::launch_fused_argmax(a, p->batch, in->dim, s);
+  return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
 int32_t ix_sparse_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, void* ws,

@@ -13,7 +13,8 @@ struct FusedArgs {
   const float* w;         // [B][n_q][H]
   const uint16_t* keys;   // bf16 rows, row stride d, sequence stride key_bstride
   const float* scale;     // per-key fp32 scale, or nullptr
-  int32_t* idx;           // [B][n_q][k]
+  int32_t* idx;           // [B][n_q][k]; the argmax variant: [B][n_q] best positions
+  float* best;            // argmax variant: [B][n_q] best scores (nullable)
   float2* cand;           // workspace: per row C fp32 scores then C int32 positions (C float2 of room)
   int64_t key_bstride;    // elements
   int64_t scale_bstride;  // elements
@@ -25,6 +26,10 @@ size_t fused_lds_bytes(int d);
 bool fused_dim_supported(int d);   // d in {16, 32, 64, 128}
 int fused_candidates(int k);
 hipError_t launch_fused_indexer(const FusedArgs& a, int B, int d, hipStream_t s);
+// The same score stream with a running maximum instead of the top-k: idx[row]
+// = the row's best position (equal scores: lower), best[row] = its score.
+// Uses neither cand nor C nor k.
+hipError_t launch_fused_argmax(const FusedArgs& a, int B, int d, hipStream_t s);
 
 // e4m3fn codes -> bf16 (exact), rows [0, rows) of every sequence.
 // Key staging for the fused indexer: the first `rows` key rows of every

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
             "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
-            "ix_index_overlap", "ix_append_keys"} <= set(names)
+            "ix_index_overlap", "ix_append_keys", "ix_indexer_argmax"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -165,6 +165,26 @@ def test_group_role_mask_validation():
     assert lib.ix_group_forward(ctypes.byref(p), 4, 1, ixr2, att, DUMMY, None, 0, None) == ix.IX_E_WORKSPACE
 
 
+def test_indexer_argmax_validation():
+    """The top-1 entry point: fused path only, outputs 4-byte aligned, the
+    staged-key workspace checked before anything is enqueued."""
+    lib = ensure_lib()
+    p = _prob(n_q=256, kv_len=256, kv_cap=256)
+    call = lambda d, pos=DUMMY, score=None, ws=None, nb=0: lib.ix_indexer_argmax(
+        ctypes.byref(p), ctypes.byref(d), pos, score, ws, nb, None)
+    assert call(_ixr(), pos=None) == ix.IX_E_NULL
+    assert call(_ixr(q=None)) == ix.IX_E_NULL
+    assert call(_ixr(dim=48)) == ix.IX_E_SHAPE           # no fused kernel for d = 48
+    assert call(_ixr(path=ix.IX_PATH_MATERIALIZED)) == ix.IX_E_SHAPE
+    assert call(_ixr(), pos=DUMMY + 2) == ix.IX_E_SHAPE
+    assert call(_ixr(), score=DUMMY + 1) == ix.IX_E_SHAPE
+    assert call(_ixr()) == ix.IX_E_WORKSPACE
+    need = ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_ARGMAX, _ixr())
+    assert need >= (256 + 64) * 32 * 2                  # the bf16 key copy, one tile of padding
+    assert call(_ixr(), ws=None, nb=need) == ix.IX_E_NULL
+    assert ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_ARGMAX, _ixr(dim=48)) == 0
+
+
 def test_topk_scores_validation():
     lib = ensure_lib()
     p = _prob()
@@ -175,7 +195,7 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 3
+    assert ix.ix_abi_version() == 4
 
 
 def test_index_overlap_validation():

@@ -17,6 +17,10 @@ from oracle import dsa_oracle as O
 pytestmark = pytest.mark.gpu
 
 ATOL = 2e-2
+# float mode: summed set overlap >= 99.9% (the bar), and no row may lose more
+# than 0.5% of its slots (fp32 accumulation on the GPU against float64 in the
+# oracle only swaps entries that tie the k-th score to within rounding)
+OVERLAP_MIN, OVERLAP_ROW_MIN = 0.999, 0.995
 
 
 @pytest.fixture(scope="module")
@@ -89,15 +93,15 @@ def check_group(w, ixl, atl, idx, rows, b=0, exact=False):
                 np.testing.assert_array_equal(got, ref)
             else:
                 ov, worst = overlap(got, ref)
-                print(f"  layer {l}: overlap {ov:.6f} worst {worst:.4f}")
-                assert ov >= 0.999
+                print(f"  layer {l}: overlap {ov:.6f} worst row {worst:.4f} over {len(rows)} rows", flush=True)
+                assert ov >= OVERLAP_MIN and worst >= OVERLAP_ROW_MIN
         a = atl[l]
         gidx = host(idx[f, b:b + 1, rows])
         ref_o, ref_lse = O.sparse_attention(bits16(a["q"][b:b + 1, rows]), bits16(a["kv"][b:b + 1]), gidx,
                                             w.kv_len, 1.0 / math.sqrt(w.d_qk), w.d_v)
         err = np.abs(a["out"][b:b + 1, rows].float().cpu().numpy() - ref_o).max()
         lerr = np.abs(host(a["lse"][b:b + 1, rows]) - ref_lse).max()
-        print(f"  layer {l}: attention max-abs {err:.2e} lse {lerr:.2e}")
+        print(f"  layer {l}: attention max-abs {err:.2e} lse {lerr:.2e}", flush=True)
         assert err <= ATOL and lerr <= 1e-3
 
 
@@ -105,7 +109,7 @@ def test_prefill_l16k_group(ix):
     w = synth.L16K
     ixl, atl, idx = run_group(ix, w, w.roles)
     device_idx_invariants(idx[0], w.q_start, w.k)
-    check_group(w, ixl, atl, idx, synth.sample_rows(w, 16))
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 64))
 
 
 def test_prefill_l16k_exact_indices(ix):
@@ -115,7 +119,7 @@ def test_prefill_l16k_exact_indices(ix):
     idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
     ix.ix_indexer_topk(q, wt, keys, idx, q_start=0, kv_len=w.kv_len)
     torch.cuda.synchronize()
-    rows = synth.sample_rows(w, 16)
+    rows = synth.sample_rows(w, 64)
     np.testing.assert_array_equal(host(idx[0, rows]),
                                   oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=None), rows))
 
@@ -126,7 +130,7 @@ def test_prefill_l128k_group(ix):
     w = synth.L128K
     ixl, atl, idx = run_group(ix, w, "FSSS")
     device_idx_invariants(idx[0], w.q_start, w.k)
-    check_group(w, ixl, atl, idx, synth.sample_rows(w, 10))
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 64))
 
 
 def test_prefill_l128k_exact_indices(ix):
@@ -136,7 +140,7 @@ def test_prefill_l128k_exact_indices(ix):
     idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
     ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=0, kv_len=w.kv_len)
     torch.cuda.synchronize()
-    rows = synth.sample_rows(w, 8)
+    rows = synth.sample_rows(w, 64)
     np.testing.assert_array_equal(host(idx[0, rows]),
                                   oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=scale), rows))
 
@@ -145,7 +149,7 @@ def test_chunked_prefill_1m(ix):
     w = synth.CHUNK_1M
     ixl, atl, idx = run_group(ix, w, w.roles)
     device_idx_invariants(idx[0], w.q_start, w.k)
-    check_group(w, ixl, atl, idx, synth.sample_rows(w, 6))
+    check_group(w, ixl, atl, idx, synth.sample_rows(w, 64))
 
 
 def test_chunked_prefill_1m_exact_indices(ix):
@@ -155,20 +159,20 @@ def test_chunked_prefill_1m_exact_indices(ix):
     idx = torch.empty((1, w.n_q, w.k), dtype=torch.int32, device="cuda")
     ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len)
     torch.cuda.synchronize()
-    rows = [0, 4095, 8191]
+    rows = synth.sample_rows(w, 24)
     np.testing.assert_array_equal(host(idx[0, rows]),
                                   oracle_idx(w, dict(q=q, w=wt, keys=keys, k_scale=scale), rows))
 
 
-@pytest.mark.parametrize("step", [0, 63])
+@pytest.mark.parametrize("step", [0, 31, 63])
 def test_decode_b32_step(ix, step):
     """Decode: 32 sequences with a 200,000-token cache, one new query each;
-    step j sees kv_len = 200,001 + j."""
+    step j sees kv_len = 200,001 + j.  Every sequence is checked."""
     base = synth.DECODE_B32
     w = base.with_(q_start=base.q_start + step, kv_len=base.kv_len + step)
     ixl, atl, idx = run_group(ix, w, base.roles, step=step)
     device_idx_invariants(idx[0], w.q_start, w.k)
-    for b in (0, 13, 31):
+    for b in range(w.batch):
         check_group(w, ixl, atl, idx, [0], b=b)
 
 
@@ -179,5 +183,5 @@ def test_decode_b32_exact_indices(ix):
     idx = torch.empty((32, 1, base.k), dtype=torch.int32, device="cuda")
     ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=base.q_start, kv_len=base.kv_len)
     torch.cuda.synchronize()
-    for b in (0, 17, 31):
+    for b in range(base.batch):
         np.testing.assert_array_equal(host(idx[b]), oracle_idx(base, dict(q=q, w=wt, keys=keys, k_scale=scale), [0], b))

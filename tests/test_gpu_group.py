@@ -122,3 +122,43 @@ def test_decode_shape_group(ix):
         ref, _ = O.sparse_attention(bits16(atl[l]["q"]), bits16(atl[l]["kv"]), host(idx[0]), w.kv_len,
                                     1.0 / math.sqrt(w.d_qk), w.d_v)
         assert np.abs(atl[l]["out"].float().cpu().numpy() - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("roles", ["FFSS", "FSFS", "FFFSSS", "FFSSSFSFSSS", "FSSSSSSF"])
+def test_irregular_masks_against_oracle(ix, roles):
+    """Masks with full layers after shared ones and irregular starts (the
+    released pattern repeats F,S,S,S after a few initial exceptions: "GLM-5.2
+    and IndexShare for Long-Context Sparse Attention", section "What IndexShare
+    reuses"; any F/S assignment is allowed: "IndexShare", section "Why Reusing
+    Indices Can Work").  Each F layer's slot is bit-exact against the oracle
+    (exact mode), every layer attends over the slot of the most recent F layer
+    (the oracle's `used` map), byte for byte as a standalone call over that
+    slot, and its output is within 2e-2 of the oracle's."""
+    w = synth.TINY_L1K.with_(name=f"mask_{roles}", n_q=300, kv_len=300, k=48)
+    ixl, atl = _layers(w, roles)
+    idx = _group(ix, w, roles, ixl, atl)
+    ix_in, at_in = [], []
+    for l, r in enumerate(roles):
+        e = ixl[l]
+        if r == "F":
+            kb, kd = key_bytes(e["keys"])
+            ix_in.append((bits16(e["q"]), host(e["w"]), kb, kd, host(e["k_scale"])))
+        else:
+            ix_in.append(None)
+        at_in.append((bits16(atl[l]["q"]), bits16(atl[l]["kv"])))
+    rows = list(range(0, w.n_q, 3)) + [w.n_q - 1]
+    ref = O.group_forward(roles, ix_in, at_in, w.q_start, w.kv_len, w.k, 1.0 / math.sqrt(w.d_qk), w.d_v,
+                          rows=rows)
+    assert ref["n_indexer_runs"] == roles.count("F")
+    expect_used = [roles[:l + 1].count("F") - 1 for l in range(len(roles))]
+    assert ref["used"] == expect_used
+    for f in range(roles.count("F")):
+        np.testing.assert_array_equal(host(idx[f])[:, rows], ref["idx"][f], err_msg=f"slot {f}")
+    for l in range(len(roles)):
+        solo = torch.empty_like(atl[l]["out"])
+        ix.ix_sparse_attn(atl[l]["q"], atl[l]["kv"], idx[expect_used[l]], solo, q_start=w.q_start,
+                          kv_len=w.kv_len)
+        torch.cuda.synchronize()
+        assert torch.equal(solo, atl[l]["out"]), f"layer {l} did not attend over slot {expect_used[l]}"
+        err = np.abs(atl[l]["out"].float().cpu().numpy()[:, rows] - ref["O"][l]).max()
+        assert err <= 2e-2, (l, err)
