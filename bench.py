@@ -209,13 +209,25 @@ def _worker_init():
 
 
 def _task_indexer(job):
-    """Oracle indexer + top-k of some query rows of one sequence."""
+    """Oracle indexer + top-k of some query rows of one sequence: the keys the
+    rows reach are decoded once (O.key_matrix), then each row is scored
+    (O.indexer_scores) and selected (O.select_topk), as O.indexer_topk does
+    for a whole sequence.  Returns the rows' indices and the task's time, its
+    decode time and decoded key rows, and its per-row time."""
+    import numpy as np
     from oracle import dsa_oracle as O
     t0 = time.perf_counter()
-    res = O.indexer_topk_rows(job["q"], job["w"], _mm(job["keys"]), job["kd"],
-                              None if job["scale"] is None else _mm(job["scale"]), job["pos"], job["kv_len"],
-                              job["k"])
-    return job["tag"], res, time.perf_counter() - t0
+    n_dec = min(max(job["pos"]), job["kv_len"] - 1) + 1
+    sc = None if job["scale"] is None else _mm(job["scale"])[:n_dec]
+    kmat = O.key_matrix(_mm(job["keys"])[:n_dec], job["kd"], sc)
+    t1 = time.perf_counter()
+    res = np.full((len(job["pos"]), job["k"]), -1, dtype=np.int32)
+    for i, p in enumerate(job["pos"]):
+        n = min(p, job["kv_len"] - 1) + 1
+        s = O.indexer_scores(O.decode_bf16(job["q"][i]), np.asarray(job["w"][i], np.float64), kmat[:n])
+        res[i] = O.select_topk(s, job["k"])
+    t2 = time.perf_counter()
+    return job["tag"], res, t2 - t0, t1 - t0, n_dec, t2 - t1
 
 
 def _task_attention(job):
@@ -320,9 +332,11 @@ def cpu_baseline(w, inp, torch, rows, pool):
             kpath = pool.put(kb)
             spath = None if e["k_scale"] is None else pool.put(e["k_scale"][0].cpu().numpy())
             q, wt = bits(e["q"][0, rows_t]), e["w"][0, rows_t].cpu().numpy()
-            # two rows per job, the longest first so the pool drains evenly
+            # one job per worker, rows dealt round-robin from the longest so
+            # the jobs carry similar work
             order = sorted(range(len(rows)), key=lambda i: -rows[i])
-            for grp in _chunks(order, 2):
+            for j in range(min(pool.n, len(rows))):
+                grp = order[j::pool.n]
                 ix_jobs.append(dict(tag=(f, grp), q=q[grp], w=wt[grp], keys=kpath, kd=kd, scale=spath,
                                     pos=[w.q_start + rows[i] for i in grp], kv_len=w.kv_len, k=w.k))
         a = inp.attn[l]
@@ -337,16 +351,23 @@ def cpu_baseline(w, inp, torch, rows, pool):
     at_res, at_wall, at_sum = pool.run(_task_attention, at_jobs)
     n_f = w.roles.count("F")
     idx_oracle = [np.full((len(rows), w.k), -1, np.int32) for _ in range(n_f)]
-    for (fi, grp), res, _ in ix_res:
+    for (fi, grp), res, *_ in ix_res:
         idx_oracle[fi][grp] = res
     outs = [np.zeros((len(rows), w.q_heads, w.d_v)) for _ in range(w.n_layers)]
     for (l, r0, r1), o, _ in at_res:
         outs[l][r0:r1] = o[:, 0]
-    samp_pairs = sum(w.q_start + t + 1 for t in rows) * w.batch
-    samp_rows = sum(min(w.k, w.q_start + t + 1) for t in rows) * w.batch
-    full_s = ix_wall * causal_pairs(w) / samp_pairs + at_wall * gathered_rows(w) / samp_rows
-    return dict(t_ix=ix_wall, t_at=at_wall, t_sum=ix_sum + at_sum, full_s=full_s, idx=idx_oracle, O=outs,
-                n_f=n_f, samp_rows=len(rows))
+    # whole step in worker seconds: each full layer decodes every key row once
+    # (at the sample's decode rate), each row costs its sample rate times its
+    # candidates (indexer) or min(k, candidates) (attention); the rows are
+    # independent, so the pool's wall time is that over its workers
+    samp_pairs = sum(w.q_start + t + 1 for t in rows)
+    samp_rows = sum(min(w.k, w.q_start + t + 1) for t in rows)
+    dec_s = sum(r[3] for r in ix_res) / sum(r[4] for r in ix_res)        # seconds per decoded key row
+    row_s = sum(r[5] for r in ix_res) / n_f
+    full_worker_s = (n_f * w.batch * w.kv_len * dec_s + n_f * row_s * causal_pairs(w) / samp_pairs
+                     + at_sum * gathered_rows(w) / samp_rows)
+    return dict(t_ix=ix_wall, t_at=at_wall, t_sum=ix_sum + at_sum, full_s=full_worker_s / pool.n,
+                full_worker_s=full_worker_s, idx=idx_oracle, O=outs, n_f=n_f, samp_rows=len(rows))
 
 
 def sampled_parity(w, inp, rows, cb, torch):
@@ -547,8 +568,9 @@ def run(args, pool):
             f"{len(rows)} query rows of {w.n_q} (first and last rows, rows with k-1, k, k+1 candidates, "
             f"the rest seeded-uniform) through all {w.n_layers} layers (indexer + top-k on {cb['n_f']} full "
             f"layers, attention given the GPU's indices): {cb['t_ix'] + cb['t_at']:.1f} s wall on the pool "
-            f"({cb['t_sum']:.1f} s of worker time), extrapolated to all rows by candidates per row (indexer) "
-            f"and min(k, candidates) (attention)")
+            f"({cb['t_sum']:.1f} s of worker time); extrapolated to the whole step ({cb['full_worker_s']:.0f} "
+            f"worker-s, spread over the {pool.n} workers) by one key decode per full layer and, per row, its "
+            f"candidates (indexer) or min(k, candidates) (attention)")
         parity = sampled_parity(w, inp, rows, cb, torch)
 
     topk_ms = ix_ms - am_ms
