@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 4
+#define IX_ABI_VERSION 5
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -148,7 +148,8 @@ typedef struct ix_group_desc {
 
 int32_t ix_abi_version(void);
 const char* ix_status_str(int32_t status);
-/* Text of the last IX_E_HIP failure on the calling thread ("" if none). */
+/* Text of the last IX_E_HIP failure on the calling thread, or of the last
+ * IX_E_WORKSPACE rejection by ix_group_forward_noalloc ("" if none). */
 const char* ix_last_error(void);
 
 /* Workspace bytes `op` needs for `prob` and its descriptor (0 if none).
@@ -219,6 +220,32 @@ int32_t ix_sparse_attn(const ix_problem* prob, const ix_attn_in* in, const int32
 int32_t ix_group_forward(const ix_problem* prob, int32_t n_layers, uint64_t f_mask,
                          const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch ix_group_forward_noalloc works in. */
+#define IX_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* ix_group_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * (a decode step is one group call), harnesses that forbid hipMalloc.  Same
+ * arguments, semantics and results (byte for byte) as ix_group_forward, whose
+ * kernels it runs; their workspace is instead a file-scope static __device__
+ * array of IX_NOALLOC_SCRATCH_BYTES (64 MiB) in the library, of which each
+ * GPU the library runs on holds one copy from load until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the first call on a device looks up that device's scratch
+ * address once (hipGetSymbolAddress, with the stream's device current).
+ * A call whose workspace would exceed the scratch -- ix_workspace_bytes(prob,
+ * IX_OP_GROUP_FORWARD, desc) > IX_NOALLOC_SCRATCH_BYTES, e.g. long prefills
+ * on the fused path -- returns IX_E_WORKSPACE before anything is enqueued,
+ * with the sizes in ix_last_error().  Every call on one GPU shares that GPU's
+ * scratch and its contents stay from the last call (no kernel of the group
+ * needs them zeroed: each writes its scratch before reading it); calls that
+ * overlap on one GPU -- concurrent streams, or threads -- race on it, so the
+ * caller must order them (e.g. one stream).  Other errors as
+ * ix_group_forward. */
+int32_t ix_group_forward_noalloc(const ix_problem* prob, int32_t n_layers, uint64_t f_mask,
+                                 const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx,
+                                 void* stream);
 
 /* The top-k step alone, over caller-provided fp32 score rows (the selection
  * of "IndexShare" (LLM Architecture Gallery), section "How IndexShare Works",

@@ -24,16 +24,17 @@ import torch
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
     "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys",
-    "ix_indexer_argmax", "lib_path",
+    "ix_indexer_argmax", "ix_group_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "lib_path",
     "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
 IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20          # IX_NOALLOC_SCRATCH_BYTES in ix.h
 IX_PATH_AUTO, IX_PATH_FUSED, IX_PATH_MATERIALIZED = 0, 1, 2
 IX_OP_INDEXER_TOPK, IX_OP_SPARSE_ATTN, IX_OP_GROUP_FORWARD, IX_OP_TOPK_SCORES, IX_OP_INDEXER_ARGMAX = 1, 2, 3, 4, 5
 
@@ -62,7 +63,7 @@ class GroupDesc(ctypes.Structure):
 class IxError(RuntimeError):
     def __init__(self, status: int, what: str):
         detail = ""
-        if status == IX_E_HIP and _lib is not None:
+        if _lib is not None and (status == IX_E_HIP or (status == IX_E_WORKSPACE and what.endswith("_noalloc"))):
             detail = ": " + _lib.ix_last_error().decode()
         super().__init__(f"{what}: {ix_status_str(status)}{detail}")
         self.status = status
@@ -103,6 +104,9 @@ def load():
     lib.ix_group_forward.restype = c_int32
     lib.ix_group_forward.argtypes = [POINTER(Problem), c_int32, c_uint64, POINTER(IndexerIn),
                                      POINTER(AttnIn), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ix_group_forward_noalloc.restype = c_int32
+    lib.ix_group_forward_noalloc.argtypes = [POINTER(Problem), c_int32, c_uint64, POINTER(IndexerIn),
+                                             POINTER(AttnIn), c_void_p, c_void_p]
     lib.ix_topk_scores.restype = c_int32
     lib.ix_topk_scores.argtypes = [POINTER(Problem), c_void_p, c_int64, c_void_p, c_void_p,
                                    c_size_t, c_void_p]
@@ -297,15 +301,8 @@ def ix_sparse_attn(q, kv, idx, out, *, lse=None, q_start=0, kv_len=None, sm_scal
                               _stream(stream)), "ix_sparse_attn")
 
 
-def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=None, kv_len=None,
-                     sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, seq_q_start=None, stream=None):
-    """One IndexShare layer group (see ix.h).
-
-    indexer_layers[l]: dict(q=, w=, keys=, k_scale=) for full layers (None for
-    shared ones); attn_layers[l]: dict(q=, kv=, out=, lse=).  Bit l of f_mask
-    marks layer l full.  idx: int32 [n_full, B, n_q, k].  ``seq_q_start`` as
-    in ix_indexer_topk."""
-    lib = load()
+def _group_args(indexer_layers, attn_layers, f_mask, idx, q_start, kv_len, sm_scale, kv_splits, path,
+                seq_q_start):
     n = len(attn_layers)
     _need(len(indexer_layers) == n, "one indexer entry per layer (None for shared layers)")
     _dev(idx, "idx")
@@ -326,10 +323,36 @@ def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=N
         a = attn_layers[l]
         _need(a["q"].shape[:2] == a0["q"].shape[:2] and a["kv"].shape[1] == cap, "layers must share sizes")
         att[l] = _attn_in(a["q"], a["kv"], a["out"], a.get("lse"), sm_scale, kv_splits)
+    return n, prob, ixr, att, a0["q"].device
+
+
+def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=None, kv_len=None,
+                     sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, seq_q_start=None, stream=None):
+    """One IndexShare layer group (see ix.h).
+
+    indexer_layers[l]: dict(q=, w=, keys=, k_scale=) for full layers (None for
+    shared ones); attn_layers[l]: dict(q=, kv=, out=, lse=).  Bit l of f_mask
+    marks layer l full.  idx: int32 [n_full, B, n_q, k].  ``seq_q_start`` as
+    in ix_indexer_topk."""
+    lib = load()
+    n, prob, ixr, att, dev = _group_args(indexer_layers, attn_layers, f_mask, idx, q_start, kv_len, sm_scale,
+                                         kv_splits, path, seq_q_start)
     gd = GroupDesc(n, 0, f_mask, ixr, att)
-    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_GROUP_FORWARD, gd), a0["q"].device, stream)
+    ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_GROUP_FORWARD, gd), dev, stream)
     _check(lib.ix_group_forward(ctypes.byref(prob), n, f_mask, ixr, att, _ptr(idx), _ptr(ws), nb,
                                 _stream(stream)), "ix_group_forward")
+
+
+def ix_group_forward_noalloc(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=None, kv_len=None,
+                             sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, seq_q_start=None, stream=None):
+    """ix_group_forward in the library's static scratch: no workspace is
+    allocated, by this binding or the library (see ix.h; calls that overlap
+    on one GPU race on the scratch)."""
+    lib = load()
+    n, prob, ixr, att, _ = _group_args(indexer_layers, attn_layers, f_mask, idx, q_start, kv_len, sm_scale,
+                                       kv_splits, path, seq_q_start)
+    _check(lib.ix_group_forward_noalloc(ctypes.byref(prob), n, f_mask, ixr, att, _ptr(idx), _stream(stream)),
+           "ix_group_forward_noalloc")
 
 
 def ix_topk_scores(scores, idx, *, q_start=None, kv_len=None, seq_q_start=None, stream=None):

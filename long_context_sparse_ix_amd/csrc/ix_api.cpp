@@ -10,10 +10,18 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "ix.h"
 #include "kernels.hpp"
+
+// Scratch of ix_group_forward_noalloc: device memory that exists without any
+// allocation call.  Each GPU the library runs on holds its own copy from
+// module load until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device address: that comes from
+// hipGetSymbolAddress, once per device (scratch_for_stream below).
+static __device__ __align__(256) unsigned char scratch[IX_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -276,6 +284,39 @@ size_t group_ws(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix
   return need;
 }
 
+// Device address of `scratch` on the device of `stream` (the current device
+// for the NULL stream), looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e);
+    if (e2 != hipSuccess) return hip_fail(e2);
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return IX_OK;
+}
+
+// Layers of a validated group in order on one stream, workspace ws.
+int32_t run_group(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix_indexer_in* ixr,
+                  const ix_attn_in* attn, int32_t* idx, void* ws, hipStream_t s);
+
 int32_t check_group(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
                     const ix_indexer_in* ixr, const ix_attn_in* attn) {
   if (n_layers < 1 || n_layers > 64) return IX_E_ROLES;
@@ -395,20 +436,27 @@ int32_t ix_group_forward(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
   if (!aligned16(idx)) return IX_E_SHAPE;
   st = check_ws(group_ws(p, n_layers, f_mask, ixr, attn), ws, ws_bytes);
   if (st != IX_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t slot = (size_t)p->batch * p->n_q * p->k;
-  int32_t* cur = nullptr;
-  int f = 0;
-  for (int l = 0; l < n_layers; ++l) {
-    if ((f_mask >> l) & 1u) {          // full layer: fresh positions into its own slot
-      cur = idx + slot * f++;
-      st = run_indexer(p, &ixr[l], cur, ws, s);
-      if (st != IX_OK) return st;
-    }
-    st = run_attn(p, &attn[l], cur, ws, s);   // shared layers reuse `cur` untouched
-    if (st != IX_OK) return st;
+  return run_group(p, n_layers, f_mask, ixr, attn, idx, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t ix_group_forward_noalloc(const ix_problem* p, int32_t n_layers, uint64_t f_mask,
+                                 const ix_indexer_in* ixr, const ix_attn_in* attn, int32_t* idx, void* stream) {
+  int32_t st = check_problem(p);
+  if (st == IX_OK) st = check_group(p, n_layers, f_mask, ixr, attn);
+  if (st != IX_OK) return st;
+  if (!idx) return IX_E_NULL;
+  if (!aligned16(idx)) return IX_E_SHAPE;
+  const size_t need = group_ws(p, n_layers, f_mask, ixr, attn);
+  if (need > (size_t)IX_NOALLOC_SCRATCH_BYTES) {
+    g_last_error = "ix_group_forward_noalloc: the call needs " + std::to_string(need) +
+                   " bytes of scratch, the static scratch holds " +
+                   std::to_string((size_t)IX_NOALLOC_SCRATCH_BYTES);
+    return IX_E_WORKSPACE;
   }
-  return IX_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_for_stream(s, &ws)) != IX_OK) return st;
+  return run_group(p, n_layers, f_mask, ixr, attn, idx, ws, s);
 }
 
 int32_t ix_topk_scores(const ix_problem* p, const float* scores, int64_t ld, int32_t* idx,
@@ -452,3 +500,24 @@ int32_t ix_append_keys(const ix_problem* p, int32_t dim, const float* k_new, int
 }
 
 }  // extern "C"
+
+namespace {
+
+int32_t run_group(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix_indexer_in* ixr,
+                  const ix_attn_in* attn, int32_t* idx, void* ws, hipStream_t s) {
+  const size_t slot = (size_t)p->batch * p->n_q * p->k;
+  int32_t* cur = nullptr;
+  int f = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((f_mask >> l) & 1u) {          // full layer: fresh positions into its own slot
+      cur = idx + slot * f++;
+      const int32_t st = run_indexer(p, &ixr[l], cur, ws, s);
+      if (st != IX_OK) return st;
+    }
+    const int32_t st = run_attn(p, &attn[l], cur, ws, s);   // shared layers reuse `cur` untouched
+    if (st != IX_OK) return st;
+  }
+  return IX_OK;
+}
+
+}  // namespace

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
             "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
-            "ix_index_overlap", "ix_append_keys", "ix_indexer_argmax"} <= set(names)
+            "ix_index_overlap", "ix_append_keys", "ix_indexer_argmax",
+            "ix_group_forward_noalloc"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -195,7 +196,7 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 4
+    assert ix.ix_abi_version() == 5
 
 
 def test_index_overlap_validation():
@@ -255,3 +256,28 @@ def test_workspace_sizes_cover_the_row_select_state():
     assert lib.ix_workspace_bytes(ctypes.byref(many), ix.IX_OP_TOPK_SCORES, None) == 0
     short = _prob(batch=4, n_q=1, q_start=1000, kv_len=1001, kv_cap=1001, k=2048)
     assert lib.ix_workspace_bytes(ctypes.byref(short), ix.IX_OP_TOPK_SCORES, None) == 0
+
+
+def test_group_noalloc_validates_and_rejects_oversized_calls_before_any_hip_call():
+    """ix_group_forward_noalloc: argument errors as ix_group_forward, and a
+    call whose workspace exceeds the 64 MiB static scratch (the fused path at
+    L = 128K needs GiBs) is rejected with IX_E_WORKSPACE and its sizes in
+    ix_last_error(), all before any HIP call (this runs without a GPU)."""
+    lib = ensure_lib()
+    p = _prob(n_q=131072, kv_len=131072, kv_cap=131072, k=2048)
+    ixr = (ix.IndexerIn * 4)(*[_ixr(heads=64, dim=128) for _ in range(4)])
+    att = (ix.AttnIn * 4)(*[_att() for _ in range(4)])
+    call = lambda n, mask, idx=DUMMY, prob=p: lib.ix_group_forward_noalloc(ctypes.byref(prob), n, mask, ixr, att,
+                                                                         idx, None)
+    gd = ix.GroupDesc(4, 0, 1, ixr, att)
+    assert ix.ix_workspace_bytes(p, ix.IX_OP_GROUP_FORWARD, gd) > ix.NOALLOC_SCRATCH_BYTES
+    assert call(4, 0b0001) == ix.IX_E_WORKSPACE
+    msg = lib.ix_last_error().decode()
+    assert "needs" in msg and str(ix.NOALLOC_SCRATCH_BYTES) in msg
+    assert call(4, 0b1110) == ix.IX_E_ROLES
+    assert call(0, 0b1) == ix.IX_E_ROLES
+    assert call(4, 0b1, idx=None) == ix.IX_E_NULL
+    assert call(4, 0b1, idx=DUMMY + 4) == ix.IX_E_SHAPE
+    assert call(4, 0b1, prob=_prob(k=0)) == ix.IX_E_SHAPE
+    bad = (ix.AttnIn * 4)(*[_att() for _ in range(3)] + [_att(d_v=100)])
+    assert lib.ix_group_forward_noalloc(ctypes.byref(p), 4, 1, ixr, bad, DUMMY, None) == ix.IX_E_SHAPE
