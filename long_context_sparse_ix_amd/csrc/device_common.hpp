@@ -64,15 +64,30 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t codes) {
   return r;
 }
 
+// Wave-wide inclusive prefix sum in lane order, in registers: DPP row_shr
+// steps of 1, 2, 4 and 8 scan each 16-lane row (a lane whose source lies
+// before its row adds the 0 given as the old value), then every row adds the
+// totals of the rows before it, read from lanes 15, 31 and 47.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_shr<0x111>(v);     // row_shr:1
+  v += dpp_shr<0x112>(v);     // row_shr:2
+  v += dpp_shr<0x114>(v);     // row_shr:4
+  v += dpp_shr<0x118>(v);     // row_shr:8
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
 // Wave-wide inclusive suffix sum (lane l gets the sum over lanes >= l).
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_down(v, d);
-    if (l + d < kWave) v += o;
-  }
-  return v;
+  const uint32_t incl = wave_incl_scan(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1) - incl + v;
 }
 
 // Position of query row 0 of sequence b: the sequence's own start when a

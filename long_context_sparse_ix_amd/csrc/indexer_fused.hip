@@ -180,7 +180,7 @@ __device__ Thresh select_kth(Cand c, int cnt, int k, uint32_t* hist) {
 // return the new count.  In place is safe: every chunk is read before any of
 // its slots can be overwritten, and writes never pass the chunk being read.
 template <bool EMIT>
-__device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
+__device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst, int limit = 0) {
   const int l = lane_id();
   int out = 0, eq_seen = 0;
   for (int base = 0; base < cnt; base += kWave * kUnroll) {
@@ -203,7 +203,7 @@ __device__ int keep_pass(Cand c, int cnt, Thresh t, int32_t* dst) {
       if (keep) {
         const int o = out + wave_prefix(km);
         if constexpr (EMIT) {
-          dst[o] = pos[u];
+          if (o < limit) dst[o] = pos[u];        // exactly limit entries are kept
         } else {
           c.s[o] = v[u];
           c.p[o] = pos[u];
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     int written;
     if (cnt > a.k) {
       const Thresh th = select_kth(cand, cnt, a.k, my_hist);
-      keep_pass<true>(cand, cnt, th, dst);
+      keep_pass<true>(cand, cnt, th, dst, a.k);
       written = a.k;
     } else {
       for (int i = l; i < cnt; i += kWave) dst[i] = cand.p[i];

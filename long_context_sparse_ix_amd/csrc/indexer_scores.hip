@@ -172,15 +172,12 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
     // tiles past the last, are masked)
     const int piece = blockIdx.x * kWavesPerWG + wave;
     const int P = (int)((p + kScoreSpan) / kScoreSpan);       // waves that score this row
-    uint64_t valid[kTilesPerWave];
-#pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-      const int64_t c = p + 1 - (s_begin + (int64_t)j * kTileKeys);
-      valid[j] = c >= kWave ? ~0ull : (c <= 0 ? 0ull : (1ull << c) - 1ull);
-    }
+    // keys s_begin .. p are valid (at most kScoreSpan of them are this wave's)
+    const int64_t rem64 = p + 1 - s_begin;
+    const int rem = rem64 < 0 ? 0 : (rem64 > kScoreSpan ? kScoreSpan : (int)rem64);
     const int cap = kLocalCap / P;
     __shared__ uint32_t hist[kWavesPerWG][kLocalBins];
-    const uint4 r = wave_keep_top<kTilesPerWave>(kept, valid, (int)s_begin, cap, hist[wave],
+    const uint4 r = wave_keep_top<kTilesPerWave>(kept, rem, (int)s_begin, cap, hist[wave],
                                                  a.cand + (int64_t)row * kLocalCap + (int64_t)piece * cap);
     if (l == 0) a.local[(int64_t)row * a.rng_stride + piece] = r;
   } else if (a.rng) {

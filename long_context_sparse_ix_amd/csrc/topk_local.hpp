@@ -21,40 +21,42 @@ constexpr int kLocalMaxPieces = 512;  // at least 16 slots per piece
 constexpr int kLocalBins = 256;       // value bins of a wave's histogram (4 per lane)
 
 // Keeps at most cap of this wave's valid values.  Lane l's value j sits at
-// position pos0 + 64 j + l (ascending in (j, l)); valid[j] marks the lanes
-// whose value j exists.  A kLocalBins-bin histogram over the wave's [min, max]
-// (in hist, kLocalBins words of LDS private to the wave) gives the bin holding
-// the (cap+1)-th best; the values in higher bins are kept.  They go to
-// dst[0..kept) in position order as (order key, position).  Returns the
-// piece's record (kept, largest dropped order key or 0, smallest and largest
-// kept order key or ~0 / 0), uniform over the wave.
+// position pos0 + 64 j + l (ascending in (j, l)) and is valid when
+// 64 j + l < rem (the wave's valid positions are a prefix of length rem, which
+// may be <= 0 or beyond NV * 64).  A kLocalBins-bin histogram over the wave's
+// [min, max] (in hist, kLocalBins words of LDS private to the wave) gives the
+// bin holding the (cap+1)-th best; the values in higher bins are kept (all of
+// them when there are at most cap).  They go to dst[0..kept) in position
+// order as (order key, position).  Returns the piece's record (kept, largest
+// dropped order key or 0, smallest and largest kept order key or ~0 / 0),
+// uniform over the wave.  Each value's bin is computed once and reused.
 template <int NV>
-__device__ __forceinline__ uint4 wave_keep_top(const float (&v)[NV], const uint64_t (&valid)[NV], int pos0,
-                                               int cap, uint32_t* hist, uint2* __restrict__ dst) {
+__device__ __forceinline__ uint4 wave_keep_top(const float (&v)[NV], int rem, int pos0, int cap, uint32_t* hist,
+                                               uint2* __restrict__ dst) {
   const int l = lane_id();
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) n += __popcll(valid[j]);
+  const int lim = rem - l;                 // value j of this lane is valid when 64 j < lim
+  const int n = rem <= 0 ? 0 : (rem < NV * kWave ? rem : NV * kWave);
+  int bn[NV];                              // value bin, or -1 for an invalid value
   int vb = -1;                             // keep values in bins above vb
-  float lo = 0.0f, inv = 0.0f;
   if (n > cap) {
-    float hi = -INFINITY;
-    lo = INFINITY;
+    float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      if ((valid[j] >> l) & 1u) {
+      if (kWave * j < lim) {
         lo = fminf(lo, v[j]);
         hi = fmaxf(hi, v[j]);
       }
     lo = wave_min(lo);
     hi = wave_max(hi);
-    inv = (float)kLocalBins / (hi - lo);
+    float inv = (float)kLocalBins / (hi - lo);
     if (!(hi > lo) || !(inv > 0.0f) || !(inv < INFINITY)) inv = 0.0f;   // one bin: keep nothing
     *reinterpret_cast<u32x4*>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if ((valid[j] >> l) & 1u) atomicAdd(&hist[min(kLocalBins - 1, max(0, (int)((v[j] - lo) * inv)))], 1u);
+    for (int j = 0; j < NV; ++j) {
+      bn[j] = kWave * j < lim ? min(kLocalBins - 1, max(0, (int)((v[j] - lo) * inv))) : -1;
+      if (bn[j] >= 0) atomicAdd(&hist[bn[j]], 1u);
+    }
     wave_lds_sync();
     // bin holding the (cap+1)-th best: lane l owns bins 4l .. 4l+3
     const int kk = cap + 1;
@@ -69,20 +71,23 @@ __device__ __forceinline__ uint4 wave_keep_top(const float (&v)[NV], const uint6
     else if (a0 < kk && kk <= a0 + (int)h.x) bin = 4 * l;
     const uint64_t bm = __ballot(bin >= 0);
     vb = __shfl(bin, __ffsll((unsigned long long)bm) - 1);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) bn[j] = kWave * j < lim ? 0 : -1;
   }
   int out = 0;
   uint32_t dropped = 0u, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const bool in = (valid[j] >> l) & 1u;
-    const bool keep = in && min(kLocalBins - 1, max(0, (int)((v[j] - lo) * inv))) > vb;
+    const bool keep = bn[j] > vb;
     const uint64_t km = __ballot(keep);
     const uint32_t key = order_key(v[j]);
     if (keep) {
-      dst[out + wave_prefix(km)] = make_uint2(key, (uint32_t)(pos0 + 64 * j + l));
+      const int o = out + wave_prefix(km);
+      if (o < cap) dst[o] = make_uint2(key, (uint32_t)(pos0 + 64 * j + l));   // at most cap are kept
       kmin = min(kmin, key);
       kmax = max(kmax, key);
-    } else if (in) {
+    } else if (bn[j] >= 0) {
       dropped = max(dropped, key);
     }
     out += __popcll(km);

@@ -525,28 +525,41 @@ __global__ __launch_bounds__(kCT) void tk_collect_kernel(ChunkArgs a) {
 constexpr int kCapPadded = kCap + kCap / 8;
 __device__ __forceinline__ int lds_at(int i) { return i + (i >> 3); }
 
+// Exclusive prefix sum over the kFT threads in thread order, one barrier
+// (wtot: kFT / kWave words of LDS used by this call only).
+__device__ __forceinline__ uint32_t block_excl_scan1(uint32_t v, uint32_t* wtot) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (l == kWave - 1) wtot[w] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < w; ++i) before += wtot[i];
+  return before + x - v;
+}
+
 // Stable emission of a position-ordered candidate list (keys ck, positions
-// cp, m entries in LDS at lds_at(i)): every entry with key > v and the first
-// `need` with key == v, in list order.  Thread t owns entries [t*P, t*P + P):
-// one pass counts them, two scans place them, a second pass writes.
+// cp, m <= 8192 entries in LDS at lds_at(i)): every entry with key > v and the
+// first `need` with key == v, in list order.  Thread t owns entries [t*P,
+// t*P + P).  One scan of the packed per-thread counts (key > v in the low 16
+// bits, key == v in the high 16) places every thread's output: the ties kept
+// before it are min(ties before it, need).
 __device__ __forceinline__ void emit_stable(const uint32_t* ck, const int* cp, int m, uint32_t v, int need,
-                                            int k, int32_t* __restrict__ dst, int* redi) {
+                                            int k, int32_t* __restrict__ dst, uint32_t* wtot) {
   const int tid = threadIdx.x;
   const int P = (m + kFT - 1) / kFT;
   const int e0 = min(m, tid * P), e1 = min(m, e0 + P);
-  int gt = 0, eq = 0;
+  uint32_t gt = 0, eq = 0;
   for (int i = e0; i < e1; ++i) {
     const uint32_t key = ck[lds_at(i)];
     gt += key > v;
     eq += key == v;
   }
-  int tot;
-  int eq_rank = block_excl_scan<kFT>(eq, redi, &tot);
-  const int take_eq = min(eq, max(0, need - eq_rank));
-  int out = block_excl_scan<kFT>(gt + take_eq, redi, &tot);
-  for (int i = e0; i < e1; ++i) {
+  const uint32_t ex = block_excl_scan1(gt | (eq << 16), wtot);
+  int eq_rank = (int)(ex >> 16);
+  int out = (int)(ex & 0xFFFFu) + min(eq_rank, need);
+  for (int i = e0; i < e1 && out < k; ++i) {
     const uint32_t key = ck[lds_at(i)];
-    if ((key > v || (key == v && eq_rank++ < need)) && out < k) dst[out++] = cp[lds_at(i)];
+    if (key > v || (key == v && eq_rank++ < need)) dst[out++] = cp[lds_at(i)];
   }
 }
 
@@ -555,7 +568,7 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
   __shared__ int cp[kCapPadded];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t redu[kFT / kWave];
-  __shared__ int redi[kFT / kWave];
+  __shared__ uint32_t wtot[kFT / kWave];
   __shared__ int sel_bin, sel_above;
   const int row = blockIdx.x, tid = threadIdx.x;
   const int n = row_len(row, a.n_q, a.q_start, a.seq);
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(kFT) void tk_finish_kernel(ChunkArgs a, int32_t* __
       m, a.k - rs.above, kmin, kmax, [&](int i) { return ck[lds_at(i)]; }, [&](int i) { return in_vb(ck[lds_at(i)]); }, hist,
       &sel_bin, &sel_above, &need);
 
-  emit_stable(ck, cp, m, v, need, a.k, dst, redi);
+  emit_stable(ck, cp, m, v, need, a.k, dst, wtot);
 }
 
 // ---- wave-local keep + merge (rows of at most kLocalMaxPieces pieces) ----
@@ -609,120 +622,209 @@ __global__ __launch_bounds__(256) void tk_wave_local_kernel(ChunkArgs a) {
   const int pos0 = piece * kLocalSpan;
   const float* src = a.scores + (int64_t)row * a.ld;
   float v[kLocalNV];
-  uint64_t valid[kLocalNV];
 #pragma unroll
-  for (int j = 0; j < kLocalNV; ++j) {
-    const int c = n - (pos0 + kWave * j);     // valid lanes of value j
-    valid[j] = c >= kWave ? ~0ull : (c <= 0 ? 0ull : (1ull << c) - 1ull);
-    v[j] = src[min(pos0 + kWave * j + l, n - 1)];
-  }
+  for (int j = 0; j < kLocalNV; ++j) v[j] = src[min(pos0 + kWave * j + l, n - 1)];
   const int cap = kLocalCap / P;
   __shared__ uint32_t hist[4][kLocalBins];
-  const uint4 r = wave_keep_top<kLocalNV>(v, valid, pos0, cap, hist[wave],
+  const uint4 r = wave_keep_top<kLocalNV>(v, n - pos0, pos0, cap, hist[wave],
                                           a.cand + (int64_t)row * kLocalCap + (int64_t)piece * cap);
   if (l == 0) a.local[(int64_t)row * a.local_stride + piece] = r;
 }
 
 // Per row: the pieces' kept entries (piece c at slots [c*cap, c*cap + kept_c)
-// of the candidate list) gathered in position order into LDS.  Entries at or
-// below the largest dropped key D rank below some dropped entry; if at least
-// k entries lie above D, the row's k-th best is among them and every dropped
-// entry ranks below it, so the k-th best of the entries above D and a stable
-// emission give the row's top k.  Otherwise the whole-row select runs.
-//   pass 1: load the entries into LDS; those above D also go into a
-//           kSingleBins value histogram over (D, largest kept];
-//   the bin vb holding the k-th best, then pass 2 copies vb's entries to a
-//   short list on which the exact radix select runs (all of vb's entries are
-//   above D, so ties at the k-th key are all there);
-//   passes 3 and 4: stable emission.
-constexpr int kShort = 1024;     // short-list capacity (else the radix runs over the whole list)
+// of the candidate list, in position order).  Entries at or below the largest
+// dropped key D rank below some dropped entry; if at least k entries lie
+// above D, the row's k-th best is among them and every dropped entry ranks
+// below it, so the k-th best of the entries above D and a stable emission
+// give the row's top k.  Otherwise the whole-row select runs.
+// Thread t holds the 8 contiguous slots [8t, 8t + 8) in registers, so the
+// valid entries' list order is thread order and nothing is copied to LDS:
+//   A  every thread loads its slots and one piece's record at once; per-wave
+//      sums / extremes of the records and one barrier give the kept count m,
+//      D and the kept key range;
+//   B  valid slots above D go into a kMergeBins value histogram over
+//      (D, largest kept];
+//   C  one wave finds the bin holding the k-th best;
+//   D  that bin's keys form a short list (all above D, so every tie of the
+//      k-th key is in it);
+//   E  one wave ranks the short list (one key per lane) for the k-th key v and
+//      the number of its ties to keep; a longer list runs the radix select;
+//   F  stable emission: one scan of per-thread counts places each thread's
+//      kept positions.
+constexpr int kShort = 1024;            // short-list capacity (else the whole-row select runs)
+constexpr int kMergeBins = 1024;
+constexpr int kMergeSlots = kLocalCap / kFT;   // contiguous candidate slots per thread
+static_assert(kMergeSlots == 8, "two 16-byte loads of two slots, twice");
 
 __global__ __launch_bounds__(kFT) void tk_merge_kernel(ChunkArgs a, int32_t* __restrict__ idx) {
-  __shared__ uint32_t ck[kCapPadded];
-  __shared__ int cp[kCapPadded];
-  __shared__ uint32_t hist[kSingleBins];
+  __shared__ uint32_t hist[kMergeBins];
   __shared__ uint32_t sk[kShort];
+  __shared__ int kept[kLocalMaxPieces];
+  __shared__ uint4 wpart[kFT / kWave];
+  __shared__ int wabove[kFT / kWave];
+  __shared__ uint32_t wtot[kFT / kWave];
   __shared__ uint32_t redu[kFT / kWave];
-  __shared__ int redi[kFT / kWave];
-  __shared__ int offs[kLocalMaxPieces + 1];
-  __shared__ int sel_bin, sel_above, sh_short;
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ int sel_bin, sel_above, sh_short, sh_need;
+  __shared__ uint32_t sh_v;
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int n = row_len(row, a.n_q, a.q_start, a.seq);
   int32_t* dst = idx + (int64_t)row * a.k;
   if (n <= a.k) {
     write_trivial(dst, n, a.k);
     return;
   }
-  for (int i = tid; i < kSingleBins; i += kFT) hist[i] = 0u;
-  if (tid == 0) sh_short = 0;
   const int P = (n + a.local_span - 1) / a.local_span;     // <= kLocalMaxPieces
   const int cap = kLocalCap / P;
+  // A (the row's list has kLocalCap slots, so all of them can be read)
+  const int s0 = kMergeSlots * tid;
+  uint2 x[kMergeSlots];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.cand + (int64_t)row * kLocalCap + s0);
+#pragma unroll
+    for (int j = 0; j < kMergeSlots / 2; ++j) {
+      const u32x4 q = src[j];
+      x[2 * j] = make_uint2(q.x, q.y);
+      x[2 * j + 1] = make_uint2(q.z, q.w);
+    }
+  }
   const uint4 e = tid < P ? a.local[(int64_t)row * a.local_stride + tid] : make_uint4(0u, 0u, 0xFFFFFFFFu, 0u);
-  int m;
-  const int ex = block_excl_scan<kFT>((int)e.x, redi, &m);
-  if (tid < P) offs[tid] = ex;
-  if (tid == 0) offs[P] = m;
-  const uint32_t dmax = block_reduce<kFT>(e.y, redu, UMaxOp{});   // its barriers publish offs
-  const uint32_t gmin = block_reduce<kFT>(e.z, redu, UMinOp{});
-  const uint32_t gmax = block_reduce<kFT>(e.w, redu, UMaxOp{});
-  if (m >= a.k) {
+  static_assert(kMergeBins == kFT, "one histogram bin per thread to clear");
+  hist[tid] = 0u;
+  if (tid == 0) sh_short = 0;
+  if (tid < P) kept[tid] = (int)e.x;
+  {
+    const uint32_t sum_w = wave_reduce(e.x, [](uint32_t p, uint32_t q) { return p + q; });
+    const uint32_t dmax_w = wave_max(e.y), gmin_w = wave_min(e.z), gmax_w = wave_max(e.w);
+    if (l == 0) wpart[wave] = make_uint4(sum_w, dmax_w, gmin_w, gmax_w);
+  }
+  __syncthreads();
+  uint32_t m = 0, dmax = 0u, gmin = 0xFFFFFFFFu, gmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kFT / kWave; ++w) {
+    const uint4 q = wpart[w];
+    m += q.x;
+    dmax = max(dmax, q.y);
+    gmin = min(gmin, q.z);
+    gmax = max(gmax, q.w);
+  }
+  if ((int)m >= a.k) {
+    // B: slot s0 + u lies in piece c0 (or c0 + 1: cap >= 16 > 8 slots); for
+    // s < 2^13 and cap <= 2^13, floor(s / cap) = umulhi(s, floor((2^32 - 1) / cap) + 1)
+    const uint32_t mul = 0xFFFFFFFFu / (uint32_t)cap + 1u;
+    const int c0 = (int)__umulhi((uint32_t)s0, mul);
+    const int j0 = s0 - c0 * cap;
+    const int kept0 = c0 < P ? kept[c0] : 0, kept1 = c0 + 1 < P ? kept[c0 + 1] : 0;
     const float lo = key_value(max(dmax + 1u, gmin));
-    const float inv = bin_scale(lo, key_value(gmax), kSingleBins);
-    const uint2* src = a.cand + (int64_t)row * kLocalCap;
-    const int slots = P * cap;
-    constexpr int kB = 8;                     // loads per thread in flight
+    const float inv = bin_scale(lo, key_value(gmax), kMergeBins);
+    uint32_t valid = 0u;
+    int bn[kMergeSlots];
     int above = 0;
-    for (int i0 = tid; i0 < slots; i0 += kFT * kB) {
-      uint2 x[kB];
-      int o[kB];
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const int i = min(i0 + u * kFT, slots - 1);
-        x[u] = src[i];
-        const int c = i / cap;
-        const int at = offs[c] + (i - c * cap);
-        o[u] = (i0 + u * kFT < slots && at < offs[c + 1]) ? at : -1;
+    for (int u = 0; u < kMergeSlots; ++u) {
+      const int j = j0 + u;
+      const bool ok = j < cap ? j < kept0 : j - cap < kept1;
+      valid |= ok ? 1u << u : 0u;
+      bn[u] = -1;
+      if (ok && x[u].x > dmax) {
+        bn[u] = vbin(key_value(x[u].x), lo, inv, kMergeBins);
+        ++above;
+        atomicAdd(&hist[bn[u]], 1u);
       }
+    }
+    above = (int)wave_reduce((uint32_t)above, [](uint32_t p, uint32_t q) { return p + q; });
+    if (l == 0) wabove[wave] = above;
+    __syncthreads();
+    int n_above = 0;
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (o[u] >= 0) {
-          ck[lds_at(o[u])] = x[u].x;
-          cp[lds_at(o[u])] = (int)x[u].y;
-          if (x[u].x > dmax) {
-            ++above;
-            atomicAdd(&hist[vbin(key_value(x[u].x), lo, inv, kSingleBins)], 1u);
+    for (int w = 0; w < kFT / kWave; ++w) n_above += wabove[w];
+    if (n_above >= a.k) {
+      // C: lane l owns bins 16l .. 16l + 15
+      if (wave == 0) {
+        uint32_t h[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 q = *reinterpret_cast<const u32x4*>(hist + 16 * l + 4 * j);
+          h[4 * j] = q.x; h[4 * j + 1] = q.y; h[4 * j + 2] = q.z; h[4 * j + 3] = q.w;
+        }
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tot += h[j];
+        int ab = (int)(wave_suffix_sum(tot) - tot);     // entries in higher lanes' bins
+        if (ab < a.k && a.k <= ab + (int)tot) {            // exactly one lane
+#pragma unroll
+          for (int j = 15; j >= 0; --j) {
+            if (ab < a.k && a.k <= ab + (int)h[j]) {
+              sel_bin = 16 * l + j;
+              sel_above = ab;
+            }
+            ab += (int)h[j];
           }
         }
-    }
-    int n_above;
-    block_excl_scan<kFT>(above, redi, &n_above);     // its barriers publish ck, cp and hist
-    if (n_above >= a.k) {
-      pick_from_top(hist, kSingleBins, a.k, &sel_bin, &sel_above);
-      const int vb = sel_bin, kb = a.k - sel_above;
-      const auto in_vb = [&](uint32_t key) { return key > dmax && vbin(key_value(key), lo, inv, kSingleBins) == vb; };
-      uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
-      for (int i = tid; i < m; i += kFT) {
-        const uint32_t key = ck[lds_at(i)];
-        if (in_vb(key)) {
-          const int j = atomicAdd(&sh_short, 1);
-          if (j < kShort) sk[j] = key;
-          bmin = min(bmin, key);
-          bmax = max(bmax, key);
-        }
       }
-      bmin = block_reduce<kFT>(bmin, redu, UMinOp{});   // its barriers publish sk and sh_short
-      bmax = block_reduce<kFT>(bmax, redu, UMaxOp{});
+      __syncthreads();
+      // D
+      const int vb = sel_bin, kb = a.k - sel_above;
+#pragma unroll
+      for (int u = 0; u < kMergeSlots; ++u)
+        if (bn[u] == vb) {
+          const int j = atomicAdd(&sh_short, 1);
+          if (j < kShort) sk[j] = x[u].x;
+        }
+      __syncthreads();
       const int ns = sh_short;
-      int need = 0;
-      uint32_t v;
-      if (ns <= kShort)
-        v = radix_kth<kFT>(ns, kb, bmin, bmax, [&](int i) { return sk[i]; }, [&](int) { return true; }, hist,
-                           &sel_bin, &sel_above, &need);
-      else
-        v = radix_kth<kFT>(m, kb, bmin, bmax, [&](int i) { return ck[lds_at(i)]; },
-                           [&](int i) { return in_vb(ck[lds_at(i)]); }, hist, &sel_bin, &sel_above, &need);
-      emit_stable(ck, cp, m, v, need, a.k, dst, redi);
-      return;
+      if (ns <= kShort) {
+        uint32_t v;
+        int need;
+        if (ns <= kWave) {
+          // E: lane i holds short-list key i; v is the key with fewer than kb
+          // keys above it and at least kb at or above it
+          if (wave == 0) {
+            const uint32_t mine = l < ns ? sk[l] : 0u;
+            int gt = 0, ge = 0;
+            for (int j = 0; j < ns; ++j) {
+              const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+              gt += kj > mine;
+              ge += kj >= mine;
+            }
+            const bool hit = l < ns && gt < kb && kb <= ge;
+            const uint64_t hm = __ballot(hit);
+            if (l == __ffsll((unsigned long long)hm) - 1) {
+              sh_v = mine;
+              sh_need = kb - gt;
+            }
+          }
+          __syncthreads();
+          v = sh_v;
+          need = sh_need;
+        } else {
+          const uint32_t mine = tid < ns ? sk[tid] : 0u;
+          const uint32_t bmin = block_reduce<kFT>(tid < ns ? mine : 0xFFFFFFFFu, redu, UMinOp{});
+          const uint32_t bmax = block_reduce<kFT>(mine, redu, UMaxOp{});
+          v = radix_kth<kFT>(ns, kb, bmin, bmax, [&](int i) { return sk[i]; }, [&](int) { return true; }, hist,
+                             &sel_bin, &sel_above, &need);
+        }
+        // F
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int u = 0; u < kMergeSlots; ++u)
+          if ((valid >> u) & 1u) {
+            gt += x[u].x > v;
+            eq += x[u].x == v;
+          }
+        const uint32_t ex = block_excl_scan1(gt | (eq << 16), wtot);
+        int eq_rank = (int)(ex >> 16);
+        int out = (int)(ex & 0xFFFFu) + min(eq_rank, need);
+#pragma unroll
+        for (int u = 0; u < kMergeSlots; ++u)
+          if ((valid >> u) & 1u) {
+            const uint32_t key = x[u].x;
+            if (key > v || (key == v && eq_rank++ < need)) {
+              if (out < a.k) dst[out] = (int)x[u].y;
+              ++out;
+            }
+          }
+        return;
+      }
     }
   }
   select_row_single(a.scores + (int64_t)row * a.ld, n, a.k, dst);
