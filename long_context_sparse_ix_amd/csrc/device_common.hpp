@@ -109,6 +109,21 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// op of v over lanes l and l ^ 16 (xor16_op) or l ^ 32 (xor32_op), in
+// registers: with both operands v, v_permlane16_swap / v_permlane32_swap
+// return v of the lane and of its partner (the last two steps of wave_reduce
+// below).
+template <typename Op>
+__device__ __forceinline__ float xor16_op(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32_op(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Full-wave reduction with the result in every lane, in registers: DPP moves
 // pair lanes within 16 (xor 1, xor 2, then the 8- and 16-lane mirrors, which
 // pair each already-reduced half with the other), v_permlane16_swap and

@@ -12,17 +12,26 @@
 // Layout of the work
 //   * one wave = one (query row, slot range); all Hq <= 16 heads of the row
 //     share every gathered latent row, so each gathered byte feeds 16 heads;
-//   * 16 slots per step: lane (key n16 = l%16, group g = l/16) loads 16-byte
-//     pieces 4ks + g of latent row idx[n16] straight from HBM into the MFMA A
-//     operand (k-group g of step ks; 64 contiguous bytes per row and load),
-//     prefetched one step ahead, index words two steps ahead;
+//   * 16 slots per step.  The step's 16 latent rows are gathered with
+//     coalesced loads: one instruction moves 1 KB of one row (consecutive
+//     lanes, consecutive 16-byte pieces, the row id uniform), so the vector L1
+//     sees one tag lookup per cache line instead of one per lane (with the
+//     pieces spread the way the MFMA operand wants them, 16 rows per
+//     instruction, the L1's tag rate bounded the kernel).  Two named register
+//     buffers alternate, so the next step's rows are in flight while this
+//     step computes, and index words are loaded two steps ahead;
+//   * each step parks its rows in a wave-private LDS tile (one 16-byte store
+//     per register) whose row stride is 8 or 40 (mod 64) dwords, so the
+//     transposed value reads and the key-operand reads below are
+//     bank-conflict free.  (Direct HBM -> LDS loads of the same tile measured
+//     about 40% slower than this register path at L = 128K.)
 //   * S^T = KV . Q^T with v_mfma_f32_16x16x32_bf16 (M = keys, N = heads, the
-//     query slice stays in VGPRs), so lane l ends with 4 logits of head l%16
-//     -- exactly the B-operand layout of the P.V product below;
-//   * the value part of the 16 rows is parked in a wave-private LDS tile and
-//     read back transposed by ds_read_b64_tr_b16 (lane (dv, key group) gets 4
-//     keys of one value dim) as the A operand of O^T = V^T . P^T
-//     (v_mfma_f32_16x16x16_bf16);
+//     query slice stays in VGPRs; the key operand is read from the tile), so
+//     lane l ends with 4 logits of head l%16 -- exactly the B-operand layout
+//     of the P.V product below;
+//   * the value part of the 16 rows is read straight from the tile by
+//     ds_read_b64_tr_b16 (lane (dv, key group) gets 4 keys of one value dim)
+//     as the A operand of O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16);
 //   * online softmax in base 2 against a reference max that may trail the
 //     running max by up to 2^8, so the accumulators are rescaled only when a
 //     head's max jumps further (rarely);
@@ -44,32 +53,81 @@ constexpr float kSlack = 8.0f;   // how far the softmax reference may trail the 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
 
-template <int MT>
-struct VTile {
-  static constexpr int Dv = 16 * MT;
-  // row stride in dwords chosen == 8 (mod 64): the 8 rows x 32 bytes one
-  // half-wave of a transposed read touches cover all banks once, and the 16
-  // rows a parking store touches collide at most pairwise
-  static constexpr int stride_dw = Dv / 2 + ((8 - (Dv / 2) % 64) + 64) % 64;
-  static constexpr int stride = 2 * stride_dw;      // bf16 elements
-  static constexpr int bytes = 16 * stride_dw * 4;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wave-private tile of one 16-slot step, generic layout: row r (D bf16 = C
+// 16-byte pieces) at byte r * RS, RS = 16 * CP with CP the smallest piece
+// count >= C that is 2 (mod 8) pieces, i.e. 8 or 40 (mod 64) dwords: the 8
+// rows x 32 bytes a half-wave of a transposed value read touches then fall in
+// 8 disjoint bank groups.  Lane l of gather load j fetches slot s = 64 j + l,
+// i.e. row s / CP, piece s % CP, and parks it at byte 16 s; pad pieces and the
+// slack of the last load repeat a valid piece of the same or the last row.
+template <int KS>
+struct GTile {
+  static constexpr bool kLatent = false;
+  static constexpr int D = 32 * KS;
+  static constexpr int C = D / 8;
+  static constexpr int CP = C + ((2 - C % 8) + 8) % 8;
+  static constexpr int RS = 16 * CP;
+  static constexpr int NI = (16 * CP + kWave - 1) / kWave;   // gather loads per step
+  static constexpr int bytes = NI * kWave * 16;
+  static constexpr int RPI = (kWave + CP - 1) / CP + 1;       // rows one load can touch
+  static_assert(CP % 8 == 2, "row stride 2 (mod 8) pieces");
+  // byte offset of the key operand (row n16, k-group g of k-step ks) and of
+  // a row's value part
+  __device__ static __forceinline__ int qk_off(int n16, int ks, int g) { return n16 * RS + 64 * ks + 16 * g; }
+  __device__ static __forceinline__ int v_off(int row) { return row * RS; }
 };
 
-// LDS of a workgroup: the waves' value tiles, reused after the slot loop as
-// the buffer of the in-workgroup merge (two waves' accumulators), then the
-// merge's per-wave (m, l) of every head.
-template <int MT>
+// The 576-wide latent row (V = its first 512 dims = 1 KB): one gather load
+// per row moves the value part (64 lanes x 16 bytes, the row id uniform over
+// the load, so its address is a scalar base plus a lane constant), parked in
+// a value region of stride 1056 bytes (8 (mod 64) dwords, as above); two loads
+// move the 16 rows' 128-byte rope parts (8 lanes per row), parked in a rope
+// region of stride 144 bytes (36 (mod 64) dwords: the 8 rows one 16-byte
+// operand read phase touches fall in disjoint bank groups).
+struct GTileLatent {
+  static constexpr bool kLatent = true;
+  static constexpr int D = 576, Dv = 512;
+  static constexpr int RSV = 1056;
+  static constexpr int ROPE = 16 * RSV;
+  static constexpr int RSR = 144;
+  static constexpr int NR = 2;                                  // rope loads (8 rows each)
+  static constexpr int NI = 16 + NR;                            // gather loads per step
+  static constexpr int bytes = ROPE + 16 * RSR;
+  __device__ static __forceinline__ int qk_off(int n16, int ks, int g) {
+    return ks < 16 ? n16 * RSV + 64 * ks + 16 * g : ROPE + n16 * RSR + 64 * (ks - 16) + 16 * g;
+  }
+  __device__ static __forceinline__ int v_off(int row) { return row * RSV; }
+};
+
+template <int KS, int MT>
+struct TileOf {
+  using type = GTile<KS>;
+};
+template <>
+struct TileOf<18, 32> {
+  using type = GTileLatent;
+};
+
+// LDS of a workgroup: one tile per wave; after the slot loop the tiles are
+// reused as the buffer of the in-workgroup merge (two waves' accumulators),
+// then the merge's per-wave (m, l) of every head.
+template <int KS, int MT>
 struct AttnLds {
-  static constexpr int tiles = kWavesPerWG * VTile<MT>::bytes;
+  static constexpr int wave_bytes = (TileOf<KS, MT>::type::bytes + 15) / 16 * 16;
+  static constexpr int tiles = kWavesPerWG * wave_bytes;
   static constexpr int merge = 2 * MT * kWave * 16;
   static constexpr int stat_off = ((tiles > merge ? tiles : merge) + 15) / 16 * 16;
   static constexpr int bytes = stat_off + 2 * kWavesPerWG * 16 * 4;
+  static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
 };
 
 template <int KS, int MT, int WPI>
 __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(AttnArgs a) {
   constexpr int D = 32 * KS, Dv = 16 * MT;
-  using V = VTile<MT>;
+  using G = typename TileOf<KS, MT>::type;
+  using L = AttnLds<KS, MT>;
   static_assert(WPI == 1 || WPI == kWavesPerWG, "a (row, split) has one wave or the whole workgroup");
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -78,14 +136,10 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   if (item >= a.rows * a.splits) return;     // whole workgroup when WPI > 1
   const int r = item / a.splits, sp = item % a.splits;
   const int b = r / a.n_q;
-  uint16_t* vl = reinterpret_cast<uint16_t*>(smem + wave * V::bytes);
+  unsigned char* const tile = smem + wave * L::wave_bytes;
 
   // Query slice as the B operand: head n16, elements [32ks + 8g, +8) -- the
-  // MFMA's k-group g of step ks.  The gathered latent rows use the same
-  // split, so in every gather instruction the four lanes of a row read 64
-  // contiguous bytes: 16 cache lines per instruction instead of 64 (a split
-  // into one contiguous run per lane spreads each instruction over 4 lines per
-  // row, and the vector L1's line rate, not memory, then bounds the kernel).
+  // MFMA's k-group g of step ks; the key operand is read the same way.
   const bool hq_ok = n16 < a.Hq;
   bf16x8 qf[KS];
   {
@@ -103,7 +157,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     j1 = min(j1, j0 + per);
   }
   const int32_t* irow = a.idx + (int64_t)r * a.k;
-  const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride + 8 * g;
+  const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride;
 
   f32x4 oacc[MT];
 #pragma unroll
@@ -115,33 +169,81 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   // would stall each step on the next step's prefetch.  An index word past
   // the range reads an in-row slot and becomes -1; an invalid slot gathers
   // row 0, whose logit is masked to -inf and whose value row is weighted by 0.
+  // Lane n16 (every g) holds the id of slot c0 + n16.
   auto slot_row = [&](int c0) -> int {
     const int slot = c0 + n16;
     const int v = irow[min(slot, a.k - 1)];
     return slot < j1 ? v : -1;
   };
-  auto fetch = [&](int rid, bf16x8* kf) -> bool {
+  // The 16 latent rows of a step into register buffer kf; returns whether
+  // this lane's slot (n16) is valid.
+  auto fetch = [&](int rid, bf16x8 (&kf)[G::NI]) -> bool {
     const bool valid = rid >= 0 && (int64_t)rid < a.kv_len;
-    const uint16_t* src = kvb + (int64_t)(valid ? rid : 0) * D;
+    const int rid_c = valid ? rid : 0;
+    int rs[16];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+    for (int q = 0; q < 16; ++q) rs[q] = __builtin_amdgcn_readlane(rid_c, q);
+    if constexpr (G::kLatent) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) kf[q] = *reinterpret_cast<const bf16x8*>(kvb + (int64_t)rs[q] * D + 8 * l);
+#pragma unroll
+      for (int h = 0; h < G::NR; ++h) {
+        const int rid_h = __shfl(rid_c, 8 * h + (l >> 3));
+        kf[16 + h] = *reinterpret_cast<const bf16x8*>(kvb + (int64_t)rid_h * D + G::Dv + 8 * (l & 7));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G::NI; ++j) {
+        const int sl = kWave * j + l;
+        const int row = sl / G::CP;                 // >= 16 only in the last load's slack
+        const int pc = min(sl - row * G::CP, G::C - 1);
+        const int r0 = (kWave * j) / G::CP;         // constant once the loop is unrolled
+        int rq = rs[min(r0, 15)];
+#pragma unroll
+        for (int dr = 1; dr < G::RPI; ++dr)
+          if (row == r0 + dr) rq = rs[min(r0 + dr, 15)];
+        kf[j] = *reinterpret_cast<const bf16x8*>(kvb + (int64_t)rq * D + 8 * pc);
+      }
+    }
     return valid;
   };
 
-  // One 16-slot step on gathered rows kf.
-  auto step = [&](const bf16x8 (&kf)[KS], bool valid) {
-    const uint32_t vm = (uint32_t)__ballot(valid) & 0xFFFFu;   // lanes 0..15 own slots 0..15
+  // Park a step's gathered rows kf in the tile (nothing when no slot is
+  // valid); returns the valid-slot mask (bit n: slot n, from lanes 0..15).
+  // The stores follow the previous step's tile reads in program order, and a
+  // wave's LDS operations complete in order, so one tile suffices.
+  auto park = [&](const bf16x8 (&kf)[G::NI], bool valid) -> uint32_t {
+    const uint32_t vm = (uint32_t)__ballot(valid) & 0xFFFFu;
+    if (vm == 0u) return 0u;
+    if constexpr (G::kLatent) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) *reinterpret_cast<bf16x8*>(tile + G::v_off(q) + 16 * l) = kf[q];
+#pragma unroll
+      for (int h = 0; h < G::NR; ++h)
+        *reinterpret_cast<bf16x8*>(tile + G::ROPE + (8 * h + (l >> 3)) * G::RSR + 16 * (l & 7)) = kf[16 + h];
+    } else {
+#pragma unroll
+      for (int j = 0; j < G::NI; ++j) *reinterpret_cast<bf16x8*>(tile + 16 * (kWave * j + l)) = kf[j];
+    }
+    // the stores are visible to this wave's later LDS reads; the compiler
+    // must not move reads of other lanes' pieces above them
+    asm volatile("" ::: "memory");
+    return vm;
+  };
+
+  // One 16-slot step on the parked tile: S^T = KV . Q^T, online softmax,
+  // O^T += V^T . P^T.
+  auto step = [&](uint32_t vm) {
     if (vm == 0u) return;
-
-    f32x4 sacc = f32x4{};
+    // two independent accumulator chains (even and odd k-steps)
+    f32x4 sa = f32x4{}, sb = f32x4{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
-    // park the value part of row n16 for the transposed read
-    static_assert(Dv % 32 == 0, "the value part is whole k-steps");
-#pragma unroll
-    for (int ks = 0; ks < Dv / 32; ++ks) *reinterpret_cast<bf16x8*>(vl + n16 * V::stride + 32 * ks + 8 * g) = kf[ks];
-
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(tile + G::qk_off(n16, ks, g));
+      if (ks & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[ks], sb, 0, 0, 0);
+      else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[ks], sa, 0, 0, 0);
+    }
+    const f32x4 sacc = sa + sb;
     float z[4];
     float cmax = -INFINITY;
 #pragma unroll
@@ -149,8 +251,9 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
       z[i] = ((vm >> (4 * g + i)) & 1u) ? sacc[i] * a.scale_log2 : -INFINITY;
       cmax = fmaxf(cmax, z[i]);
     }
-    cmax = wave_max_xor(cmax, 16);
-    cmax = wave_max_xor(cmax, 32);
+    const auto fmax_op = [](float x, float y) { return fmaxf(x, y); };
+    const auto add_op = [](float x, float y) { return x + y; };
+    cmax = xor32_op(xor16_op(cmax, fmax_op), fmax_op);
     // The reference m_run may trail the running max by up to kSlack (log2
     // units): every p = 2^(z - m_run) then stays below 2^kSlack, far inside
     // the fp32 and bf16 ranges, and the normalised softmax does not depend on
@@ -172,51 +275,56 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
       pv[i] = m_run == -INFINITY ? 0.0f : exp2f(z[i] - m_run);
       psum += pv[i];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = xor32_op(xor16_op(psum, add_op), add_op);
     l_run += psum;
     const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
     const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
-
-    wave_lds_sync();
     // transposed read: lane (n16, g) supplies 4 value dims of key 4g + n16/4
     // and receives value dim 16mt + n16 of keys 4g .. 4g+3
-    const uint16_t* vrow = vl + (4 * g + (n16 >> 2)) * V::stride + 4 * (n16 & 3);
+    const uint16_t* vrow = reinterpret_cast<const uint16_t*>(tile + G::v_off(4 * g + (n16 >> 2))) + 4 * (n16 & 3);
     v4s_t vt[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[mt]), pb, oacc[mt], 0, 0, 0);
-    wave_lds_sync();
+    // the next step's stores come after these reads (in-order LDS); keep
+    // the compiler from moving them above
+    asm volatile("" ::: "memory");
   };
 
   // Two named buffers in turn (unrolled by 2): the step on one runs while the
-  // other's gathers are in flight.  A loop-carried copy of the buffer would
-  // make the compiler wait for those gathers at every step.  (A third buffer,
-  // two steps of lookahead, measured no faster: the gathers are bound by the
-  // rate at which the CUs take in scattered 64-byte pieces, not by latency.)
-  bf16x8 kA[KS], kB[KS];
+  // other's gathers are in flight; a step's rows are parked right after the
+  // previous step's compute is issued, so the stores overlap its P.V MFMAs.
+  // A loop-carried copy of the buffer would make the compiler wait for those
+  // gathers at every step.
+  bf16x8 kA[G::NI], kB[G::NI];
   bool vA = fetch(slot_row(j0), kA), vB = false;
   int rid_after = slot_row(j0 + 16);             // -1 past the range
-  for (int c0 = j0; c0 < j1; c0 += 32) {
-    // prefetch: latent rows of the next step, index words of the one after
-    int rid_next = rid_after;
-    rid_after = slot_row(c0 + 32);
-    vB = fetch(rid_next, kB);
-    step(kA, vA);
-    if (c0 + 16 >= j1) break;
-    rid_next = rid_after;
-    rid_after = slot_row(c0 + 48);
-    vA = fetch(rid_next, kA);
-    step(kB, vB);
+  if (j0 < j1) {
+    uint32_t vm = park(kA, vA);
+    for (int c0 = j0;; c0 += 32) {
+      // prefetch: latent rows of the next step, index words of the one after
+      int rid_next = rid_after;
+      rid_after = slot_row(c0 + 32);
+      vB = fetch(rid_next, kB);
+      step(vm);
+      if (c0 + 16 >= j1) break;
+      vm = park(kB, vB);
+      rid_next = rid_after;
+      rid_after = slot_row(c0 + 48);
+      vA = fetch(rid_next, kA);
+      step(vm);
+      if (c0 + 32 >= j1) break;
+      vm = park(kA, vA);
+    }
   }
 
   // oacc[mt][i] = O^T[dv = 16mt + 4g + i][head n16]
   if constexpr (WPI > 1) {
     // merge the waves: common max per head, rescale, then sum the
     // accumulators pairwise through LDS (waves 2,3 -> 0,1, then 1 -> 0)
-    float* st_m = reinterpret_cast<float*>(smem + AttnLds<MT>::stat_off);
+    float* st_m = reinterpret_cast<float*>(smem + L::stat_off);
     float* st_l = st_m + kWavesPerWG * 16;
     f32x4* buf = reinterpret_cast<f32x4*>(smem);
     __syncthreads();                          // every wave is done with its tile
@@ -325,7 +433,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int Dv) {
 
 template <int KS, int MT, int WPI>
 hipError_t launch_attn_w(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = WPI == 1 ? (size_t)kWavesPerWG * VTile<MT>::bytes : (size_t)AttnLds<MT>::bytes;
+  const size_t lds = (size_t)AttnLds<KS, MT>::bytes;
   const void* fn = reinterpret_cast<const void*>(&sparse_attn_kernel<KS, MT, WPI>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
