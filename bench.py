@@ -204,8 +204,14 @@ def _mm(path):
 
 
 def _worker_init():
+    # one BLAS thread per worker process: the variables must be set before
+    # numpy loads its BLAS (the workers are forked before the parent imports
+    # numpy), and threadpool_limits then covers a BLAS already loaded
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401
     from threadpoolctl import threadpool_limits
-    globals()["_LIMIT"] = threadpool_limits(limits=1)      # one BLAS thread per worker process
+    globals()["_LIMIT"] = threadpool_limits(limits=1)
 
 
 def _task_indexer(job):
@@ -238,6 +244,11 @@ def _task_attention(job):
     kvg = _mm(job["kv"])[job["r0"]:job["r1"]]                      # [R, k, D]
     o, _ = O.sparse_attention(job["Q"], kvg, job["slot"], kvg.shape[1], job["sm"], job["d_v"])
     return job["tag"], o, time.perf_counter() - t0
+
+
+def _worker_blas():
+    from threadpoolctl import threadpool_info
+    return [(p.get("internal_api"), p.get("num_threads")) for p in threadpool_info() if p.get("user_api") == "blas"]
 
 
 def cpu_info():
@@ -394,6 +405,7 @@ def sampled_parity(w, inp, rows, cb, torch):
 
 
 def cpu_block(value, unit, pool, info, sample):
+    info = dict(info, worker_blas_threads=pool.pool.apply(_worker_blas))
     return {"value": value, "unit": unit, "cores": pool.n, "kind": "oracle", "sample": sample,
             "workers": f"{pool.n} processes x 1 BLAS thread (capped at the {HOST_CPU_SHARE}-core CPU share "
                        f"of one GPU, or the cores this process may run on)", "host": info}
