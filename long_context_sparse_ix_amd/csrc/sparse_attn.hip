@@ -19,19 +19,26 @@
 //     pieces spread the way the MFMA operand wants them, 16 rows per
 //     instruction, the L1's tag rate bounded the kernel).  Two named register
 //     buffers alternate, so the next step's rows are in flight while this
-//     step computes, and index words are loaded two steps ahead;
+//     step computes, and index words are loaded two steps ahead.  The
+//     buffers and the query slice are held in AGPRs (MFMA operands and LDS
+//     stores may come from either register file), the output accumulators
+//     and the LDS operand reads in VGPRs;
 //   * each step parks its rows in a wave-private LDS tile (one 16-byte store
 //     per register) whose row stride is 8 or 40 (mod 64) dwords, so the
 //     transposed value reads and the key-operand reads below are
 //     bank-conflict free.  (Direct HBM -> LDS loads of the same tile measured
 //     about 40% slower than this register path at L = 128K.)
 //   * S^T = KV . Q^T with v_mfma_f32_16x16x32_bf16 (M = keys, N = heads, the
-//     query slice stays in VGPRs; the key operand is read from the tile), so
-//     lane l ends with 4 logits of head l%16 -- exactly the B-operand layout
-//     of the P.V product below;
+//     query slice stays in registers; the key operand is read from the tile
+//     several MFMAs ahead of its use), so lane l ends with 4 logits of head
+//     l%16 -- exactly the B-operand layout of the P.V product below;
 //   * the value part of the 16 rows is read straight from the tile by
 //     ds_read_b64_tr_b16 (lane (dv, key group) gets 4 keys of one value dim)
-//     as the A operand of O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16);
+//     as the A operand of O^T = V^T . P^T (v_mfma_f32_16x16x16_bf16), also
+//     read ahead of use.  (Without the read-ahead every MFMA waited for its
+//     own LDS read: about 4,000 cycles per step against about 550 of MFMA
+//     work.  A second tile per wave, with two steps of gathers in flight,
+//     measured no faster, and neither did four waves per row.)
 //   * online softmax in base 2 against a reference max that may trail the
 //     running max by up to 2^8, so the accumulators are rescaled only when a
 //     head's max jumps further (rarely);
@@ -101,6 +108,12 @@ struct GTileLatent {
   __device__ static __forceinline__ int v_off(int row) { return row * RSV; }
 };
 
+// LDS operand reads issued ahead of their MFMAs, and the instruction classes
+// of the scheduling-group hints that place them (AMDGPU sched_group_barrier
+// masks)
+constexpr int kQkAhead = 6, kPvAhead = 8;
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
 template <int KS, int MT>
 struct TileOf {
   using type = GTile<KS>;
@@ -130,7 +143,9 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   using L = AttnLds<KS, MT>;
   static_assert(WPI == 1 || WPI == kWavesPerWG, "a (row, split) has one wave or the whole workgroup");
   extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  // the wave index is uniform across the wave; saying so keeps the slot
+  // range scalar and the loop exits uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int n16 = l & 15, g = l >> 4;
   const int item = WPI == 1 ? blockIdx.x * kWavesPerWG + wave : blockIdx.x;
   if (item >= a.rows * a.splits) return;     // whole workgroup when WPI > 1
@@ -147,6 +162,10 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks) : bf16x8{};
+    // register-class hint: the query slice stays in AGPRs (an MFMA operand
+    // may come from either file)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[ks]));
   }
 
   int j0 = sp * a.slots_per_split;
@@ -169,16 +188,15 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   // would stall each step on the next step's prefetch.  An index word past
   // the range reads an in-row slot and becomes -1; an invalid slot gathers
   // row 0, whose logit is masked to -inf and whose value row is weighted by 0.
-  // Lane n16 (every g) holds the id of slot c0 + n16.
-  auto slot_row = [&](int c0) -> int {
-    const int slot = c0 + n16;
-    const int v = irow[min(slot, a.k - 1)];
-    return slot < j1 ? v : -1;
-  };
-  // The 16 latent rows of a step into register buffer kf; returns whether
-  // this lane's slot (n16) is valid.
-  auto fetch = [&](int rid, bf16x8 (&kf)[G::NI]) -> bool {
-    const bool valid = rid >= 0 && (int64_t)rid < a.kv_len;
+  // Lane n16 (every g) loads the index word of slot c0 + n16; the word is
+  // checked only when its step is gathered (a check right after the load
+  // would wait for it, and loads complete in order, so for every gather
+  // issued before it).
+  auto slot_word = [&](int c0) -> int { return irow[min(c0 + n16, a.k - 1)]; };
+  // The 16 latent rows of the step at slot c0 (index word rid) into register
+  // buffer kf; returns whether this lane's slot (n16) is valid.
+  auto fetch = [&](int c0, int rid, bf16x8 (&kf)[G::NI]) -> bool {
+    const bool valid = c0 + n16 < j1 && rid >= 0 && (int64_t)rid < a.kv_len;
     const int rid_c = valid ? rid : 0;
     int rs[16];
 #pragma unroll
@@ -210,9 +228,15 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
 
   // Park a step's gathered rows kf in the tile (nothing when no slot is
   // valid); returns the valid-slot mask (bit n: slot n, from lanes 0..15).
-  // The stores follow the previous step's tile reads in program order, and a
-  // wave's LDS operations complete in order, so one tile suffices.
-  auto park = [&](const bf16x8 (&kf)[G::NI], bool valid) -> uint32_t {
+  // The stores follow the last reads of that tile in program order, and a
+  // wave's LDS operations complete in order.
+  auto park = [&](bf16x8 (&kf)[G::NI], bool valid, unsigned char* tile) -> uint32_t {
+    // Register-class hint: the buffers live in AGPRs (the loads write them
+    // there, the stores read them there), leaving the VGPRs to the output
+    // accumulators and the read-ahead of the LDS operands.  The empty asm
+    // reads the gathered values, which the stores below wait for anyway.
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) asm volatile("" : "+a"(kf[j]));
     const uint32_t vm = (uint32_t)__ballot(valid) & 0xFFFFu;
     if (vm == 0u) return 0u;
     if constexpr (G::kLatent) {
@@ -231,19 +255,31 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     return vm;
   };
 
-  // One 16-slot step on the parked tile: S^T = KV . Q^T, online softmax,
+  // One 16-slot step on a parked tile: S^T = KV . Q^T, online softmax,
   // O^T += V^T . P^T.
-  auto step = [&](uint32_t vm) {
+  auto step = [&](uint32_t vm, const unsigned char* tile) {
     if (vm == 0u) return;
-    // two independent accumulator chains (even and odd k-steps)
-    f32x4 sa = f32x4{}, sb = f32x4{};
+    // one accumulator chain, so the MFMAs consume the key operand reads in
+    // the order they are issued (LDS reads complete in order; a chain taken
+    // out of that order waits for every earlier read); the reads run
+    // kQkAhead MFMAs ahead of their use (left alone, the compiler waits for
+    // each read right before its MFMA)
+    f32x4 sacc = f32x4{};
+    {
+      constexpr int A = KS < kQkAhead ? KS : kQkAhead;
+      bf16x8 kk[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(tile + G::qk_off(n16, ks, g));
-      if (ks & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[ks], sb, 0, 0, 0);
-      else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[ks], sa, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) kk[ks] = *reinterpret_cast<const bf16x8*>(tile + G::qk_off(n16, ks, g));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[ks], qf[ks], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
+#pragma unroll
+      for (int i = 0; i < KS - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, A, 0);
     }
-    const f32x4 sacc = sa + sb;
     float z[4];
     float cmax = -INFINITY;
 #pragma unroll
@@ -282,12 +318,23 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
     // transposed read: lane (n16, g) supplies 4 value dims of key 4g + n16/4
     // and receives value dim 16mt + n16 of keys 4g .. 4g+3
     const uint16_t* vrow = reinterpret_cast<const uint16_t*>(tile + G::v_off(4 * g + (n16 >> 2))) + 4 * (n16 & 3);
-    v4s_t vt[MT];
+    // the value reads run kPvAhead MFMAs ahead of their use
+    {
+      constexpr int A = MT < kPvAhead ? MT : kPvAhead;
+      v4s_t vt[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
+      for (int mt = 0; mt < MT; ++mt) vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(vrow + 16 * mt));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[mt]), pb, oacc[mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt)
+        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[mt]), pb, oacc[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 1);
+#pragma unroll
+      for (int i = 0; i < MT - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, A, 1);
+    }
     // the next step's stores come after these reads (in-order LDS); keep
     // the compiler from moving them above
     asm volatile("" ::: "memory");
@@ -299,24 +346,23 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   // A loop-carried copy of the buffer would make the compiler wait for those
   // gathers at every step.
   bf16x8 kA[G::NI], kB[G::NI];
-  bool vA = fetch(slot_row(j0), kA), vB = false;
-  int rid_after = slot_row(j0 + 16);             // -1 past the range
+  bool vA = fetch(j0, slot_word(j0), kA), vB = false;
+  int r1 = slot_word(j0 + 16);
   if (j0 < j1) {
-    uint32_t vm = park(kA, vA);
+    uint32_t vm = park(kA, vA, tile);
     for (int c0 = j0;; c0 += 32) {
-      // prefetch: latent rows of the next step, index words of the one after
-      int rid_next = rid_after;
-      rid_after = slot_row(c0 + 32);
-      vB = fetch(rid_next, kB);
-      step(vm);
+      int rn = r1;
+      r1 = slot_word(c0 + 32);
+      vB = fetch(c0 + 16, rn, kB);
+      step(vm, tile);
       if (c0 + 16 >= j1) break;
-      vm = park(kB, vB);
-      rid_next = rid_after;
-      rid_after = slot_row(c0 + 48);
-      vA = fetch(rid_next, kA);
-      step(vm);
+      vm = park(kB, vB, tile);
+      rn = r1;
+      r1 = slot_word(c0 + 48);
+      vA = fetch(c0 + 32, rn, kA);
+      step(vm, tile);
       if (c0 + 32 >= j1) break;
-      vm = park(kA, vA);
+      vm = park(kA, vA, tile);
     }
   }
 
