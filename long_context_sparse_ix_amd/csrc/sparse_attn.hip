@@ -155,17 +155,15 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
 
   // Query slice as the B operand: head n16, elements [32ks + 8g, +8) -- the
   // MFMA's k-group g of step ks; the key operand is read the same way.
+  // Lanes of heads past Hq load head 0's query (in bounds, finite): their
+  // logits and outputs are never stored.  The loads are unconditional, so no
+  // branch splits them.
   const bool hq_ok = n16 < a.Hq;
   bf16x8 qf[KS];
   {
     const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = hq_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks) : bf16x8{};
-    // register-class hint: the query slice stays in AGPRs (an MFMA operand
-    // may come from either file)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[ks]));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
 
   int j0 = sp * a.slots_per_split;
@@ -345,24 +343,35 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   // previous step's compute is issued, so the stores overlap its P.V MFMAs.
   // A loop-carried copy of the buffer would make the compiler wait for those
   // gathers at every step.
+  // The first two steps' gathers are issued together, so the second does not
+  // wait for the first to land (a decode wave walks only a few steps).
   bf16x8 kA[G::NI], kB[G::NI];
-  bool vA = fetch(j0, slot_word(j0), kA), vB = false;
-  int r1 = slot_word(j0 + 16);
+  const int w0 = slot_word(j0), w1 = slot_word(j0 + 16);
+  int r1 = slot_word(j0 + 32), r2 = slot_word(j0 + 48);
+  bool vA = fetch(j0, w0, kA);
+  bool vB = fetch(j0 + 16, w1, kB);
   if (j0 < j1) {
     uint32_t vm = park(kA, vA, tile);
+    // Register-class hint: the query slice stays in AGPRs (an MFMA operand may
+    // come from either file).  The empty asm reads it, so it sits after the
+    // first park, which has waited for every earlier load anyway; placed at the
+    // query loads it held the index words and the first gathers behind them.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[ks]));
     for (int c0 = j0;; c0 += 32) {
-      int rn = r1;
-      r1 = slot_word(c0 + 32);
-      vB = fetch(c0 + 16, rn, kB);
+      // tile: step c0; kB: step c0+16 in flight; r1, r2: index words of c0+32, c0+48
       step(vm, tile);
       if (c0 + 16 >= j1) break;
       vm = park(kB, vB, tile);
-      rn = r1;
-      r1 = slot_word(c0 + 48);
-      vA = fetch(c0 + 32, rn, kA);
+      vA = fetch(c0 + 32, r1, kA);
+      r1 = r2;
+      r2 = slot_word(c0 + 64);
       step(vm, tile);
       if (c0 + 32 >= j1) break;
       vm = park(kA, vA, tile);
+      vB = fetch(c0 + 48, r1, kB);
+      r1 = r2;
+      r2 = slot_word(c0 + 80);
     }
   }
 
