@@ -6,9 +6,12 @@
 // but for workloads with only a handful of query rows (decode: one row per
 // sequence) there is nothing to share across rows, so the key range of every
 // row is split over many waves instead and each wave streams its own keys
-// straight from HBM into MFMA B operands (no LDS).  fp8 e4m3fn keys are
-// widened to bf16 in registers (exact) and the per-key scale is applied to the
-// finished score.  The rows are then reduced by the per-row top-k: for rows of
+// from HBM into MFMA B operands.  fp8 keys of width 128 load coalesced (1 KB
+// per instruction) and pass through a small wave-private LDS transpose;
+// other widths load each lane's key directly.  fp8 e4m3fn keys are widened
+// to bf16 in registers (exact) and the per-key scale is applied to the
+// finished score.  The row's head weights sit in LDS, shared by the
+// workgroup's four waves.  The rows are then reduced by the per-row top-k: for rows of
 // at most 512 waves' spans, each wave first keeps the best of its own 640
 // scores for the row's candidate list (the top-k's wave-local stage, run here
 // as the epilogue on the scores just written), so the top-k itself is one
@@ -42,6 +45,12 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   const int b = row / a.n_q, t = row % a.n_q;
   const int64_t p = seq_start(a.seq_q_start, b, a.q_start) + t;
   const int64_t s_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kTilesPerWave * kTileKeys;
+  // The row's head weights sit in LDS (all four waves score the same row)
+  // rather than in 32 registers per lane.  Filled before any wave leaves.
+  __shared__ __align__(16) float w_lds[HT * 32];
+  for (int i = threadIdx.x; i < HT * 32; i += kWavesPerWG * kWave)
+    w_lds[i] = i < a.H ? a.w[(int64_t)row * a.H + i] : 0.0f;
+  __syncthreads();
   if (s_begin > p) return;
   const int n_tiles = (int)min<int64_t>(kTilesPerWave, (p - s_begin) / kTileKeys + 1);
 
@@ -53,11 +62,28 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   // s0 + l.  kDepth - 1 tiles are in flight while one is widened and used.
   constexpr int RAW = FP8 ? (KS % 2 == 0 ? KS / 2 : KS) : KS;   // 16-byte (or 8-byte) pieces per half
   typedef typename std::conditional<FP8 && (KS % 2 != 0), u32x2, u32x4>::type piece_t;
+  // fp8 keys of d = 128 (128 bytes a key) load coalesced: piece c of half nt
+  // is the c-th kilobyte of the half tile's 32 keys (lane l: key 8c + l/8,
+  // bytes 16 (l%8) ..), and an LDS transpose gives each lane its key's bytes.
+  // Lane-per-key loads touched 32 cache lines per instruction and kept the
+  // texture addresser ~87% busy.
+  constexpr bool kCoal = FP8 && KS == 8;
   piece_t raw[kDepth][2][RAW];
   float sc[kDepth];
   auto load_raw = [&](int64_t s0, piece_t (&rw)[2][RAW], float& scl) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
+      if constexpr (kCoal) {
+        // 32-bit offsets from the wave's (uniform) first key: a wave's span is
+        // 640 keys, so they stay small whatever the context length
+        const unsigned char* kb = static_cast<const unsigned char*>(a.keys) + (int64_t)b * a.key_bstride + s_begin * d;
+        const uint32_t lim = (uint32_t)min<int64_t>((p - s_begin) * d + d - 16, (int64_t)UINT32_MAX);
+        const uint32_t off0 = (uint32_t)((s0 - s_begin + nt * 32) * d) + 16u * (uint32_t)l;
+#pragma unroll
+        for (int c = 0; c < RAW; ++c)   // keys past p read key p's last piece (inside the cache; masked below)
+          rw[nt][c] = *reinterpret_cast<const piece_t*>(kb + min(off0 + 1024u * c, lim));
+        continue;
+      }
       int64_t s = s0 + nt * 32 + m;
       if (s > p) s = p;                       // stays inside the cache; masked below
       const unsigned char* kr = static_cast<const unsigned char*>(a.keys) +
@@ -91,7 +117,6 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   };
 
   bf16x8 qf[HT][KS];
-  float wr[HT][16];
   {
     const uint16_t* qrow = a.q + (int64_t)row * a.H * d;
 #pragma unroll
@@ -101,11 +126,6 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
       for (int ks = 0; ks < KS; ++ks)
         qf[ht][ks] = h < a.H ? *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks)
                              : bf16x8{};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hh = ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        wr[ht][r] = hh < a.H ? a.w[(int64_t)row * a.H + hh] : 0.0f;
-      }
     }
   }
 
@@ -114,6 +134,32 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   // waits drain every load in flight, the prefetched tiles included.
 #pragma unroll
   for (int j = 0; j < kDepth - 1; ++j) load_raw(s_begin + (int64_t)j * kTileKeys, raw[j], sc[j]);
+
+  // kCoal transpose buffer, private to the wave: key r's 16-byte piece c sits
+  // in slot c ^ ((r >> 1) & 7) of its 128-byte row, so both the stores (two
+  // keys per 16 lanes) and the reads (16 keys per 16 lanes) fall in distinct
+  // banks.
+  __shared__ __align__(16) u32x4 tbuf[kWavesPerWG][kCoal ? 512 : 1];
+  u32x4* const tb = tbuf[wave];
+  auto park_tile = [&](const piece_t (&rw)[2][RAW]) {
+    if constexpr (kCoal) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int c = 0; c < RAW; ++c) {
+          const int r = 8 * c + (l >> 3);
+          tb[nt * 256 + r * 8 + ((l & 7) ^ ((r >> 1) & 7))] = rw[nt][c];
+        }
+      wave_lds_sync();                         // this wave's stores, then other lanes' reads
+    }
+  };
+  // this lane's key (m) bytes [64 hf, +64) of half nt, from the parked tile
+  auto half_pieces = [&](int nt, piece_t (&pc)[RAW]) {
+    if constexpr (kCoal) {
+#pragma unroll
+      for (int cc = 0; cc < RAW; ++cc) pc[cc] = tb[nt * 256 + m * 8 + ((4 * hf + cc) ^ ((m >> 1) & 7))];
+    }
+  };
 
   float smin = INFINITY, smax = -INFINITY;     // range of this wave's scores
   float kept[kTilesPerWave] = {};               // this lane's score of every tile (top-k stage)
@@ -129,6 +175,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
         const int jn = j + kDepth - 1;
         load_raw(s_begin + (int64_t)jn * kTileKeys, raw[(u + kDepth - 1) % kDepth], sc[(u + kDepth - 1) % kDepth]);
         const int64_t s0 = s_begin + (int64_t)j * kTileKeys;
+        park_tile(raw[u]);
         // the two 32-key halves one after the other: only one half's B
         // fragments and accumulators are live, which leaves room for two
         // waves per SIMD (one computes while the other waits on its keys)
@@ -136,7 +183,13 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           bf16x8 bfr[KS];
-          widen(raw[u][nt], bfr);
+          if constexpr (kCoal) {
+            piece_t pc[RAW];
+            half_pieces(nt, pc);
+            widen(pc, bfr);
+          } else {
+            widen(raw[u][nt], bfr);
+          }
           f32x16 acc[HT];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
@@ -148,7 +201,13 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r & 3] = fmaf(wr[ht][r], relu(acc[ht][r]), sacc[r & 3]);
+            for (int r4 = 0; r4 < 4; ++r4) {
+              // weights of heads ht*32 + 8 r4 + 4 hf + (0..3): accumulator
+              // rows 4 r4 .. 4 r4 + 3 of this lane
+              const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + ht * 32 + 8 * r4 + 4 * hf);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sacc[i] = fmaf(wv[i], relu(acc[ht][4 * r4 + i]), sacc[i]);
+            }
           part[nt] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
@@ -160,7 +219,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
         if (j < kTilesPerWave) kept[j < kTilesPerWave ? j : 0] = FP8 ? score * sc[u] : score;
         if (s <= p) {
           if constexpr (FP8) score *= sc[u];
-          out[s] = score;
+          out[(uint32_t)s] = score;             // 32-bit index off a wave-uniform base
           smin = fminf(smin, score);
           smax = fmaxf(smax, score);
         }
