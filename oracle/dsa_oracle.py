@@ -36,7 +36,11 @@ Readings taken where the pages are silent:
 * sequences of different lengths in one batch: row t of sequence b sits at
   its own start q_start[b] + t, with the same candidate rule;
 * MTP draft steps after the first attend over the first step's positions in
-  the first step's KV cache, so no position a later step adds is selected.
+  the first step's KV cache, so no position a later step adds is selected;
+* the indexer's inputs from hidden states (IndexCache notes, section 1: a
+  small low-rank indexer with few heads): one bf16 input row x per query and
+  one bf16 weight W of H*d + H rows give [q_I | w] = x . W^T; q_I is rounded
+  to bf16 (nearest, ties to the even pattern), the head weights stay wide.
 """
 from __future__ import annotations
 
@@ -45,7 +49,8 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "key_matrix", "indexer_scores", "select_topk",
     "indexer_topk", "indexer_topk_rows", "attention_row", "sparse_attention", "group_forward",
-    "mtp_draft", "index_overlap", "encode_e4m3fn", "quantize_key_rows",
+    "mtp_draft", "index_overlap", "encode_e4m3fn", "quantize_key_rows", "encode_bf16",
+    "indexer_project",
 ]
 
 
@@ -128,6 +133,43 @@ def quantize_key_rows(k_rows):
     scale = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
     y = (k / scale[..., None]).astype(np.float32)
     return encode_e4m3fn(y), scale
+
+
+# ---------------------------------------------------------- indexer inputs --
+def encode_bf16(x) -> np.ndarray:
+    """finite float values -> bf16 bit patterns (uint16), round to nearest with
+    ties to the pattern whose last bit is 0.
+
+    bf16 keeps 8 significant bits.  A nonzero v = f * 2^e with 0.5 <= |f| < 1
+    is rounded as an integer multiple of 2^(e - 8) (a power-of-two scaling,
+    exact in float64); np.rint rounds halves to even, and an even multiple is
+    a pattern with last bit 0.  The rounded value is a bf16 value, so its
+    float32 image carries the pattern in its upper 16 bits.  (Values below
+    the normal range do not occur in this library's uses.)"""
+    v = np.asarray(x, dtype=np.float64)
+    f, e = np.frexp(v)
+    step = np.ldexp(1.0, e - 8)
+    r = np.where(v == 0.0, v, np.rint(v / step) * step)
+    bits = r.astype(np.float32).view(np.uint32) >> np.uint32(16)
+    return bits.astype(np.uint16)
+
+
+def indexer_project(x_bits, w_bits, heads: int, dim: int):
+    """Indexer queries and head weights from hidden-state rows.
+
+    x_bits: bf16 patterns [rows, d_in]; w_bits: bf16 patterns [heads*dim +
+    heads, d_in] (one row per output column).  y = x . W^T in float64; the
+    first heads*dim columns, rounded to bf16, are q_I [rows, heads, dim]
+    (uint16 patterns); the last heads columns are w [rows, heads] (float64).
+    IndexCache notes, section 1 (a small low-rank indexer with few heads);
+    the shapes and the single input are this library's reading."""
+    X = decode_bf16(x_bits)
+    W = decode_bf16(w_bits)
+    if W.shape[0] != heads * dim + heads or W.shape[1] != X.shape[-1]:
+        raise ValueError("w must be [heads*dim + heads, d_in]")
+    Y = X @ W.T
+    q = encode_bf16(Y[..., : heads * dim]).reshape(X.shape[:-1] + (heads, dim))
+    return q, Y[..., heads * dim:]
 
 
 # ----------------------------------------------------------------- indexer --

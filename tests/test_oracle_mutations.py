@@ -92,6 +92,18 @@ def _quantize_fnuz_max(k_rows):
     return O.encode_e4m3fn((k / scale[..., None]).astype(np.float32)), scale
 
 
+def _bf16_truncate(x):
+    v = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _project_weights_first(x_bits, w_bits, heads, dim):
+    X, W = O.decode_bf16(x_bits), O.decode_bf16(w_bits)
+    Y = X @ W.T
+    q = O.encode_bf16(Y[..., heads:]).reshape(X.shape[:-1] + (heads, dim))
+    return q, Y[..., :heads]
+
+
 ATTN = O.attention_row
 INDEXER = O.indexer_topk
 
@@ -111,6 +123,8 @@ MUTATIONS = [
     ("overlap_slotwise", "index_overlap", _overlap_slotwise, P.test_overlap_shifted_ranges_closed_form),
     ("e4m3_ties_away", "encode_e4m3fn", _encode_ties_away, P.test_e4m3fn_encode_matches_torch_on_grid_and_midpoints),
     ("quantize_fnuz_range", "quantize_key_rows", _quantize_fnuz_max, P.test_quantize_rows_closed_forms),
+    ("bf16_truncate", "encode_bf16", _bf16_truncate, P.test_projection_rounds_midpoints_to_even),
+    ("project_weights_first", "indexer_project", _project_weights_first, P.test_hand_worked_projection),
 ]
 
 

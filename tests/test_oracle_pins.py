@@ -501,3 +501,68 @@ def test_quantize_rows_error_bound():
     back = O.decode_e4m3fn(codes)
     tol = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10)
     assert np.all(np.abs(back - y) <= tol)
+
+
+# ------------------------------------------------- indexer inputs (f1 opt) --
+def test_bf16_encode_matches_torch_on_random_values_and_midpoints():
+    """encode_bf16 (round to nearest, ties to even) against torch's float32 ->
+    bfloat16 conversion: random float32 values over many binades, the exact
+    midpoints between neighbouring bf16 values, and the floats just beside
+    them."""
+    rng = np.random.default_rng(11)
+    mags = np.ldexp(rng.uniform(1.0, 2.0, 4000), rng.integers(-60, 60, 4000))
+    v = (mags * rng.choice([-1.0, 1.0], 4000)).astype(np.float32)
+    lo = O.decode_bf16(O.encode_bf16(v.astype(np.float64)))          # some bf16 values
+    ulp = np.ldexp(1.0, np.frexp(lo)[1] - 8)
+    mid = (lo + 0.5 * ulp).astype(np.float32)                          # exact in float32
+    beside = np.concatenate([np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(-np.inf))])
+    for vals in (v, mid, beside.astype(np.float32)):
+        got = O.encode_bf16(vals.astype(np.float64))
+        ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_hand_worked_projection():
+    g = gold()["project"]
+    x = np.asarray(g["x"], dtype=np.float64)
+    w = np.asarray(g["w_proj"], dtype=np.float64)
+    q, wt = O.indexer_project(O.encode_bf16(x), O.encode_bf16(w), g["heads"], g["dim"])
+    np.testing.assert_array_equal(O.decode_bf16(q), np.asarray(g["q"]))
+    np.testing.assert_array_equal(wt, np.asarray(g["w"]))
+
+
+def test_projection_one_hot_rows_select_weight_columns():
+    """x = e_j picks column j of W: every output is a stored bf16 weight, so
+    q reproduces its bit pattern and w its value."""
+    rng = np.random.default_rng(5)
+    H, d, d_in = 3, 4, 16
+    wb = O.encode_bf16(rng.normal(size=(H * d + H, d_in)))
+    xb = O.encode_bf16(np.eye(d_in))
+    q, wt = O.indexer_project(xb, wb, H, d)
+    np.testing.assert_array_equal(q.reshape(d_in, H * d), wb[: H * d].T)
+    np.testing.assert_array_equal(wt, O.decode_bf16(wb[H * d:]).T)
+
+
+def test_projection_rounds_midpoints_to_even():
+    """x = [1, 2^-8]: W row [1, 1] gives 1 + 2^-8, halfway between 1 and
+    1 + 2^-7, which rounds to 1 (even pattern); W row [1, 3] gives
+    1 + 3*2^-8, halfway between 1 + 2^-7 and 1 + 2^-6, which rounds up to
+    1 + 2^-6; the head-weight column [2, 0] stays 2."""
+    xb = O.encode_bf16(np.array([[1.0, 2.0 ** -8]]))
+    wb = O.encode_bf16(np.array([[1.0, 1.0], [1.0, 3.0], [2.0, 0.0]]))
+    q, wt = O.indexer_project(xb, wb, 1, 2)
+    np.testing.assert_array_equal(O.decode_bf16(q)[0, 0], [1.0, 1.0 + 2.0 ** -6])
+    np.testing.assert_array_equal(wt, [[2.0]])
+
+
+def test_projection_head_weights_scale_exactly():
+    """Scaling x by a power of two scales the head weights exactly (and q up
+    to its own rounding, which a power of two does not change)."""
+    rng = np.random.default_rng(9)
+    H, d, d_in = 2, 4, 32
+    wb = O.encode_bf16(rng.normal(size=(H * d + H, d_in)))
+    x = rng.normal(size=(5, d_in))
+    q1, w1 = O.indexer_project(O.encode_bf16(x), wb, H, d)
+    q2, w2 = O.indexer_project(O.encode_bf16(4.0 * O.decode_bf16(O.encode_bf16(x))), wb, H, d)
+    np.testing.assert_array_equal(w2, 4.0 * w1)
+    np.testing.assert_array_equal(O.decode_bf16(q2), 4.0 * O.decode_bf16(q1))
