@@ -432,7 +432,7 @@ def main(argv=None):
                     help="write a kernel's traffic summary from two rocprofv3 --pmc output dirs")
     ap.add_argument("--traffic-op", choices=sorted(TRAFFIC_OPS), default="attention")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
-    ap.add_argument("--op", choices=["indexer", "argmax", "attention"],
+    ap.add_argument("--op", choices=["indexer", "argmax", "attention", "project"],
                     help="time one op of the workload's first layer alone (warmup + steps launches), for profiling")
     args = ap.parse_args(argv)
     if args.write_traffic:
@@ -553,6 +553,9 @@ def run(args, pool):
                    "us": ov_ms * 1e3, "rows_per_s": w.batch * w.n_q / (ov_ms / 1e3),
                    "note": "independent synthetic layers: about k / candidates expected"}
 
+    log("indexer projection")
+    project = project_leg(w, torch, synth, ix, args.kernel_reps)
+
     allf_ms = None
     if not args.no_all_full:
         log("all-full baseline")
@@ -626,6 +629,7 @@ def run(args, pool):
                             "rows_per_s": dk.batch / (tk_ms / 1e3),
                             "frac_hbm_peak": tk_bytes / (tk_ms / 1e3) / 1e9 / PEAK_HBM_GBPS},
         "index_overlap": overlap,
+        "project": project,
         "group": {"ms_fsss": ms_step / n_groups, "ms_all_full": None if allf_ms is None else allf_ms / n_groups,
                   "speedup_vs_all_full": None if allf_ms is None else allf_ms / ms_step},
         "cpu_baseline": result_cpu,
@@ -646,12 +650,42 @@ def copy_calibration(torch):
     torch.cuda.synchronize()
 
 
+def project_leg(w, torch, synth, ix, reps):
+    """The indexer projection (q_I and head weights from hidden states) at the
+    workload's rows: time, TFLOP/s against the bf16 MFMA peak."""
+    x, wp = synth.projection_inputs(w, "cuda")
+    rows, d_in = x.shape
+    q = torch.empty((rows, w.ix_heads, w.ix_dim), dtype=torch.bfloat16, device="cuda")
+    wo = torch.empty((rows, w.ix_heads), dtype=torch.float32, device="cuda")
+    fn = lambda: ix.ix_indexer_project(x, wp, q, wo, heads=w.ix_heads, dim=w.ix_dim)
+    fn()
+    ms = event_time(torch, fn, reps)
+    flop = 2.0 * rows * wp.shape[0] * d_in
+    tflops = flop / (ms / 1e3) / 1e12
+    return {"shape": f"{rows} x {d_in} -> {w.ix_heads} x {w.ix_dim} + {w.ix_heads}", "ms": ms, "us": ms * 1e3,
+            "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+            "weight_GBps": wp.numel() * 2 / (ms / 1e3) / 1e9,
+            "note": "ix_indexer_project: one GEMM on bf16 MFMA, q_I rounded to bf16, head weights fp32"}
+
+
 def bench_op(args, w, torch, synth, ix):
     """One op of the first layer, launched warmup + steps times: the indexer
     (+ fused top-k), the same score stream with a running maximum
     (ix_indexer_argmax), or the sparse attention over the indexer's
     positions."""
     dev = "cuda"
+    if args.op == "project":
+        x, wp = synth.projection_inputs(w, dev)
+        pq = torch.empty((x.shape[0], w.ix_heads, w.ix_dim), dtype=torch.bfloat16, device=dev)
+        pw = torch.empty((x.shape[0], w.ix_heads), dtype=torch.float32, device=dev)
+        fn = lambda: ix.ix_indexer_project(x, wp, pq, pw, heads=w.ix_heads, dim=w.ix_dim)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
+        print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
+                          "ms_per_launch": ms}), flush=True)
+        return 0
     q, wt = synth.indexer_queries(w, dev, 0)
     keys, scale = synth.indexer_keys(w, dev, 0)
     idx = torch.empty((w.batch, w.n_q, w.k), dtype=torch.int32, device=dev)
@@ -835,6 +869,8 @@ def bench_decode(args, w, torch, synth, ix, pool):
     attention = {"us_per_layer": at_ms * 1e3, "gathered_GBps": at_bytes / (at_ms / 1e3) / 1e9,
                  "gathered_bytes": at_bytes}
 
+    project = project_leg(w, torch, synth, ix, 50)
+
     result_cpu, parity = None, None
     if pool is not None:
         result_cpu, parity = decode_oracle_leg(w, torch, keys, scale, kvs, steps[j_last], last, j_last, log, pool)
@@ -847,7 +883,7 @@ def bench_decode(args, w, torch, synth, ix, pool):
            "roofline": roofline, "cpu_baseline": result_cpu, "parity": parity,
            "append_keys_us": app_ms * 1e3, "attention": attention,
            "group": {"ms_fsss": ms, "ms_all_full": allf, "speedup_vs_all_full": allf / ms},
-           "varlen": varlen, "mtp_draft": mtp,
+           "varlen": varlen, "mtp_draft": mtp, "project": project,
            "indexer_key_GBps_lower_bound": key_bytes / (ms / 1e3) / 1e9}
     print(json.dumps(out))
     return 0

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 5
+#define IX_ABI_VERSION 6
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -292,6 +292,30 @@ int32_t ix_index_overlap(const ix_problem* prob, const int32_t* idx_a, const int
  * IX_E_NULL on a NULL pointer, IX_E_SHAPE on a bad size or alignment. */
 int32_t ix_append_keys(const ix_problem* prob, int32_t dim, const float* k_new, int32_t n_new, int64_t pos,
                        uint8_t* k_cache, float* k_scale, void* stream);
+
+/* Indexer inputs from hidden states.  The pages describe the indexer as a
+ * small low-rank module with few heads (IndexCache notes, section 1); this
+ * library's reading is one bf16 input row per query and one bf16 weight:
+ *   y[r][n] = sum_j x[r][j] * w_proj[n][j]   (fp32 accumulation),
+ *   q_out[r][h][i] = bf16(y[r][h*dim + i])   (nearest, ties to even),
+ *   w_out[r][h]    = y[r][heads*dim + h]     (fp32),
+ * i.e. the q and w arguments of ix_indexer_topk for these rows. */
+typedef struct ix_project_in {
+  int32_t heads;          /* H >= 1                                           */
+  int32_t dim;            /* d >= 1                                           */
+  int32_t d_in;           /* input width, a multiple of 64 in [64, 2^22)      */
+  int32_t reserved;       /* must be 0                                        */
+  const void* x;          /* bf16 [rows][d_in], 16-byte aligned               */
+  const void* w_proj;     /* bf16 [heads*dim + heads][d_in], 16-byte aligned  */
+} ix_project_in;
+
+/* Computes q_out (bf16 [rows][heads][dim], 2-byte aligned) and w_out (fp32
+ * [rows][heads], 4-byte aligned) from in (see above).  rows >= 0 (0 does
+ * nothing); heads*dim + heads < 2^31; ceil(rows/64) * ceil((heads*dim +
+ * heads)/64) < 2^31.  Caller-owned buffers, no workspace.
+ * IX_E_NULL on a NULL pointer, IX_E_SHAPE on a bad size, a nonzero reserved
+ * field or misalignment, IX_E_HIP on a launch failure. */
+int32_t ix_indexer_project(int64_t rows, const ix_project_in* in, void* q_out, float* w_out, void* stream);
 
 #ifdef __cplusplus
 }

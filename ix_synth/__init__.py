@@ -15,6 +15,10 @@ Recipe (all draws come from torch generators seeded by ``_seed(...)`` below):
   fp32 rows, each row is scaled by max|k|/448 and rounded to e4m3fn (RNE,
   saturated to +-448), and that scale is stored next to the codes.
 * attention queries and latent KV rows ~ N(0, 1) rounded to bf16.
+* indexer projection (q_I and head weights from hidden states): hidden rows
+  ~ N(0, 1) and the stacked weight [H*d + H][d_in] ~ N(0, 1/d_in), both
+  rounded to bf16 (exact mode: integers in -8..8); d_in = 6144, the hidden
+  width of the GLM-5.2 configuration.
 
 Tensors are generated on the device the caller names (``cpu`` or ``cuda``);
 the two devices draw different streams for the same seed, so a test always
@@ -87,6 +91,9 @@ CHUNK_1M = Workload("chunked_prefill_1m_8k", 1, 8192, 1040384, 1048576, 2048, "F
                     128, "fp8", 16, 576, 512)
 
 WORKLOADS = {w.name: w for w in (TINY_L1K, L16K, L128K, DECODE_B32, CHUNK_1M)}
+
+# hidden width feeding the indexer projection (GLM-5.2 configuration)
+D_HIDDEN = 6144
 
 
 def _seed(*parts) -> int:
@@ -207,3 +214,17 @@ def sample_rows(w: Workload, n: int = 64, seed: int = 0):
             break
         rows.add(int(t))
     return sorted(rows)
+
+
+def projection_inputs(w: Workload, device, layer: int = 0, d_in: int = D_HIDDEN):
+    """Hidden-state rows [B * n_q, d_in] and the stacked indexer projection
+    weight [H*d + H, d_in] (q_I rows first, then one row per head weight),
+    both bf16."""
+    rows, n = w.batch * w.n_q, w.ix_heads * w.ix_dim + w.ix_heads
+    gx = _gen(device, w.seed, w.name, "proj_x", layer)
+    gw = _gen(device, w.seed, w.name, "proj_w", layer)
+    if w.mode == "exact":
+        return (_ints((rows, d_in), -8, 8, gx, device, torch.bfloat16),
+                _ints((n, d_in), -8, 8, gw, device, torch.bfloat16))
+    return (_normal((rows, d_in), 1.0, gx, device, torch.bfloat16),
+            _normal((n, d_in), 1.0 / math.sqrt(d_in), gw, device, torch.bfloat16))

@@ -24,14 +24,14 @@ import torch
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
     "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys",
-    "ix_indexer_argmax", "ix_group_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "lib_path",
+    "ix_indexer_argmax", "ix_group_forward_noalloc", "ix_indexer_project", "NOALLOC_SCRATCH_BYTES", "lib_path",
     "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
 IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
 NOALLOC_SCRATCH_BYTES = 64 << 20          # IX_NOALLOC_SCRATCH_BYTES in ix.h
@@ -53,6 +53,11 @@ class AttnIn(ctypes.Structure):
     _fields_ = [("q_heads", c_int32), ("d_qk", c_int32), ("d_v", c_int32), ("sm_scale", c_float),
                 ("kv_splits", c_int32), ("reserved", c_int32), ("q", c_void_p), ("kv", c_void_p),
                 ("out", c_void_p), ("lse", c_void_p)]
+
+
+class ProjectIn(ctypes.Structure):
+    _fields_ = [("heads", c_int32), ("dim", c_int32), ("d_in", c_int32), ("reserved", c_int32),
+                ("x", c_void_p), ("w_proj", c_void_p)]
 
 
 class GroupDesc(ctypes.Structure):
@@ -115,6 +120,8 @@ def load():
                                    c_void_p]
     lib.ix_index_overlap.restype = c_int32
     lib.ix_index_overlap.argtypes = [POINTER(Problem), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.ix_indexer_project.restype = c_int32
+    lib.ix_indexer_project.argtypes = [c_int64, POINTER(ProjectIn), c_void_p, c_void_p, c_void_p]
     if lib.ix_abi_version() != ABI_VERSION:   # the structs above follow this version of ix.h
         raise ImportError(f"{LIB_PATH} has ABI {lib.ix_abi_version()}, this binding needs {ABI_VERSION}; rebuild it")
     _lib = lib
@@ -414,3 +421,26 @@ def ix_append_keys(k_new, k_cache, k_scale, pos=None, *, seq_pos=None, stream=No
     _check(lib.ix_append_keys(ctypes.byref(prob), d, _ptr(k_new), n_new, int(pos), _ptr(kc), _ptr(k_scale),
                               _stream(stream)), "ix_append_keys")
 
+
+def ix_indexer_project(x, w_proj, q_out, w_out, *, heads, dim, stream=None):
+    """Indexer queries and head weights from hidden states (see ix.h):
+    ``x`` bf16 [..., d_in] (rows flattened), ``w_proj`` bf16
+    [heads*dim + heads, d_in] -> ``q_out`` bf16 [..., heads, dim] (rounded to
+    nearest, ties to even) and ``w_out`` fp32 [..., heads]."""
+    lib = load()
+    for t, name in ((x, "x"), (w_proj, "w_proj"), (q_out, "q_out"), (w_out, "w_out")):
+        _dev(t, name)
+    _need(x.dtype == torch.bfloat16 and x.dim() >= 1, "x must be bf16 [..., d_in]")
+    d_in = x.shape[-1]
+    rows = x.numel() // d_in if d_in else 0
+    _need(w_proj.dtype == torch.bfloat16 and tuple(w_proj.shape) == (heads * dim + heads, d_in),
+          "w_proj must be bf16 [heads*dim + heads, d_in]")
+    _need(q_out.dtype == torch.bfloat16 and tuple(q_out.shape) == tuple(x.shape[:-1]) + (heads, dim),
+          "q_out must be bf16 [..., heads, dim]")
+    _need(w_out.dtype == torch.float32 and tuple(w_out.shape) == tuple(x.shape[:-1]) + (heads,),
+          "w_out must be fp32 [..., heads]")
+    if rows == 0:
+        return                                   # nothing to do (empty tensors may hold no pointer)
+    pin = ProjectIn(heads, dim, d_in, 0, _ptr(x), _ptr(w_proj))
+    _check(lib.ix_indexer_project(rows, ctypes.byref(pin), _ptr(q_out), _ptr(w_out), _stream(stream)),
+           "ix_indexer_project")

@@ -34,6 +34,19 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Sources whose kernels keep MFMA accumulators in AGPRs (the compiler's
+# default form): the projection GEMM holds a 256-register accumulator per
+# wave, which only the AGPR file can take next to its VGPRs.
+AGPR_FORM = {"indexer_project.hip"}
+
+
+def _flags(src: str) -> list:
+    if os.path.basename(src) not in AGPR_FORM:
+        return CFLAGS
+    i = CFLAGS.index("-amdgpu-mfma-vgpr-form=1")
+    return CFLAGS[:i - 1] + CFLAGS[i + 1:]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -41,7 +54,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *_flags(src), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

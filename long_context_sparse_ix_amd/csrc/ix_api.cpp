@@ -499,6 +499,30 @@ int32_t ix_append_keys(const ix_problem* p, int32_t dim, const float* k_new, int
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
+int32_t ix_indexer_project(int64_t rows, const ix_project_in* in, void* q_out, float* w_out, void* stream) {
+  if (!in || !in->x || !in->w_proj || !q_out || !w_out) return IX_E_NULL;
+  if (rows < 0 || in->heads < 1 || in->dim < 1 || in->d_in < 64 || in->d_in % 64 != 0 || in->reserved != 0)
+    return IX_E_SHAPE;
+  const int64_t n = (int64_t)in->heads * in->dim + in->heads;
+  if (n >= (int64_t)INT32_MAX) return IX_E_SHAPE;
+  // a 256-row tile of x or W spans < 2^31 bytes; the 64 x 64 tile count fits an int
+  if (in->d_in >= (1 << 22) || ((rows + 63) / 64) * ((n + 63) / 64) > (int64_t)INT32_MAX) return IX_E_SHAPE;
+  if (!aligned16(in->x) || !aligned16(in->w_proj) || (reinterpret_cast<uintptr_t>(q_out) & 1u) != 0 ||
+      (reinterpret_cast<uintptr_t>(w_out) & 3u) != 0)
+    return IX_E_SHAPE;
+  ix::ProjArgs a{};
+  a.x = static_cast<const uint16_t*>(in->x);
+  a.w = static_cast<const uint16_t*>(in->w_proj);
+  a.q = static_cast<uint16_t*>(q_out);
+  a.wo = w_out;
+  a.M = rows;
+  a.N = (int)n;
+  a.K = in->d_in;
+  a.Nq = in->heads * in->dim;
+  hipError_t e = ix::launch_indexer_project(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
 }  // extern "C"
 
 namespace {

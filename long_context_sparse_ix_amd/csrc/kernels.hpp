@@ -97,6 +97,19 @@ hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_sca
                               const int64_t* seq_shift, int64_t shift_bound, int64_t kv_cap, int dim,
                               hipStream_t s);
 
+// Indexer inputs from hidden states: [q | w] = x . W^T with x bf16 [M][K],
+// W bf16 [N][K] (K a multiple of 64); the first Nq columns go to q as bf16
+// (nearest, ties to even) [M][Nq], the rest to wo as fp32 [M][N - Nq].
+struct ProjArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* q;
+  float* wo;
+  int64_t M;
+  int N, K, Nq;
+};
+hipError_t launch_indexer_project(const ProjArgs& a, hipStream_t s);
+
 // Per-row overlap count of two [rows][k] index buffers (k <= 2048).
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int32_t* counts, int64_t rows, int k,
                                 hipStream_t s);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
             "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
             "ix_index_overlap", "ix_append_keys", "ix_indexer_argmax",
-            "ix_group_forward_noalloc"} <= set(names)
+            "ix_group_forward_noalloc", "ix_indexer_project"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -47,12 +47,14 @@ def test_struct_layout_matches_header():
 #include "ix.h"
 #define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
 int main(void) {
-  printf("ix_problem %zu\nix_indexer_in %zu\nix_attn_in %zu\nix_group_desc %zu\n",
-         sizeof(ix_problem), sizeof(ix_indexer_in), sizeof(ix_attn_in), sizeof(ix_group_desc));
+  printf("ix_problem %zu\nix_indexer_in %zu\nix_attn_in %zu\nix_group_desc %zu\nix_project_in %zu\n",
+         sizeof(ix_problem), sizeof(ix_indexer_in), sizeof(ix_attn_in), sizeof(ix_group_desc),
+         sizeof(ix_project_in));
   F(ix_problem, q_start) F(ix_problem, kv_cap) F(ix_problem, k) F(ix_problem, seq_q_start)
   F(ix_indexer_in, q) F(ix_indexer_in, k_scale) F(ix_indexer_in, path)
   F(ix_attn_in, sm_scale) F(ix_attn_in, kv_splits) F(ix_attn_in, q) F(ix_attn_in, lse)
   F(ix_group_desc, f_mask) F(ix_group_desc, ixr) F(ix_group_desc, attn)
+  F(ix_project_in, d_in) F(ix_project_in, reserved) F(ix_project_in, x) F(ix_project_in, w_proj)
   return 0;
 }
 """
@@ -63,7 +65,7 @@ int main(void) {
         lines = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True,
                                                        check=True).stdout.splitlines())
     m = {"ix_problem": ix.Problem, "ix_indexer_in": ix.IndexerIn, "ix_attn_in": ix.AttnIn,
-         "ix_group_desc": ix.GroupDesc}
+         "ix_group_desc": ix.GroupDesc, "ix_project_in": ix.ProjectIn}
     for k, v in lines.items():
         if "." in k:
             s, f = k.split(".")
@@ -196,7 +198,7 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 5
+    assert ix.ix_abi_version() == 6
 
 
 def test_index_overlap_validation():
@@ -224,6 +226,35 @@ def test_append_keys_validation():
     assert call(kn=DUMMY + 8) == ix.IX_E_SHAPE
     assert call(ks=DUMMY + 2) == ix.IX_E_SHAPE
 
+
+
+def test_project_validation():
+    lib = ensure_lib()
+
+    def call(rows=4, q=DUMMY, w=DUMMY, **kw):
+        base = dict(heads=2, dim=16, d_in=64, reserved=0, x=DUMMY, w_proj=DUMMY)
+        base.update(kw)
+        pin = ix.ProjectIn(**base)
+        return lib.ix_indexer_project(rows, ctypes.byref(pin), q, w, None)
+    assert lib.ix_indexer_project(4, None, DUMMY, DUMMY, None) == ix.IX_E_NULL
+    assert call(x=None) == ix.IX_E_NULL
+    assert call(w_proj=None) == ix.IX_E_NULL
+    assert call(q=None) == ix.IX_E_NULL
+    assert call(w=None) == ix.IX_E_NULL
+    assert call(rows=-1) == ix.IX_E_SHAPE
+    assert call(heads=0) == ix.IX_E_SHAPE
+    assert call(dim=0) == ix.IX_E_SHAPE
+    assert call(d_in=96) == ix.IX_E_SHAPE           # not a multiple of 64
+    assert call(d_in=0) == ix.IX_E_SHAPE
+    assert call(reserved=1) == ix.IX_E_SHAPE
+    assert call(heads=1 << 16, dim=1 << 15) == ix.IX_E_SHAPE
+    assert call(d_in=1 << 22) == ix.IX_E_SHAPE       # a 256-row tile would span 2^31 bytes
+    assert call(rows=1 << 40) == ix.IX_E_SHAPE       # more tiles than an int counts
+    assert call(x=DUMMY + 8) == ix.IX_E_SHAPE
+    assert call(w_proj=DUMMY + 8) == ix.IX_E_SHAPE
+    assert call(q=DUMMY + 1) == ix.IX_E_SHAPE
+    assert call(w=DUMMY + 2) == ix.IX_E_SHAPE
+    assert call(rows=0) == ix.IX_OK                 # nothing to do, nothing launched
 
 
 def test_append_keys_per_sequence_rows_need_pos_at_the_bound():
