@@ -15,8 +15,8 @@
 //     two workgroups per CU (two waves per SIMD, so one wave's memory and LDS
 //     waits overlap the other's MFMAs); row blocks are issued longest-first so
 //     the causal triangle drains evenly;
-//   * keys stream HBM -> LDS with direct loads (global_load_lds_dwordx4, no
-//     VGPR staging) into a 4-slot ring of 64-key bf16 tiles shared by the 4
+//   * keys stream HBM -> LDS with direct loads (buffer_load_dwordx4 ... lds,
+//     no VGPR staging) into a 4-slot ring of 64-key bf16 tiles shared by the 4
 //     rows, rows XOR-swizzled so B-operand reads are bank-conflict free; tiles
 //     are consumed in pairs, one LDS-only barrier per pair;
 //   * each wave keeps its row's heads x d query slice in registers as the MFMA
@@ -59,6 +59,8 @@ constexpr int kUnroll = 8;      // (score, position) entries per lane in flight 
 constexpr int kUnrollS = 16;    // scores per lane in flight in score-only passes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// buffer resource word 3 for raw (unformatted, unswizzled) 32-bit data on CDNA
+constexpr int kRsrcWord3 = 0x00020000;
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding (direct-to-LDS loads are invisible to the compiler's waitcnt
@@ -413,22 +415,29 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     const int r = S / G::CPR;
     return (r * d + G::swz(r, S % G::CPR) * 8) * 2;
   }();
+  // The loads are buffer loads through a resource based at the tile (the
+  // flat form, global_load_lds, makes the compiler treat every outstanding
+  // one as an LDS access too, so each LDS read's wait became lgkmcnt(0)).
   const unsigned char* key_bytes = reinterpret_cast<const unsigned char*>(keys_b);
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
     const unsigned char* tile = key_bytes + (int64_t)s0 * d * 2;   // staged keys: whole tiles exist
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, (short)0, G::tile_bytes, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < G::inst_per_wave; ++j) {
       const int J = wave + 4 * j;
       if (G::lanes_per_inst == 64 || l < G::lanes_per_inst)
-        __builtin_amdgcn_global_load_lds((void*)(tile + key_off + 4096 * j),
-                                         (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(tb + J * G::lanes_per_inst * 16), 16,
+                                                 key_off + 4096 * j, 0, 0, 0);
     }
     if constexpr (SCALE) {
+      const __amdgpu_buffer_rsrc_t sr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(scale_b + s0), (short)0, kTileKeys * 4, kRsrcWord3);
       if (l < 16)
-        __builtin_amdgcn_global_load_lds((void*)(scale_b + s0 + 16 * wave + l),
-                                         (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4,
+                                                 (16 * wave + l) * 4, 0, 0, 0);
     }
   };
 
