@@ -28,7 +28,10 @@ Readings taken where the pages are silent:
   included), and s < kv_len;
 * order: larger score first, equal scores -> lower position first; the row is
   emitted as ascending positions, padded with -1 to length k;
-* fp8 keys are e4m3fn codes times a per-row fp32 scale;
+* fp8 keys are e4m3fn codes times a per-row fp32 scale; queries may be given
+  the same way, as e4m3fn codes times one fp32 scale per (row, head) (the
+  pages' FP8 indexer taken as an input format, a mode declared by the caller;
+  the default queries are bf16);
 * attention over the selected rows: o = softmax(sm_scale * Q K^T) V with K the
   whole latent row and V its first d_v dims; slots holding -1 (or any value
   outside [0, kv_len)) are ignored; a row with no valid slot gives o = 0 and
@@ -50,7 +53,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3fn", "key_matrix", "indexer_scores", "select_topk",
     "indexer_topk", "indexer_topk_rows", "attention_row", "sparse_attention", "group_forward",
     "mtp_draft", "index_overlap", "encode_e4m3fn", "quantize_key_rows", "encode_bf16",
-    "indexer_project",
+    "indexer_project", "query_matrix",
 ]
 
 
@@ -88,6 +91,14 @@ def key_matrix(keys, key_dtype: str, scale=None) -> np.ndarray:
         v = decode_e4m3fn(keys)
         return v * np.asarray(scale, dtype=np.float64)[..., None]
     raise ValueError(f"unknown key dtype {key_dtype!r}")
+
+
+def query_matrix(q, q_scale=None) -> np.ndarray:
+    """Indexer queries [..., H, d] -> float64 values: bf16 bit patterns, or,
+    with q_scale [..., H], e4m3fn codes times their (row, head) scale."""
+    if q_scale is None:
+        return decode_bf16(q)
+    return decode_e4m3fn(q) * np.asarray(q_scale, dtype=np.float64)[..., None]
 
 
 # ---------------------------------------------------------- key quantizing --
@@ -197,7 +208,7 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
 
 
 def indexer_topk(q, w, keys, key_dtype, scale, q_start, kv_len: int, k: int,
-                 rows=None) -> np.ndarray:
+                 rows=None, q_scale=None) -> np.ndarray:
     """Full-layer indexer + top-k for every (sequence, query row).
 
     q: bf16 bits [B, n_q, H, d]; w: fp32 [B, n_q, H]; keys: [B, cap, d] bf16
@@ -206,7 +217,8 @@ def indexer_topk(q, w, keys, key_dtype, scale, q_start, kv_len: int, k: int,
     (a batch of sequences of different lengths: row t of sequence b sits at
     q_start[b] + t and may select the keys up to there, as any query does).
     ``rows`` limits the work to the listed query rows (the result then has
-    len(rows) rows).  Returns int32 [B, len(rows), k].
+    len(rows) rows).  With q_scale [B, n_q, H], q holds e4m3fn codes (see
+    query_matrix).  Returns int32 [B, len(rows), k].
     """
     q = np.asarray(q)
     B, n_q = q.shape[0], q.shape[1]
@@ -223,19 +235,21 @@ def indexer_topk(q, w, keys, key_dtype, scale, q_start, kv_len: int, k: int,
         for i, t in enumerate(rows):
             p = starts[b] + t
             n = min(p, kv_len - 1) + 1
-            s = indexer_scores(decode_bf16(q[b, t]), np.asarray(w[b, t], np.float64),
+            qs = None if q_scale is None else np.asarray(q_scale)[b, t]
+            s = indexer_scores(query_matrix(q[b, t], qs), np.asarray(w[b, t], np.float64),
                                kmat[:n])
             out[b, i] = select_topk(s, k)
     return out
 
 
 def indexer_topk_rows(q_rows, w_rows, keys_b, key_dtype, scale_b, positions, kv_len: int,
-                      k: int) -> np.ndarray:
+                      k: int, q_scale_rows=None) -> np.ndarray:
     """Indexer + top-k for individual query rows of one sequence, given their
     absolute positions (decodes the reachable keys once).
 
     q_rows: bf16 bits [R, H, d]; w_rows: fp32 [R, H]; keys_b: [cap, d] of one
-    sequence; scale_b: [cap] (fp8 only); positions: [R].  Returns int32 [R, k].
+    sequence; scale_b: [cap] (fp8 only); positions: [R]; q_scale_rows: [R, H]
+    for e4m3fn-coded queries.  Returns int32 [R, k].
     """
     positions = [int(p) for p in positions]
     p_max = min(max(positions), kv_len - 1)
@@ -244,7 +258,8 @@ def indexer_topk_rows(q_rows, w_rows, keys_b, key_dtype, scale_b, positions, kv_
     out = np.full((len(positions), k), -1, dtype=np.int32)
     for i, p in enumerate(positions):
         n = min(p, kv_len - 1) + 1
-        s = indexer_scores(decode_bf16(q_rows[i]), np.asarray(w_rows[i], np.float64), kmat[:n])
+        qs = None if q_scale_rows is None else np.asarray(q_scale_rows)[i]
+        s = indexer_scores(query_matrix(q_rows[i], qs), np.asarray(w_rows[i], np.float64), kmat[:n])
         out[i] = select_topk(s, k)
     return out
 
@@ -301,8 +316,8 @@ def group_forward(roles: str, indexer_layers, attn_layers, q_start, kv_len: int,
 
     roles: one letter per layer, "F" (runs indexer + top-k and stores the
     positions) or "S" (reuses the most recent F layer's positions untouched).
-    indexer_layers[l] = (q, w, keys, key_dtype, scale) — read for F layers
-    only; attn_layers[l] = (Q, KV).  q_start as in indexer_topk (one int, or
+    indexer_layers[l] = (q, w, keys, key_dtype, scale[, q_scale]) — read for
+    F layers only; attn_layers[l] = (Q, KV).  q_start as in indexer_topk (one int, or
     one per sequence).  Returns a dict with per-layer outputs
     "O"/"lse", the list "idx" of index buffers (one per F layer), "used" (for
     each layer, which F buffer it attended over) and "n_indexer_runs".
@@ -314,8 +329,9 @@ def group_forward(roles: str, indexer_layers, attn_layers, q_start, kv_len: int,
     runs = 0
     for l, role in enumerate(roles):
         if role == "F":
-            q, w, keys, kd, sc = indexer_layers[l]
-            cur = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows)
+            q, w, keys, kd, sc, *qsc = indexer_layers[l]
+            cur = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows,
+                               q_scale=qsc[0] if qsc else None)
             idx_list.append(cur)
             runs += 1
         elif role != "S":
@@ -338,15 +354,16 @@ def mtp_draft(indexer_in, draft_q, kv, q_start, kv_len: int, k: int, sm_scale: f
     in the MTP layer": the first draft step runs the indexer and keeps its
     positions; every later draft step attends over those same positions in
     the same, earlier KV cache (nothing the later steps add is selected).
-    indexer_in = (q, w, keys, key_dtype, scale) of the first step's query rows
+    indexer_in = (q, w, keys, key_dtype, scale[, q_scale]) of the first step's query rows
     (positions q_start + t); draft_q: one bf16-bit Q [B, n_q, Hq, D] per draft
     step; kv: the MTP layer's latent cache [B, cap, D], shared by all steps.
     Returns dict(idx, O: list per step, lse: list per step, n_indexer_runs).
     """
     if len(draft_q) < 1:
         raise ValueError("at least one draft step")
-    q, w, keys, kd, sc = indexer_in
-    idx = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows)
+    q, w, keys, kd, sc, *qsc = indexer_in
+    idx = indexer_topk(q, w, keys, kd, sc, q_start, kv_len, k, rows=rows,
+                       q_scale=qsc[0] if qsc else None)
     outs, lses = [], []
     for Q in draft_q:
         o, lse = sparse_attention(Q, kv, idx, kv_len, sm_scale, d_v, rows=rows,

@@ -104,6 +104,10 @@ def _project_weights_first(x_bits, w_bits, heads, dim):
     return q, Y[..., :heads]
 
 
+def _query_scale_ignored(q, q_scale=None):
+    return O.decode_bf16(q) if q_scale is None else O.decode_e4m3fn(q)
+
+
 ATTN = O.attention_row
 INDEXER = O.indexer_topk
 
@@ -125,6 +129,7 @@ MUTATIONS = [
     ("quantize_fnuz_range", "quantize_key_rows", _quantize_fnuz_max, P.test_quantize_rows_closed_forms),
     ("bf16_truncate", "encode_bf16", _bf16_truncate, P.test_projection_rounds_midpoints_to_even),
     ("project_weights_first", "indexer_project", _project_weights_first, P.test_hand_worked_projection),
+    ("query_scale_ignored", "query_matrix", _query_scale_ignored, P.test_hand_worked_fp8_queries),
 ]
 
 

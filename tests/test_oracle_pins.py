@@ -566,3 +566,41 @@ def test_projection_head_weights_scale_exactly():
     q2, w2 = O.indexer_project(O.encode_bf16(4.0 * O.decode_bf16(O.encode_bf16(x))), wb, H, d)
     np.testing.assert_array_equal(w2, 4.0 * w1)
     np.testing.assert_array_equal(O.decode_bf16(q2), 4.0 * O.decode_bf16(q1))
+
+
+def test_hand_worked_fp8_queries():
+    """e4m3fn-coded queries times their (row, head) scale (IndexCache notes,
+    section 1: an FP8 indexer), worked by hand in the golden file."""
+    c = gold()["fp8_queries"]
+    q = O.query_matrix(np.array(c["q_codes"], dtype=np.uint8), np.array(c["q_scale"]))
+    np.testing.assert_array_equal(q, [[3.0, -4.0], [0.125, 1.0]])
+    s = O.indexer_scores(q, np.array(c["w"], dtype=np.float64), np.array(c["keys"], dtype=np.float64))
+    np.testing.assert_array_equal(s, c["scores"])
+
+
+def _e4m3_code_of(values):
+    """Codes of e4m3fn-representable values, found by inverting the (pinned)
+    decode table over all 256 codes."""
+    table = {float(v): c for c, v in enumerate(O.decode_e4m3fn(np.arange(256, dtype=np.uint8)))
+             if np.isfinite(v) and not (v == 0.0 and c != 0)}
+    return np.vectorize(lambda v: table[float(v)], otypes=[np.uint8])(values)
+
+
+def test_fp8_queries_with_power_of_two_scales_match_bf16_values():
+    """Queries whose values are e4m3fn codes times a power of two per (row,
+    head) are exactly bf16 values too: both query forms give the same scores
+    and the same top-k."""
+    rng = np.random.default_rng(7)
+    B, n_q, H, d, L, k = 1, 6, 3, 8, 40, 9
+    ints = rng.integers(-8, 9, (B, n_q, H, d)).astype(np.float64)
+    scale = np.ldexp(1.0, rng.integers(-3, 4, (B, n_q, H))).astype(np.float32)
+    codes = _e4m3_code_of(ints)
+    vals = ints * scale[..., None].astype(np.float64)
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(O.decode_bf16(bits), vals)
+    w = rng.standard_normal((B, n_q, H)).astype(np.float32)
+    keys = (rng.standard_normal((B, L, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    a = O.indexer_topk(bits, w, keys, "bf16", None, L - n_q, L, k)
+    b = O.indexer_topk(codes, w, keys, "bf16", None, L - n_q, L, k, q_scale=scale)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(O.query_matrix(codes, scale), vals)
