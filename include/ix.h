@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IX_ABI_VERSION 6
+#define IX_ABI_VERSION 7
 
 typedef enum ix_status {
   IX_OK = 0,
@@ -109,7 +109,11 @@ typedef struct ix_problem {
  * the bf16 row, or the e4m3fn codes of row s times k_scale[s].  The pages
  * describe the indexer only as a small low-rank FP8 module with few heads
  * (IndexCache notes, section 1); this weighted-ReLU form is the library's
- * stated reading. */
+ * stated reading.  Queries are bf16 by default; with q_dtype
+ * IX_DTYPE_FP8_E4M3FN they are e4m3fn codes times one fp32 scale per (row,
+ * head), q[t,h,:] = codes[t,h,:] * q_scale[t,h] (a mode the caller declares:
+ * the full-layer kernel then multiplies fp8 codes on fp8 MFMA).  FP8 queries
+ * need FP8 keys and d in {64, 128}. */
 typedef struct ix_indexer_in {
   int32_t heads;    /* H, 1..64                                                */
   int32_t dim;      /* d, a multiple of 16 in 16..128                          */
@@ -119,6 +123,10 @@ typedef struct ix_indexer_in {
   const float* w;   /* fp32 [B][n_q][H]                                        */
   const void* k;    /* [B][kv_cap][d]: bf16, or uint8 e4m3fn codes             */
   const float* k_scale; /* fp32 [B][kv_cap] for FP8 keys; must be NULL for bf16 */
+  int32_t q_dtype;  /* 0 or IX_DTYPE_BF16: bf16 q; IX_DTYPE_FP8_E4M3FN: e4m3fn codes */
+  int32_t reserved; /* must be 0                                               */
+  const float* q_scale; /* fp32 [B][n_q][H], 16-byte aligned, for FP8 queries;
+                           must be NULL for bf16 queries                       */
 } ix_indexer_in;
 
 /* Inputs/outputs of one layer's sparse attention over selected latent rows.

@@ -14,6 +14,11 @@ Recipe (all draws come from torch generators seeded by ``_seed(...)`` below):
   ~ N(0, 1) in fp32; bf16 keys ~ N(0, 1/sqrt(d)); fp8 keys start as N(0, 1)
   fp32 rows, each row is scaled by max|k|/448 and rounded to e4m3fn (RNE,
   saturated to +-448), and that scale is stored next to the codes.
+* fp8 indexer queries (a mode the caller declares): exact mode draws
+  integers from -8..8 as e4m3fn codes with a per-(row, head) scale 2^e, e
+  uniform in {-1, 0, 1}; float mode draws N(0, 1/sqrt(d)) fp32 rows and
+  quantises each (row, head) row like an fp8 key row (scale max|q|/448).
+  Head weights follow the bf16 recipe.
 * attention queries and latent KV rows ~ N(0, 1) rounded to bf16.
 * indexer projection (q_I and head weights from hidden states): hidden rows
   ~ N(0, 1) and the stacked weight [H*d + H][d_in] ~ N(0, 1/d_in), both
@@ -184,6 +189,25 @@ def indexer_queries(w: Workload, device, layer: int = 0, step: int = 0):
     q = _normal(qs, 1.0 / math.sqrt(w.ix_dim), g, device, torch.bfloat16)
     wt = torch.randn(ws, generator=g, device=device, dtype=torch.float32)
     return q, wt
+
+
+def indexer_queries_fp8(w: Workload, device, layer: int = 0, step: int = 0):
+    """fp8 indexer queries: (codes [B, n_q, H, d] uint8 e4m3fn, q_scale
+    [B, n_q, H] fp32, head weights [B, n_q, H] fp32)."""
+    g = _gen(device, w.seed, w.name, "ix_q8", layer, step)
+    qs = (w.batch, w.n_q, w.ix_heads, w.ix_dim)
+    ws = (w.batch, w.n_q, w.ix_heads)
+    if w.mode == "exact":
+        codes = _ints(qs, -8, 8, g, device, torch.float32).to(torch.float8_e4m3fn)
+        e = torch.randint(-1, 2, ws, generator=g, device=device, dtype=torch.int32)
+        q_scale = torch.pow(2.0, e.to(torch.float32))
+        e = torch.randint(0, 3, ws, generator=g, device=device, dtype=torch.int32)
+        wt = torch.pow(2.0, e.to(torch.float32))
+        return codes.view(torch.uint8), q_scale, wt
+    q32 = torch.randn(qs, generator=g, device=device, dtype=torch.float32) / math.sqrt(w.ix_dim)
+    codes, q_scale = fp8_rows(q32)
+    wt = torch.randn(ws, generator=g, device=device, dtype=torch.float32)
+    return codes.view(torch.uint8), q_scale, wt
 
 
 def attn_queries(w: Workload, device, layer: int, step: int = 0):

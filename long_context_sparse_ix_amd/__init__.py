@@ -31,7 +31,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 IX_OK, IX_E_NULL, IX_E_SHAPE, IX_E_DTYPE, IX_E_ROLES, IX_E_WORKSPACE, IX_E_HIP = range(7)
 IX_DTYPE_BF16, IX_DTYPE_FP8_E4M3FN = 1, 2
 NOALLOC_SCRATCH_BYTES = 64 << 20          # IX_NOALLOC_SCRATCH_BYTES in ix.h
@@ -46,7 +46,8 @@ class Problem(ctypes.Structure):
 
 class IndexerIn(ctypes.Structure):
     _fields_ = [("heads", c_int32), ("dim", c_int32), ("k_dtype", c_int32), ("path", c_int32),
-                ("q", c_void_p), ("w", c_void_p), ("k", c_void_p), ("k_scale", c_void_p)]
+                ("q", c_void_p), ("w", c_void_p), ("k", c_void_p), ("k_scale", c_void_p),
+                ("q_dtype", c_int32), ("reserved", c_int32), ("q_scale", c_void_p)]
 
 
 class AttnIn(ctypes.Structure):
@@ -212,9 +213,18 @@ def _key_dtype(keys):
     raise ValueError(f"indexer keys must be bf16 or e4m3fn codes, got {keys.dtype}")
 
 
-def _indexer_in(q, w, keys, k_scale, path):
+def _indexer_in(q, w, keys, k_scale, path, q_scale=None):
     _dev(q, "q"), _dev(w, "w"), _dev(keys, "keys")
-    _need(q.dtype == torch.bfloat16 and q.dim() == 4, "indexer q must be bf16 [B, n_q, H, d]")
+    q8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
+    _need((q.dtype == torch.bfloat16 or q8) and q.dim() == 4,
+          "indexer q must be bf16 or e4m3fn codes [B, n_q, H, d]")
+    if q8:
+        _need(q_scale is not None, "fp8 queries need q_scale [B, n_q, H]")
+        _dev(q_scale, "q_scale")
+        _need(q_scale.dtype == torch.float32 and tuple(q_scale.shape) == tuple(q.shape[:3]),
+              "q_scale must be fp32 [B, n_q, H]")
+    else:
+        _need(q_scale is None, "bf16 queries take no q_scale")
     _need(w.dtype == torch.float32 and tuple(w.shape) == tuple(q.shape[:3]), "w must be fp32 [B, n_q, H]")
     kd = _key_dtype(keys)
     _need(keys.dim() == 3 and keys.shape[0] == q.shape[0] and keys.shape[2] == q.shape[3],
@@ -226,7 +236,8 @@ def _indexer_in(q, w, keys, k_scale, path):
               "k_scale must be fp32 [B, cap]")
     else:
         _need(k_scale is None, "bf16 keys take no k_scale")
-    return IndexerIn(q.shape[2], q.shape[3], kd, path, _ptr(q), _ptr(w), _ptr(keys), _ptr(k_scale))
+    return IndexerIn(q.shape[2], q.shape[3], kd, path, _ptr(q), _ptr(w), _ptr(keys), _ptr(k_scale),
+                     IX_DTYPE_FP8_E4M3FN if q8 else IX_DTYPE_BF16, 0, _ptr(q_scale))
 
 
 def _attn_in(q, kv, out, lse, sm_scale, kv_splits):
@@ -256,11 +267,12 @@ def ix_workspace_bytes(prob: Problem, op: int, desc) -> int:
 
 
 def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=None, kv_len=None, path=IX_PATH_AUTO,
-                    seq_q_start=None, stream=None):
+                    seq_q_start=None, q_scale=None, stream=None):
     """Full-layer indexer + top-k into ``idx`` int32 [B, n_q, k] (see ix.h).
 
     ``seq_q_start`` (int64 [B] on the device, optional): per-sequence position
-    of row 0; ``q_start`` is then their bound (default: their maximum)."""
+    of row 0; ``q_start`` is then their bound (default: their maximum).  With
+    ``q`` as e4m3fn codes (uint8), ``q_scale`` fp32 [B, n_q, H] is their scale."""
     lib = load()
     _dev(idx, "idx")
     _need(idx.dtype == torch.int32 and tuple(idx.shape[:2]) == tuple(q.shape[:2]), "idx must be int32 [B, n_q, k]")
@@ -268,14 +280,14 @@ def ix_indexer_topk(q, w, keys, idx, *, k_scale=None, q_start=None, kv_len=None,
     q_start = _starts(seq_q_start, q_start, q.shape[0])
     prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, idx.shape[2],
                     seq_q_start)
-    desc = _indexer_in(q, w, keys, k_scale, path)
+    desc = _indexer_in(q, w, keys, k_scale, path, q_scale)
     ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_TOPK, desc), q.device, stream)
     _check(lib.ix_indexer_topk(ctypes.byref(prob), ctypes.byref(desc), _ptr(idx), _ptr(ws), nb,
                                _stream(stream)), "ix_indexer_topk")
 
 
 def ix_indexer_argmax(q, w, keys, pos, score=None, *, k_scale=None, q_start=None, kv_len=None,
-                      seq_q_start=None, stream=None):
+                      seq_q_start=None, q_scale=None, stream=None):
     """Top-1 of the indexer scores (see ix.h): ``pos`` int32 [B, n_q] gets each
     row's best position, ``score`` (fp32 [B, n_q], optional) its score."""
     lib = load()
@@ -288,7 +300,7 @@ def ix_indexer_argmax(q, w, keys, pos, score=None, *, k_scale=None, q_start=None
     cap = keys.shape[1]
     q_start = _starts(seq_q_start, q_start, q.shape[0])
     prob = _problem(q.shape[0], q.shape[1], q_start, cap if kv_len is None else kv_len, cap, 1, seq_q_start)
-    desc = _indexer_in(q, w, keys, k_scale, IX_PATH_AUTO)
+    desc = _indexer_in(q, w, keys, k_scale, IX_PATH_AUTO, q_scale)
     ws, nb = _workspace(ix_workspace_bytes(prob, IX_OP_INDEXER_ARGMAX, desc), q.device, stream)
     _check(lib.ix_indexer_argmax(ctypes.byref(prob), ctypes.byref(desc), _ptr(pos), _ptr(score), _ptr(ws), nb,
                                  _stream(stream)), "ix_indexer_argmax")
@@ -326,7 +338,7 @@ def _group_args(indexer_layers, attn_layers, f_mask, idx, q_start, kv_len, sm_sc
             e = indexer_layers[l]
             _need(e is not None, f"layer {l} is full but has no indexer inputs")
             _need(e["keys"].shape[1] == cap, "indexer keys and latent KV need the same capacity")
-            ixr[l] = _indexer_in(e["q"], e["w"], e["keys"], e.get("k_scale"), path)
+            ixr[l] = _indexer_in(e["q"], e["w"], e["keys"], e.get("k_scale"), path, e.get("q_scale"))
         a = attn_layers[l]
         _need(a["q"].shape[:2] == a0["q"].shape[:2] and a["kv"].shape[1] == cap, "layers must share sizes")
         att[l] = _attn_in(a["q"], a["kv"], a["out"], a.get("lse"), sm_scale, kv_splits)
@@ -337,7 +349,7 @@ def ix_group_forward(indexer_layers, attn_layers, f_mask: int, idx, *, q_start=N
                      sm_scale=0.0, kv_splits=0, path=IX_PATH_AUTO, seq_q_start=None, stream=None):
     """One IndexShare layer group (see ix.h).
 
-    indexer_layers[l]: dict(q=, w=, keys=, k_scale=) for full layers (None for
+    indexer_layers[l]: dict(q=, w=, keys=, k_scale=[, q_scale=]) for full layers (None for
     shared ones); attn_layers[l]: dict(q=, kv=, out=, lse=).  Bit l of f_mask
     marks layer l full.  idx: int32 [n_full, B, n_q, k].  ``seq_q_start`` as
     in ix_indexer_topk."""

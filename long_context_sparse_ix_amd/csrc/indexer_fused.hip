@@ -44,6 +44,8 @@
 // streams the same scores through the same tile ring and MFMA pipeline, so
 // its time is the score stream's alone and the difference to the full kernel
 // is what the streaming top-k costs.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -309,24 +311,44 @@ __device__ __forceinline__ void read_bfrags(const unsigned char* kb, int nt, int
     bfr[ks] = *reinterpret_cast<const bf16x8*>(kb + r * G::row_bytes + G::swz(r, hf * (G::CPR / 2) + ks) * 16);
 }
 
+// Two 16-byte B chunks as one fp8 MFMA operand (32 codes).
+__device__ __forceinline__ i32x8 join_b(const bf16x8& lo, const bf16x8& hi) {
+  const u32x4 x = __builtin_bit_cast(u32x4, lo), y = __builtin_bit_cast(u32x4, hi);
+  return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
 // One half-tile block: the MFMAs of one 32-key half into acc_mma and/or the
 // epilogue of the other accumulator half (acc_epi), in one basic block so the
 // scheduler can put the VALU work between MFMAs.  Returns the partial (this
-// lane's heads) score of the epilogue half.
-template <int HT, int KS, bool MMA, bool EPI>
-__device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const float (&wr)[HT][16],
-                                            const bf16x8 (&bfr)[KS], f32x16 (&acc_mma)[HT],
+// lane's heads) score of the epilogue half.  AF = bf16x8: NA = NB k-steps of
+// v_mfma_f32_32x32x16_bf16.  AF = i32x8 (e4m3fn codes): NA k-steps of
+// v_mfma_f32_32x32x64_f8f6f4, each taking B chunks 2kk and 2kk+1 (the A
+// fragment holds the same 32 dims of the query as those two key chunks).
+template <int HT, int NA, int NB, bool MMA, bool EPI, typename AF>
+__device__ __forceinline__ float half_block(const AF (&qf)[HT][NA], const float (&wr)[HT][16],
+                                            const bf16x8 (&bfr)[NB], f32x16 (&acc_mma)[HT],
                                             const f32x16 (&acc_epi)[HT]) {
+  constexpr bool kF8 = std::is_same<AF, i32x8>::value;
+  static_assert(kF8 ? NB == 2 * NA : NB == NA, "B chunks per A fragment");
   if constexpr (MMA) {
     // a wave issuing MFMAs outranks the other wave of its SIMD while that one
     // filters or shrinks, so the matrix pipe stays fed (0.7% at L=128K)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < NA; ++ks) {
+      if constexpr (kF8) {
+        const i32x8 bb = join_b(bfr[2 * ks], bfr[2 * ks + 1]);
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc_mma[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[ks],
-                                                              ks == 0 ? f32x16{} : acc_mma[ht], 0, 0, 0);
+        for (int ht = 0; ht < HT; ++ht)   // format 0 (e4m3) for A and B, no block scales
+          acc_mma[ht] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              qf[ht][ks], bb, ks == 0 ? f32x16{} : acc_mma[ht], 0, 0, 0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc_mma[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], bfr[ks],
+                                                                ks == 0 ? f32x16{} : acc_mma[ht], 0, 0, 0);
+      }
+    }
   }
   float part = 0.0f;
   if constexpr (EPI) {
@@ -338,20 +360,30 @@ __device__ __forceinline__ float half_block(const bf16x8 (&qf)[HT][KS], const fl
     part = (s[0] + s[1]) + (s[2] + s[3]);
   }
   if constexpr (MMA && EPI) {
+    // an fp8 MFMA is twice a bf16 one's cycles for four times its k-steps
+    constexpr int kValu = kF8 ? 32 / NA : 4;
 #pragma unroll
-    for (int i = 0; i < HT * KS; ++i) {
+    for (int i = 0; i < HT * NA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                          // 4 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                      // VALU
     }
   }
   if constexpr (MMA) __builtin_amdgcn_s_setprio(0);
   return part;
 }
 
-template <int HT, int KS, bool SCALE, bool SELECT>
+// Q8: e4m3fn queries times e4m3fn keys on the fp8 MFMA.  A key tile then
+// holds the raw codes (d bytes a row, the geometry of a d/2-wide bf16 tile),
+// loaded straight from the key cache; the per-key scale multiplies the head
+// sum and the per-(row, head) query scale is folded into the head weight.
+template <int HT, int KS, bool SCALE, bool SELECT, bool Q8>
 __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedArgs a) {
-  using G = TileGeom<KS>;
-  constexpr int d = G::d;
+  static_assert(!Q8 || ((KS == 4 || KS == 8) && SCALE), "fp8 MFMA form: d in {64, 128}, scaled keys");
+  using G = TileGeom<Q8 ? KS / 2 : KS>;
+  constexpr int d = KS * 16;                  // query / key dims
+  constexpr int NA = Q8 ? KS / 4 : KS;        // A fragments (k-steps) per head tile
+  constexpr int NB = G::CPR / 2;              // 16-byte B chunks per lane per 32-key half
+  using AF = typename std::conditional<Q8, i32x8, bf16x8>::type;
   constexpr int kLoads = G::inst_per_wave + (SCALE ? 1 : 0);   // direct loads per wave per tile
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* key_lds0 = smem;                                                   // [3][tile]
@@ -376,55 +408,82 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   uint32_t* my_hist = hist + wave * 256;
 
   // Query slice (A operand): lane (m, hf) holds head ht*32+m, elements
-  // [hf*d/2 + 8*ks, +8) of d for k-step ks.  The key B operand uses the same
-  // element split, so each dot product runs over all d elements.
-  bf16x8 qf[HT][KS];
+  // [hf*d/2 + 8*ks, +8) of d for bf16 k-step ks, or codes [hf*d/2 + 32*ks,
+  // +32) for fp8 k-step ks.  The key B operand uses the same element split,
+  // so each dot product runs over all d elements.  e4m3fn queries outside
+  // the fp8 MFMA form are widened exactly to bf16; their per-head scale is
+  // folded into the head weight.
+  AF qf[HT][NA];
   float wr[HT][16];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? t : 0)) * a.H * d;
+    const int64_t qr = ((int64_t)b * a.n_q + (row_ok ? t : 0)) * a.H;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int h = ht * 32 + m;
       const bool ok = row_ok && h < a.H;
+      if constexpr (Q8) {
+        const uint8_t* src = a.q8 + (qr + h) * d + hf * (d / 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[ht][ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks)
-                        : bf16x8{};
+        for (int ks = 0; ks < NA; ++ks) qf[ht][ks] = ok ? *reinterpret_cast<const i32x8*>(src + 32 * ks) : i32x8{};
+      } else if (a.q8) {
+        const uint8_t* src = a.q8 + (qr + h) * d + hf * (d / 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (ok) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(src + 8 * ks);
+            const u32x2 lo = e4m3x4_to_bf16x4(c.x), hi = e4m3x4_to_bf16x4(c.y);
+            v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          }
+          qf[ht][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+      } else {
+        const uint16_t* qrow = a.q + qr * d;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[ht][ks] = ok ? *reinterpret_cast<const bf16x8*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks)
+                          : bf16x8{};
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hh = ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);   // MFMA output row of acc[r]
-        wr[ht][r] = (row_ok && hh < a.H) ? a.w[((int64_t)b * a.n_q + t) * a.H + hh] : 0.0f;
+        wr[ht][r] = (row_ok && hh < a.H)
+                        ? a.w[qr + hh] * (a.q_scale ? a.q_scale[qr + hh] : 1.0f)
+                        : 0.0f;
       }
     }
   }
 
-  const uint16_t* keys_b = a.keys + (int64_t)b * a.key_bstride;
   const float* scale_b = SCALE ? a.scale + (int64_t)b * a.scale_bstride : nullptr;
 
   // Direct HBM -> LDS loads of tile `it` into ring slot `slot`: load j of this
   // wave fills LDS slots [J*n, J*n+n) (J = wave + 4j, n lanes) in lane order, so
   // lane l fetches the global chunk that belongs in slot J*n + l (tile row r,
   // chunk swz(r, slot % CPR); swz is an involution).  With several loads per
-  // wave (d >= 64) load j covers the 4 KB after load j-1 and the swizzle
-  // repeats, so one per-lane byte offset serves all of them.  The staged key
-  // copy is padded by a tile, so the last, partial tile loads whole (the rows
-  // past the last key are masked).
+  // wave (tiles of 8 KB and more) load j covers the 4 KB after load j-1 and
+  // the swizzle repeats, so one per-lane byte offset serves all of them.  The
+  // rows of the last, partial tile past the last key are masked; those past
+  // the key array's kv_rows lie outside the load's resource and read zeros.
   static_assert(G::inst_per_wave == 1 || G::lanes_per_inst * 4 * 16 == 4096, "4 KB per load round");
   const int key_off = [&] {
     const int S = wave * G::lanes_per_inst + l;
     const int r = S / G::CPR;
-    return (r * d + G::swz(r, S % G::CPR) * 8) * 2;
+    return r * G::row_bytes + G::swz(r, S % G::CPR) * 16;
   }();
   // The loads are buffer loads through a resource based at the tile (the
   // flat form, global_load_lds, makes the compiler treat every outstanding
   // one as an LDS access too, so each LDS read's wait became lgkmcnt(0)).
-  const unsigned char* key_bytes = reinterpret_cast<const unsigned char*>(keys_b);
+  const unsigned char* key_bytes;
+  if constexpr (Q8) key_bytes = a.keys8 + (int64_t)b * a.key_bstride;
+  else key_bytes = reinterpret_cast<const unsigned char*>(a.keys + (int64_t)b * a.key_bstride);
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
+    const int64_t rows_left = a.kv_rows - s0;                    // >= 1: tiles start below the last key
+    const int tile_rows = rows_left < kTileKeys ? (int)rows_left : kTileKeys;
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
-    const unsigned char* tile = key_bytes + (int64_t)s0 * d * 2;   // staged keys: whole tiles exist
+    const unsigned char* tile = key_bytes + (int64_t)s0 * G::row_bytes;
     const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tile, (short)0, G::tile_bytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, (short)0, tile_rows * G::row_bytes, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < G::inst_per_wave; ++j) {
       const int J = wave + 4 * j;
@@ -434,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     }
     if constexpr (SCALE) {
       const __amdgpu_buffer_rsrc_t sr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(scale_b + s0), (short)0, kTileKeys * 4, kRsrcWord3);
+          __builtin_amdgcn_make_buffer_rsrc((void*)(scale_b + s0), (short)0, tile_rows * 4, kRsrcWord3);
       if (l < 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(scale_lds + slot * kTileKeys + 16 * wave), 4,
                                                  (16 * wave + l) * 4, 0, 0, 0);
@@ -472,8 +531,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
     const unsigned char* kb = key_lds0 + slot * G::tile_bytes;
     // B operand of half 0 first (a stale, unused read when !mma), so its LDS
     // latency hides behind the tile issue
-    bf16x8 bfr[KS];
-    read_bfrags<KS>(kb, 0, m, hf, bfr);
+    bf16x8 bfr[NB];
+    read_bfrags<NB>(kb, 0, m, hf, bfr);
     const float sc_cur = SCALE ? scale_lds[slot * kTileKeys + l] : 1.0f;
     if (issue_pair) {
       if (it + 2 < n_tiles) issue_tile(it + 2, (it + 2) & (kRing - 1));
@@ -482,10 +541,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
 
     // block X: MFMAs of half 0 of tile it || epilogue of half 1 of tile it-1
     float part1 = 0.0f;
-    if (mma && epi) part1 = half_block<HT, KS, true, true>(qf, wr, bfr, acc0, acc1);
-    else if (mma) half_block<HT, KS, true, false>(qf, wr, bfr, acc0, acc1);
-    else if (epi) part1 = half_block<HT, KS, false, true>(qf, wr, bfr, acc0, acc1);
-    read_bfrags<KS>(kb, 1, m, hf, bfr);          // half 1, in flight during the finish
+    if (mma && epi) part1 = half_block<HT, NA, NB, true, true>(qf, wr, bfr, acc0, acc1);
+    else if (mma) half_block<HT, NA, NB, true, false>(qf, wr, bfr, acc0, acc1);
+    else if (epi) part1 = half_block<HT, NA, NB, false, true>(qf, wr, bfr, acc0, acc1);
+    read_bfrags<NB>(kb, 1, m, hf, bfr);          // half 1, in flight during the finish
 
     if (epi) {
       // finish tile it-1: lanes 0-31 take key half 0, lanes 32-63 half 1
@@ -514,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
       }
     }
     // block Y: MFMAs of half 1 of tile it || epilogue of its half 0
-    if (mma) part0 = half_block<HT, KS, true, true>(qf, wr, bfr, acc1, acc0);
+    if (mma) part0 = half_block<HT, NA, NB, true, true>(qf, wr, bfr, acc1, acc0);
     sc_prev = sc_cur;
   };
   for (int it = 0, parity = 0; it <= n_tiles; it += 2, parity ^= 1) {
@@ -595,14 +654,14 @@ __global__ void stage_keys_kernel(const void* __restrict__ src, int fp8, int64_t
   }
 }
 
-template <int HT, int KS, bool SCALE, bool SELECT>
+template <int HT, int KS, bool SCALE, bool SELECT, bool Q8 = false>
 hipError_t launch_fused_s(const FusedArgs& a, int B, hipStream_t s) {
-  const size_t lds = fused_lds_bytes(KS * 16);
-  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE, SELECT>);
+  const size_t lds = fused_lds_bytes((Q8 ? KS / 2 : KS) * 16);   // an fp8 row is half a bf16 row
+  const void* fn = reinterpret_cast<const void*>(&fused_indexer_topk_kernel<HT, KS, SCALE, SELECT, Q8>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((a.n_q + kRowsPerWG - 1) / kRowsPerWG, B);
-  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS, SCALE, SELECT>), grid, dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((fused_indexer_topk_kernel<HT, KS, SCALE, SELECT, Q8>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -629,6 +688,14 @@ template <bool SELECT>
 hipError_t launch_fused_sel(const FusedArgs& a, int B, int d, hipStream_t s) {
   const int HT = a.H > 32 ? 2 : 1;
   const int KS = d / 16;
+  if (a.keys8) {
+    if (!a.q8 || !a.scale || a.keys || a.kv_rows < 1) return hipErrorInvalidValue;
+#define IX_FUSED_Q8(ht, ks) \
+  if (HT == ht && KS == ks) return launch_fused_s<ht, ks, true, SELECT, true>(a, B, s);
+    IX_FUSED_Q8(1, 4) IX_FUSED_Q8(1, 8) IX_FUSED_Q8(2, 4) IX_FUSED_Q8(2, 8)
+#undef IX_FUSED_Q8
+    return hipErrorInvalidValue;
+  }
 #define IX_FUSED_CASE(ht, ks) \
   if (HT == ht && KS == ks) return launch_fused_t<ht, ks, SELECT>(a, B, s);
   IX_FUSED_CASE(1, 1) IX_FUSED_CASE(1, 2) IX_FUSED_CASE(1, 4) IX_FUSED_CASE(1, 8)

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
   // rather than in 32 registers per lane.  Filled before any wave leaves.
   __shared__ __align__(16) float w_lds[HT * 32];
   for (int i = threadIdx.x; i < HT * 32; i += kWavesPerWG * kWave)
-    w_lds[i] = i < a.H ? a.w[(int64_t)row * a.H + i] : 0.0f;
+    w_lds[i] = i < a.H ? a.w[(int64_t)row * a.H + i] * (a.q_scale ? a.q_scale[(int64_t)row * a.H + i] : 1.0f)
+                       : 0.0f;
   __syncthreads();
   if (s_begin > p) return;
   const int n_tiles = (int)min<int64_t>(kTilesPerWave, (p - s_begin) / kTileKeys + 1);
@@ -116,8 +117,26 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, FP8 ? 2 : 1) void indexer_scor
     }
   };
 
+  // fp8 queries: e4m3fn codes widened exactly to bf16 (their per-head scale
+  // is folded into the head weight above)
   bf16x8 qf[HT][KS];
-  {
+  if (a.q8) {
+    const uint8_t* qrow = a.q8 + (int64_t)row * a.H * d;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 32 + m;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < a.H) {
+          const u32x2 c = *reinterpret_cast<const u32x2*>(qrow + (int64_t)h * d + hf * (d / 2) + 8 * ks);
+          const u32x2 lo = e4m3x4_to_bf16x4(c.x), hi = e4m3x4_to_bf16x4(c.y);
+          v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        qf[ht][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  } else {
     const uint16_t* qrow = a.q + (int64_t)row * a.H * d;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {

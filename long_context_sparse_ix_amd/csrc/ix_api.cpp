@@ -51,15 +51,26 @@ int32_t check_indexer(const ix_problem* p, const ix_indexer_in* in) {
   if (!in->q || !in->w || !in->k) return IX_E_NULL;
   if (in->k_dtype == IX_DTYPE_FP8_E4M3FN && !in->k_scale) return IX_E_NULL;
   if (in->k_dtype == IX_DTYPE_BF16 && in->k_scale) return IX_E_SHAPE;
+  if (in->q_dtype != 0 && in->q_dtype != IX_DTYPE_BF16 && in->q_dtype != IX_DTYPE_FP8_E4M3FN) return IX_E_DTYPE;
+  if (in->reserved != 0) return IX_E_SHAPE;
+  if (in->q_dtype == IX_DTYPE_FP8_E4M3FN && !in->q_scale) return IX_E_NULL;
+  if (in->q_dtype != IX_DTYPE_FP8_E4M3FN && in->q_scale) return IX_E_SHAPE;
   if (in->heads < 1 || in->heads > 64 || in->dim < 16 || in->dim > 128 || in->dim % 16 != 0)
     return IX_E_SHAPE;
   if (in->path < IX_PATH_AUTO || in->path > IX_PATH_MATERIALIZED) return IX_E_SHAPE;
   if (in->path == IX_PATH_FUSED && !ix::fused_dim_supported(in->dim)) return IX_E_SHAPE;
   if (!aligned16(in->q) || !aligned16(in->w) || !aligned16(in->k) ||
-      (in->k_scale && !aligned16(in->k_scale)))
+      (in->k_scale && !aligned16(in->k_scale)) || (in->q_scale && !aligned16(in->q_scale)))
     return IX_E_SHAPE;
   (void)p;
   return IX_OK;
+}
+
+// fp8 queries and fp8 keys with d in {64, 128}: the fused kernel multiplies
+// the codes on the fp8 MFMA, reading the key cache in place (no staging).
+bool fp8_mma(const ix_indexer_in* in) {
+  return in->q_dtype == IX_DTYPE_FP8_E4M3FN && in->k_dtype == IX_DTYPE_FP8_E4M3FN &&
+         (in->dim == 64 || in->dim == 128);
 }
 
 int32_t check_attn(const ix_attn_in* in) {
@@ -106,11 +117,13 @@ size_t rng_bytes(const ix_problem* p) {
 }
 
 size_t stage_key_bytes(const ix_problem* p, const ix_indexer_in* in) {
+  if (fp8_mma(in)) return 0;
   return round_up((size_t)p->batch * (size_t)(p->kv_len + ix::kStagePad) * in->dim * 2);
 }
 size_t stage_scale_bytes(const ix_problem* p, const ix_indexer_in* in) {
-  return in->k_dtype == IX_DTYPE_FP8_E4M3FN ? round_up((size_t)p->batch * (size_t)(p->kv_len + ix::kStagePad) * 4)
-                                             : 0;
+  return in->k_dtype == IX_DTYPE_FP8_E4M3FN && !fp8_mma(in)
+             ? round_up((size_t)p->batch * (size_t)(p->kv_len + ix::kStagePad) * 4)
+             : 0;
 }
 
 size_t argmax_ws(const ix_problem* p, const ix_indexer_in* in) {
@@ -161,10 +174,19 @@ int32_t hip_fail(hipError_t e) {
   return IX_E_HIP;
 }
 
-// Stages the keys (widened to bf16) and fp8 scales into padded copies at
-// `stage` and fills the fused kernel's key fields.
+// Fills the fused kernel's key fields: in the fp8 MFMA form the key cache
+// itself; otherwise staged, padded copies of the keys (widened to bf16) and
+// fp8 scales at `stage`.
 hipError_t stage_fused_keys(const ix_problem* p, const ix_indexer_in* in, char* stage, ix::FusedArgs& a,
                             hipStream_t s) {
+  if (fp8_mma(in)) {
+    a.keys8 = static_cast<const uint8_t*>(in->k);
+    a.key_bstride = p->kv_cap * in->dim;
+    a.scale = in->k_scale;
+    a.scale_bstride = p->kv_cap;
+    a.kv_rows = p->kv_cap;
+    return hipSuccess;
+  }
   const bool fp8 = in->k_dtype == IX_DTYPE_FP8_E4M3FN;
   const int64_t rows_pad = p->kv_len + ix::kStagePad;
   uint16_t* kb = reinterpret_cast<uint16_t*>(stage);
@@ -173,13 +195,17 @@ hipError_t stage_fused_keys(const ix_problem* p, const ix_indexer_in* in, char* 
   a.key_bstride = rows_pad * in->dim;
   a.scale = sb;
   a.scale_bstride = fp8 ? rows_pad : 0;
+  a.kv_rows = rows_pad;
   return ix::launch_stage_keys(in->k, fp8, p->kv_cap * in->dim, in->k_scale, p->kv_cap, kb, sb, p->batch,
                                p->kv_len, rows_pad, in->dim, s);
 }
 
 ix::FusedArgs fused_args(const ix_problem* p, const ix_indexer_in* in, int32_t* idx) {
   ix::FusedArgs a{};
-  a.q = static_cast<const uint16_t*>(in->q);
+  const bool q8 = in->q_dtype == IX_DTYPE_FP8_E4M3FN;
+  a.q = q8 ? nullptr : static_cast<const uint16_t*>(in->q);
+  a.q8 = q8 ? static_cast<const uint8_t*>(in->q) : nullptr;
+  a.q_scale = q8 ? in->q_scale : nullptr;
   a.w = in->w;
   a.idx = idx;
   a.q_start = p->q_start;
@@ -203,7 +229,10 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
     return e == hipSuccess ? IX_OK : hip_fail(e);
   }
   ix::ScoreArgs a{};
-  a.q = static_cast<const uint16_t*>(in->q);
+  const bool q8 = in->q_dtype == IX_DTYPE_FP8_E4M3FN;
+  a.q = q8 ? nullptr : static_cast<const uint16_t*>(in->q);
+  a.q8 = q8 ? static_cast<const uint8_t*>(in->q) : nullptr;
+  a.q_scale = q8 ? in->q_scale : nullptr;
   a.w = in->w;
   a.keys = in->k;
   a.scale = in->k_scale;

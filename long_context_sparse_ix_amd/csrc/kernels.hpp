@@ -9,10 +9,15 @@ namespace ix {
 
 // Fused indexer score + streaming top-k (prefill and chunked prefill).
 struct FusedArgs {
-  const uint16_t* q;      // bf16 [B][n_q][H][d]
+  const uint16_t* q;      // bf16 [B][n_q][H][d], or nullptr when q8 is set
+  const uint8_t* q8;      // e4m3fn codes [B][n_q][H][d], or nullptr
+  const float* q_scale;   // with q8: fp32 [B][n_q][H], the codes' scale
   const float* w;         // [B][n_q][H]
   const uint16_t* keys;   // bf16 rows, row stride d, sequence stride key_bstride
+  const uint8_t* keys8;   // or e4m3fn code rows read in place (fp8 MFMA form; needs q8,
+                          // scale and d in {64, 128}); key_bstride then counts bytes
   const float* scale;     // per-key fp32 scale, or nullptr
+  int64_t kv_rows;        // key rows that exist per sequence (tile loads past them read zeros)
   int32_t* idx;           // [B][n_q][k]; the argmax variant: [B][n_q] best positions
   float* best;            // argmax variant: [B][n_q] best scores (nullable)
   float2* cand;           // workspace: per row C fp32 scores then C int32 positions (C float2 of room)
@@ -44,7 +49,9 @@ constexpr int kStagePad = 64;     // rows of padding after the last key (one til
 
 // Materialised indexer scores: scores[(b*n_q+t)*ld + s] for s <= q_start+t.
 struct ScoreArgs {
-  const uint16_t* q;
+  const uint16_t* q;      // bf16 queries, or nullptr when q8 is set
+  const uint8_t* q8;      // e4m3fn query codes (widened to bf16 at load), or nullptr
+  const float* q_scale;   // with q8: fp32 [rows][H]
   const float* w;
   const void* keys;       // bf16 or e4m3fn codes, row stride d, sequence stride key_bstride
   const float* scale;     // fp8 only

@@ -52,6 +52,7 @@ int main(void) {
          sizeof(ix_project_in));
   F(ix_problem, q_start) F(ix_problem, kv_cap) F(ix_problem, k) F(ix_problem, seq_q_start)
   F(ix_indexer_in, q) F(ix_indexer_in, k_scale) F(ix_indexer_in, path)
+  F(ix_indexer_in, q_dtype) F(ix_indexer_in, reserved) F(ix_indexer_in, q_scale)
   F(ix_attn_in, sm_scale) F(ix_attn_in, kv_splits) F(ix_attn_in, q) F(ix_attn_in, lse)
   F(ix_group_desc, f_mask) F(ix_group_desc, ixr) F(ix_group_desc, attn)
   F(ix_project_in, d_in) F(ix_project_in, reserved) F(ix_project_in, x) F(ix_project_in, w_proj)
@@ -81,7 +82,8 @@ def _prob(**kw):
 
 
 def _ixr(**kw):
-    base = dict(heads=4, dim=32, k_dtype=ix.IX_DTYPE_BF16, path=0, q=DUMMY, w=DUMMY, k=DUMMY, k_scale=None)
+    base = dict(heads=4, dim=32, k_dtype=ix.IX_DTYPE_BF16, path=0, q=DUMMY, w=DUMMY, k=DUMMY, k_scale=None,
+                q_dtype=0, reserved=0, q_scale=None)
     base.update(kw)
     return ix.IndexerIn(**base)
 
@@ -119,9 +121,35 @@ def test_problem_validation(kw, status):
     (dict(k_scale=DUMMY), ix.IX_E_SHAPE), (dict(heads=65), ix.IX_E_SHAPE),
     (dict(dim=24), ix.IX_E_SHAPE), (dict(dim=144), ix.IX_E_SHAPE), (dict(path=3), ix.IX_E_SHAPE),
     (dict(q=DUMMY + 8), ix.IX_E_SHAPE), (dict(dim=48, path=1), ix.IX_E_SHAPE),
+    # fp8 queries: a known query dtype, their scale present exactly when they are fp8
+    (dict(q_dtype=3), ix.IX_E_DTYPE), (dict(q_dtype=ix.IX_DTYPE_FP8_E4M3FN), ix.IX_E_NULL),
+    (dict(q_scale=DUMMY), ix.IX_E_SHAPE), (dict(q_dtype=ix.IX_DTYPE_BF16, q_scale=DUMMY), ix.IX_E_SHAPE),
+    (dict(q_dtype=ix.IX_DTYPE_FP8_E4M3FN, q_scale=DUMMY + 4), ix.IX_E_SHAPE),
+    (dict(reserved=1), ix.IX_E_SHAPE),
 ])
 def test_indexer_validation(kw, status):
     assert _call_ix(_prob(), _ixr(**kw)) == status
+
+
+def test_fp8_query_workspace():
+    """fp8 queries with fp8 keys and d in {64, 128} read the key cache in
+    place: the fused path's workspace is the candidate buffers alone, while
+    the other forms also hold a staged bf16 copy of the keys."""
+    p = _prob(n_q=256, kv_len=4096, kv_cap=4096, k=512)
+    f8 = ix.IX_DTYPE_FP8_E4M3FN
+    cand = 256 * 1024 * 8          # per row: k + max(k, 256) candidate slots of 8 bytes
+    for dim in (64, 128):
+        fast = ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_TOPK,
+                                     _ixr(dim=dim, k_dtype=f8, k_scale=DUMMY, q_dtype=f8, q_scale=DUMMY))
+        staged = ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_TOPK, _ixr(dim=dim, k_dtype=f8, k_scale=DUMMY))
+        assert staged - fast >= 4096 * dim * 2                   # the staged key copy
+        assert fast == cand
+        # the top-1 entry point needs no workspace at all in that form
+        assert ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_ARGMAX,
+                                     _ixr(dim=dim, k_dtype=f8, k_scale=DUMMY, q_dtype=f8, q_scale=DUMMY)) == 0
+    # bf16 keys with fp8 queries: widened form, keys staged as before
+    wide = ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_TOPK, _ixr(dim=128, q_dtype=f8, q_scale=DUMMY))
+    assert wide == ix.ix_workspace_bytes(p, ix.IX_OP_INDEXER_TOPK, _ixr(dim=128))
 
 
 def test_indexer_null_idx_and_workspace():
@@ -198,7 +226,7 @@ def test_topk_scores_validation():
 def test_status_strings():
     for s in range(7):
         assert ix.ix_status_str(s).startswith("IX_")
-    assert ix.ix_abi_version() == 6
+    assert ix.ix_abi_version() == 7
 
 
 def test_index_overlap_validation():
