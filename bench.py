@@ -8,11 +8,13 @@ arranged as two full+shared+shared+shared groups -- the indexer + streaming
 top-k on the 2 full layers and sparse attention on all 8.  Inputs are
 generated on the device before timing starts.  Prints one JSON line.
 
-    python bench.py --op indexer|argmax|attention [--config ...] [--steps K] [--warmup W]
+    python bench.py --op indexer|argmax|attention|project [--fp8-queries] [--config ...] [--steps K] [--warmup W]
 
 times one op of the workload's first layer alone (for profilers): the indexer
 with its streaming top-k, the same score stream with a running maximum
-instead of the top-k (ix_indexer_argmax), or the sparse attention.
+instead of the top-k (ix_indexer_argmax), the sparse attention, or the
+indexer projection; --fp8-queries poses the indexer's queries as e4m3fn codes
+with a per-(row, head) scale.
 
     python bench.py --write-traffic FETCH_DIR WRITE_DIR --traffic-op indexer|attention [--config ...]
 
@@ -432,6 +434,8 @@ def main(argv=None):
                     help="write a kernel's traffic summary from two rocprofv3 --pmc output dirs")
     ap.add_argument("--traffic-op", choices=sorted(TRAFFIC_OPS), default="attention")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
+    ap.add_argument("--fp8-queries", action="store_true",
+                    help="--op indexer/argmax: e4m3fn queries with a per-(row, head) scale")
     ap.add_argument("--op", choices=["indexer", "argmax", "attention", "project"],
                     help="time one op of the workload's first layer alone (warmup + steps launches), for profiling")
     args = ap.parse_args(argv)
@@ -556,6 +560,9 @@ def run(args, pool):
     log("indexer projection")
     project = project_leg(w, torch, synth, ix, args.kernel_reps)
 
+    log("fp8-query indexer")
+    fp8q = fp8_query_leg(w, torch, synth, ix, inp, run_group, fs_mask, args, ix_ms, ix_flop)
+
     allf_ms = None
     if not args.no_all_full:
         log("all-full baseline")
@@ -630,6 +637,7 @@ def run(args, pool):
                             "frac_hbm_peak": tk_bytes / (tk_ms / 1e3) / 1e9 / PEAK_HBM_GBPS},
         "index_overlap": overlap,
         "project": project,
+        "fp8_queries": fp8q,
         "group": {"ms_fsss": ms_step / n_groups, "ms_all_full": None if allf_ms is None else allf_ms / n_groups,
                   "speedup_vs_all_full": None if allf_ms is None else allf_ms / ms_step},
         "cpu_baseline": result_cpu,
@@ -648,6 +656,46 @@ def copy_calibration(torch):
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
+
+
+def fp8_query_leg(w, torch, synth, ix, inp, run_group, fs_mask, args, ix_ms, ix_flop):
+    """The declared fp8-query mode: every full layer's bf16 queries quantised
+    to e4m3fn codes with a per-(row, head) scale (amax / 448, the fp8 key
+    recipe).  Times the indexer call and the whole group step in that mode,
+    and counts how many of the bf16-query run's positions the fp8-query run
+    selects too.  The headline value stays the bf16-query step."""
+    saved = list(inp.ix)
+    for l, e in enumerate(saved):
+        if e is not None:
+            codes, qs = synth.fp8_rows(e["q"].float())
+            inp.ix[l] = dict(e, q=codes.view(torch.uint8), q_scale=qs)
+    idx8 = torch.empty_like(inp.idx_fs)
+    try:
+        e = inp.ix[0]
+        ms = event_time(torch, lambda: ix.ix_indexer_topk(e["q"], e["w"], e["keys"], idx8[0], k_scale=e["k_scale"],
+                                                          q_start=w.q_start, kv_len=w.kv_len,
+                                                          q_scale=e["q_scale"]), args.kernel_reps)
+        step_ms = event_time(torch, lambda: ix.ix_group_forward(inp.ix, inp.attn, fs_mask, idx8, q_start=w.q_start,
+                                                                kv_len=w.kv_len), max(1, args.steps))
+    finally:
+        inp.ix[:] = saved
+        run_group(fs_mask, inp.idx_fs)        # the attention outputs of the bf16-query step again
+        torch.cuda.synchronize()
+    same = ix.ix_index_overlap(inp.idx_fs[0], idx8[0]).float()
+    valid = (inp.idx_fs[0] >= 0).sum(dim=-1).clamp(min=1).float()
+    frac = same / valid
+    del idx8
+    n_groups = w.n_layers // 4
+    tflops = ix_flop / (ms / 1e3) / 1e12
+    fp8_form = w.key_dtype == "fp8" and w.ix_dim in (64, 128)
+    return {"indexer_ms": ms, "tflops": tflops, "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
+            "indexer_speedup_vs_bf16_queries": ix_ms / ms, "ms_per_group": step_ms / n_groups,
+            "tokens_per_s_per_group": w.batch * w.n_q / (step_ms / n_groups / 1e3),
+            "overlap_with_bf16_query_indices": {"mean": float(frac.mean()), "min_row": float(frac.min())},
+            "note": ("fp8 MFMA on the cached e4m3fn keys read in place" if fp8_form
+                     else "codes widened to bf16 (no fp8 MFMA form for these keys)")
+            + "; the first full layer's queries quantised per (row, head); a mode the caller declares, so not "
+              "the headline value"}
 
 
 def project_leg(w, torch, synth, ix, reps):
@@ -686,17 +734,23 @@ def bench_op(args, w, torch, synth, ix):
         print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
                           "ms_per_launch": ms}), flush=True)
         return 0
-    q, wt = synth.indexer_queries(w, dev, 0)
+    qs = None
+    if args.fp8_queries:
+        q, qs, wt = synth.indexer_queries_fp8(w, dev, 0)
+    else:
+        q, wt = synth.indexer_queries(w, dev, 0)
     keys, scale = synth.indexer_keys(w, dev, 0)
     idx = torch.empty((w.batch, w.n_q, w.k), dtype=torch.int32, device=dev)
-    run_ix = lambda: ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len)
+    run_ix = lambda: ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len,
+                                        q_scale=qs)
     fn = run_ix
     if args.op == "argmax":
         pos = torch.empty((w.batch, w.n_q), dtype=torch.int32, device=dev)
-        fn = lambda: ix.ix_indexer_argmax(q, wt, keys, pos, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len)
+        fn = lambda: ix.ix_indexer_argmax(q, wt, keys, pos, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len,
+                                          q_scale=qs)
     if args.op == "attention":
         run_ix()
-        del q, wt, keys, scale
+        del q, qs, wt, keys, scale
         aq = synth.attn_queries(w, dev, 0)
         kv = synth.latent_kv(w, dev, 0)
         out = torch.empty((w.batch, w.n_q, w.q_heads, w.d_v), dtype=torch.bfloat16, device=dev)
@@ -706,7 +760,7 @@ def bench_op(args, w, torch, synth, ix):
     torch.cuda.synchronize()
     ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
     print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
-                      "ms_per_launch": ms}), flush=True)
+                      "fp8_queries": bool(args.fp8_queries), "ms_per_launch": ms}), flush=True)
     if args.copy_calibration:
         copy_calibration(torch)
     return 0
