@@ -660,18 +660,21 @@ def copy_calibration(torch):
 
 def fp8_query_leg(w, torch, synth, ix, inp, run_group, fs_mask, args, ix_ms, ix_flop):
     """The declared fp8-query mode: every full layer's bf16 queries quantised
-    to e4m3fn codes with a per-(row, head) scale (amax / 448, the fp8 key
-    recipe).  Times the indexer call and the whole group step in that mode,
-    and counts how many of the bf16-query run's positions the fp8-query run
-    selects too.  The headline value stays the bf16-query step."""
+    by ix_quantize_queries to e4m3fn codes with a per-(row, head) scale
+    (amax / 448, the fp8 key recipe).  Times the quantiser, the indexer call
+    and the whole group step in that mode, and counts how many of the
+    bf16-query run's positions the fp8-query run selects too.  The headline
+    value stays the bf16-query step."""
     saved = list(inp.ix)
     for l, e in enumerate(saved):
         if e is not None:
-            codes, qs = synth.fp8_rows(e["q"].float())
-            inp.ix[l] = dict(e, q=codes.view(torch.uint8), q_scale=qs)
+            codes, qs = ix.ix_quantize_queries(e["q"])
+            inp.ix[l] = dict(e, q=codes, q_scale=qs)
     idx8 = torch.empty_like(inp.idx_fs)
     try:
         e = inp.ix[0]
+        q16 = saved[0]["q"]
+        qz_ms = event_time(torch, lambda: ix.ix_quantize_queries(q16, e["q"], e["q_scale"]), args.kernel_reps)
         ms = event_time(torch, lambda: ix.ix_indexer_topk(e["q"], e["w"], e["keys"], idx8[0], k_scale=e["k_scale"],
                                                           q_start=w.q_start, kv_len=w.kv_len,
                                                           q_scale=e["q_scale"]), args.kernel_reps)
@@ -688,7 +691,9 @@ def fp8_query_leg(w, torch, synth, ix, inp, run_group, fs_mask, args, ix_ms, ix_
     n_groups = w.n_layers // 4
     tflops = ix_flop / (ms / 1e3) / 1e12
     fp8_form = w.key_dtype == "fp8" and w.ix_dim in (64, 128)
-    return {"indexer_ms": ms, "tflops": tflops, "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
+    qz_bytes = q16.numel() * 3 + q16[..., 0].numel() * 4      # bf16 read, codes + scales written
+    return {"quantize_ms": qz_ms, "quantize_frac_hbm_peak": qz_bytes / (qz_ms / 1e3) / 1e9 / PEAK_HBM_GBPS,
+            "indexer_ms": ms, "tflops": tflops, "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
             "indexer_speedup_vs_bf16_queries": ix_ms / ms, "ms_per_group": step_ms / n_groups,
             "tokens_per_s_per_group": w.batch * w.n_q / (step_ms / n_groups / 1e3),
             "overlap_with_bf16_query_indices": {"mean": float(frac.mean()), "min_row": float(frac.min())},

@@ -325,6 +325,24 @@ typedef struct ix_project_in {
  * field or misalignment, IX_E_HIP on a launch failure. */
 int32_t ix_indexer_project(int64_t rows, const ix_project_in* in, void* q_out, float* w_out, void* stream);
 
+/* Indexer queries into the declared fp8 form (ix_indexer_in.q_dtype =
+ * IX_DTYPE_FP8_E4M3FN).  The pages make the indexer a small FP8 module
+ * (IndexCache notes, section 1); the per-(row, head) scaling is the library's
+ * reading, the same as the key cache's (see ix_append_keys): for every row r
+ * of dim bf16 values q[r][:] (a row is one query row's head, so n_rows =
+ * B*n_q*H for an indexer q of [B][n_q][H][dim]),
+ *   scale[r]    = max_j |q[r][j]| / 448, or 1 for an all-zero row,
+ *   codes[r][j] = e4m3fn(q[r][j] / scale[r]),
+ * rounded to nearest with ties to the even code and saturating at +-448, both
+ * divisions correctly rounded fp32 (a negative value that rounds to zero
+ * keeps its sign bit).  q: bf16 [n_rows][dim], 16-byte aligned; codes: uint8
+ * [n_rows][dim], 16-byte aligned; scale: fp32 [n_rows], 4-byte aligned; all
+ * caller-owned, no workspace.  dim a multiple of 16 in [16, 128]; n_rows >= 0
+ * (0 does nothing).  IX_E_NULL on a NULL pointer, IX_E_SHAPE on a bad size or
+ * misalignment, IX_E_HIP on a launch failure. */
+int32_t ix_quantize_queries(int64_t n_rows, int32_t dim, const void* q, uint8_t* codes, float* scale,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

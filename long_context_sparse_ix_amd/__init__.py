@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "IxError", "ix_abi_version", "ix_status_str", "ix_workspace_bytes", "ix_indexer_topk",
     "ix_sparse_attn", "ix_group_forward", "ix_topk_scores", "ix_index_overlap", "ix_append_keys",
-    "ix_indexer_argmax", "ix_group_forward_noalloc", "ix_indexer_project", "NOALLOC_SCRATCH_BYTES", "lib_path",
+    "ix_indexer_argmax", "ix_group_forward_noalloc", "ix_indexer_project", "ix_quantize_queries",
+    "NOALLOC_SCRATCH_BYTES", "lib_path",
     "load",
     "IX_PATH_AUTO", "IX_PATH_FUSED", "IX_PATH_MATERIALIZED",
 ]
@@ -123,6 +124,8 @@ def load():
     lib.ix_index_overlap.argtypes = [POINTER(Problem), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.ix_indexer_project.restype = c_int32
     lib.ix_indexer_project.argtypes = [c_int64, POINTER(ProjectIn), c_void_p, c_void_p, c_void_p]
+    lib.ix_quantize_queries.restype = c_int32
+    lib.ix_quantize_queries.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
     if lib.ix_abi_version() != ABI_VERSION:   # the structs above follow this version of ix.h
         raise ImportError(f"{LIB_PATH} has ABI {lib.ix_abi_version()}, this binding needs {ABI_VERSION}; rebuild it")
     _lib = lib
@@ -456,3 +459,28 @@ def ix_indexer_project(x, w_proj, q_out, w_out, *, heads, dim, stream=None):
     pin = ProjectIn(heads, dim, d_in, 0, _ptr(x), _ptr(w_proj))
     _check(lib.ix_indexer_project(rows, ctypes.byref(pin), _ptr(q_out), _ptr(w_out), _stream(stream)),
            "ix_indexer_project")
+
+
+def ix_quantize_queries(q, codes=None, scale=None, *, stream=None):
+    """bf16 indexer queries [..., d] -> (e4m3fn codes uint8 [..., d], fp32
+    scale [...]), one scale per row of d values (see ix.h): the ``q`` and
+    ``q_scale`` of the fp8-query indexer.  Returns (codes, scale)."""
+    lib = load()
+    _dev(q, "q")
+    _need(q.dtype == torch.bfloat16 and q.dim() >= 1 and q.is_contiguous(), "q must be contiguous bf16 [..., d]")
+    d = q.shape[-1]
+    if codes is None:
+        codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _dev(codes, "codes"), _dev(scale, "scale")
+    _need(codes.dtype == torch.uint8 and tuple(codes.shape) == tuple(q.shape) and codes.is_contiguous(),
+          "codes must be contiguous uint8 of q's shape")
+    _need(scale.dtype == torch.float32 and tuple(scale.shape) == tuple(q.shape[:-1]) and scale.is_contiguous(),
+          "scale must be contiguous fp32 of q's shape without its last dim")
+    n_rows = q.numel() // d if d else 0
+    if n_rows == 0:
+        return codes, scale
+    _check(lib.ix_quantize_queries(n_rows, d, _ptr(q), _ptr(codes), _ptr(scale), _stream(stream)),
+           "ix_quantize_queries")
+    return codes, scale

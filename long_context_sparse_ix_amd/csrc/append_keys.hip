@@ -16,26 +16,6 @@ namespace ix {
 namespace {
 
 constexpr int kRowsPerWG = 4;
-constexpr float kE4M3Max = 448.0f;
-
-// e4m3fn code of y, |y| <= 448 (round to nearest even; a negative value that
-// rounds to zero keeps its sign bit, -0.0 and +0.0 give +0)
-__device__ __forceinline__ uint32_t e4m3fn_code(float y) {
-  const uint32_t sign = y < 0.0f ? 0x80u : 0u;
-  const float a = fminf(fabsf(y), kE4M3Max);
-  if (a < 0.015625f) {                           // below the smallest normal 2^-6: m * 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 512.0f);   // exact scaling; m == 8 is the smallest normal
-    return sign | m;
-  }
-  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;      // a is a normal fp32 here
-  const float frac = ldexpf(a, -e);                              // exact, in [1, 2)
-  uint32_t m = (uint32_t)rintf((frac - 1.0f) * 8.0f);            // exact operands, one rounding
-  if (m == 8u) {
-    m = 0u;
-    ++e;
-  }
-  return sign | ((uint32_t)(e + 7) << 3) | m;
-}
 
 __global__ __launch_bounds__(kRowsPerWG * kWave) void append_keys_kernel(const float* __restrict__ k_new,
                                                                          uint8_t* __restrict__ k_cache,

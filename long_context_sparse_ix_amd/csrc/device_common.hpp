@@ -104,6 +104,29 @@ __device__ __forceinline__ int64_t seq_start(const int64_t* seq, int b, int64_t 
 // max(x, 0) as one v_med3_f32 (x clamped to [0, +inf]).  fmaxf would add a
 // NaN-quieting max in front; the callers' inputs (MFMA dot products of finite
 // bf16 values) are never NaN.
+// e4m3fn (OCP FP8) code of y in software, |y| clamped to 448: round to
+// nearest with ties to the even code; a negative value that rounds to zero
+// keeps its sign bit, -0.0 and +0.0 give +0.  Exact power-of-two rescaling
+// and one rintf, so the code does not depend on a conversion instruction's
+// rounding or saturation mode.
+constexpr float kE4M3Max = 448.0f;
+__device__ __forceinline__ uint32_t e4m3fn_code(float y) {
+  const uint32_t sign = y < 0.0f ? 0x80u : 0u;
+  const float a = fminf(fabsf(y), kE4M3Max);
+  if (a < 0.015625f) {                           // below the smallest normal 2^-6: m * 2^-9
+    const uint32_t m = (uint32_t)rintf(a * 512.0f);   // exact scaling; m == 8 is the smallest normal
+    return sign | m;
+  }
+  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;      // a is a normal fp32 here
+  const float frac = ldexpf(a, -e);                              // exact, in [1, 2)
+  uint32_t m = (uint32_t)rintf((frac - 1.0f) * 8.0f);            // exact operands, one rounding
+  if (m == 8u) {
+    m = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | m;
+}
+
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

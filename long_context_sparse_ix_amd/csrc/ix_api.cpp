@@ -552,6 +552,16 @@ int32_t ix_indexer_project(int64_t rows, const ix_project_in* in, void* q_out, f
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
+int32_t ix_quantize_queries(int64_t n_rows, int32_t dim, const void* q, uint8_t* codes, float* scale,
+                            void* stream) {
+  if (!q || !codes || !scale) return IX_E_NULL;
+  if (n_rows < 0 || dim < 16 || dim > 128 || dim % 16 != 0 || n_rows > ((int64_t)1 << 54)) return IX_E_SHAPE;
+  if (!aligned16(q) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return IX_E_SHAPE;
+  hipError_t e = ix::launch_quantize_queries(static_cast<const uint16_t*>(q), codes, scale, n_rows, dim,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e);
+}
+
 }  // extern "C"
 
 namespace {

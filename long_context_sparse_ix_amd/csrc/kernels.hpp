@@ -104,6 +104,11 @@ hipError_t launch_append_keys(const float* k_new, uint8_t* k_cache, float* k_sca
                               const int64_t* seq_shift, int64_t shift_bound, int64_t kv_cap, int dim,
                               hipStream_t s);
 
+// bf16 rows [n_rows][dim] -> e4m3fn codes [n_rows][dim] and one fp32 scale
+// per row (max|x|/448, 1 for a zero row); dim a multiple of 16 in [16, 128].
+hipError_t launch_quantize_queries(const uint16_t* src, uint8_t* codes, float* scale, int64_t n_rows, int dim,
+                                   hipStream_t s);
+
 // Indexer inputs from hidden states: [q | w] = x . W^T with x bf16 [M][K],
 // W bf16 [N][K] (K a multiple of 64); the first Nq columns go to q as bf16
 // (nearest, ties to even) [M][Nq], the rest to wo as fp32 [M][N - Nq].

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert {"ix_indexer_topk", "ix_sparse_attn", "ix_group_forward", "ix_topk_scores",
             "ix_workspace_bytes", "ix_status_str", "ix_abi_version", "ix_last_error",
             "ix_index_overlap", "ix_append_keys", "ix_indexer_argmax",
-            "ix_group_forward_noalloc", "ix_indexer_project"} <= set(names)
+            "ix_group_forward_noalloc", "ix_indexer_project", "ix_quantize_queries"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", ix.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ix_\w+)$", out, flags=re.M))
@@ -340,3 +340,19 @@ def test_group_noalloc_validates_and_rejects_oversized_calls_before_any_hip_call
     assert call(4, 0b1, prob=_prob(k=0)) == ix.IX_E_SHAPE
     bad = (ix.AttnIn * 4)(*[_att() for _ in range(3)] + [_att(d_v=100)])
     assert lib.ix_group_forward_noalloc(ctypes.byref(p), 4, 1, ixr, bad, DUMMY, None) == ix.IX_E_SHAPE
+
+
+def test_quantize_queries_validation():
+    lib = ensure_lib()
+    call = lambda n=4, dim=64, q=DUMMY, c=DUMMY, s=DUMMY: lib.ix_quantize_queries(n, dim, q, c, s, None)
+    assert call(q=None) == ix.IX_E_NULL
+    assert call(c=None) == ix.IX_E_NULL
+    assert call(s=None) == ix.IX_E_NULL
+    assert call(n=-1) == ix.IX_E_SHAPE
+    assert call(dim=8) == ix.IX_E_SHAPE
+    assert call(dim=40) == ix.IX_E_SHAPE            # not a multiple of 16
+    assert call(dim=144) == ix.IX_E_SHAPE
+    assert call(n=1 << 60) == ix.IX_E_SHAPE
+    assert call(q=DUMMY + 8) == ix.IX_E_SHAPE
+    assert call(c=DUMMY + 8) == ix.IX_E_SHAPE
+    assert call(s=DUMMY + 2) == ix.IX_E_SHAPE

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import ensure_lib, host, key_bytes, overlap, valid_idx_rows
+from helpers import bits16, ensure_lib, host, key_bytes, overlap, valid_idx_rows
 import ix_synth as synth
 from oracle import dsa_oracle as O
 
@@ -187,3 +187,78 @@ def test_binding_rejects_mismatched_query_forms(ix):
     q16 = torch.zeros(q.shape, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(Exception):
         ix.ix_indexer_topk(q16, wt, keys, idx, k_scale=scale, q_start=0, kv_len=8, q_scale=qs)
+
+
+def _planted_rows(dim, n=333, seed=5):
+    """bf16 query rows: seeded N(0,1) rows whose scales span 1e-3..1e3, then
+    an all-zero row, a constant row (every code 448), a row whose small
+    values land on subnormal codes and round to +0 / -0, and a row with one
+    huge and otherwise tiny values."""
+    g = torch.Generator(device="cpu").manual_seed(seed + dim)
+    q = torch.randn((n, dim), generator=g) * torch.logspace(-3, 3, n).unsqueeze(1)
+    q[0] = 0.0
+    q[1] = 1.5
+    q[2] = torch.tensor([1.0, 2e-5, -2e-5, 1e-6, -1e-6, 3e-5, -7e-6, 0.0] * (dim // 8))
+    q[3] = -1e-7
+    q[3, 5] = 3.0e4
+    return q.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("dim", [16, 48, 64, 128])
+def test_quantize_queries_bit_exact(ix, dim):
+    """ix_quantize_queries against the oracle's key-row quantiser applied to
+    every row of the same bf16 values: codes and scales bit for bit."""
+    q = _planted_rows(dim)
+    print(f"[quantize] dim={dim} rows={q.shape[0]}", flush=True)
+    codes, scale = ix.ix_quantize_queries(q.cuda())
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.quantize_key_rows(O.decode_bf16(bits16(q)))
+    np.testing.assert_array_equal(host(codes), ref_c)
+    np.testing.assert_array_equal(host(scale).view(np.uint32), ref_s.astype(np.float32).view(np.uint32))
+
+
+def test_quantize_queries_shapes(ix):
+    """A [B, n_q, H, d] query tensor maps to [B, n_q, H] scales; zero rows do
+    nothing; sizes the kernel does not take are refused."""
+    q = _planted_rows(64, n=2 * 3 * 5).view(2, 3, 5, 64).cuda()
+    codes, scale = ix.ix_quantize_queries(q)
+    torch.cuda.synchronize()
+    assert codes.shape == (2, 3, 5, 64) and scale.shape == (2, 3, 5)
+    ref_c, ref_s = O.quantize_key_rows(O.decode_bf16(bits16(q)))
+    np.testing.assert_array_equal(host(codes), ref_c)
+    np.testing.assert_array_equal(host(scale), ref_s)
+    ix.ix_quantize_queries(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(Exception):
+        ix.ix_quantize_queries(torch.zeros((4, 40), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_projected_queries_through_the_fp8_indexer(ix):
+    """Hidden rows -> ix_indexer_project (bf16 q) -> ix_quantize_queries ->
+    fp8-query indexer, against the oracle's projection, quantiser and
+    indexer: the codes and scales bit for bit (integer hidden rows and
+    weights make the projection exact on both sides), then the selected sets
+    (the non-power-of-two scales make the scores inexact) by overlap."""
+    w = synth.L16K.with_(name="fp8q_projected", n_q=700, kv_len=700, k=256, key_dtype="fp8", mode="exact")
+    x, wp = synth.projection_inputs(w, "cuda", d_in=256)
+    keys, kscale = synth.indexer_keys(w, "cuda", 0)
+    H, d = w.ix_heads, w.ix_dim
+    q16 = torch.empty((1, w.n_q, H, d), dtype=torch.bfloat16, device="cuda")
+    wt = torch.empty((1, w.n_q, H), dtype=torch.float32, device="cuda")
+    print(f"[projected fp8 indexer] n_q={w.n_q} H={H} d={d}", flush=True)
+    ix.ix_indexer_project(x.view(1, w.n_q, -1), wp, q16, wt, heads=H, dim=d)
+    codes, qs = ix.ix_quantize_queries(q16)
+    idx = torch.full((1, w.n_q, w.k), -7, dtype=torch.int32, device="cuda")
+    ix.ix_indexer_topk(codes, wt, keys, idx, k_scale=kscale, q_start=0, kv_len=w.kv_len, q_scale=qs)
+    torch.cuda.synchronize()
+    q_ref, w_ref = O.indexer_project(bits16(x), bits16(wp), H, d)
+    c_ref, s_ref = O.quantize_key_rows(O.decode_bf16(q_ref))
+    np.testing.assert_array_equal(host(codes).reshape(c_ref.shape), c_ref)
+    np.testing.assert_array_equal(host(qs).reshape(s_ref.shape), s_ref)
+    kb, kd = key_bytes(keys)
+    ref = O.indexer_topk(c_ref.reshape(1, w.n_q, H, d), np.asarray(w_ref).reshape(1, w.n_q, H), kb, kd,
+                         host(kscale), 0, w.kv_len, w.k, q_scale=s_ref.reshape(1, w.n_q, H))
+    got = host(idx)
+    valid_idx_rows(got, 0, w.k)
+    ov, worst = overlap(got, ref)
+    print(f"overlap {ov:.6f} worst row {worst:.6f}")
+    assert ov >= 0.999
