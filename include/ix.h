@@ -111,15 +111,19 @@ typedef struct ix_problem {
  * (IndexCache notes, section 1); this weighted-ReLU form is the library's
  * stated reading.  Queries are bf16 by default; with q_dtype
  * IX_DTYPE_FP8_E4M3FN they are e4m3fn codes times one fp32 scale per (row,
- * head), q[t,h,:] = codes[t,h,:] * q_scale[t,h] (a mode the caller declares:
- * the full-layer kernel then multiplies fp8 codes on fp8 MFMA).  FP8 queries
- * need FP8 keys and d in {64, 128}. */
+ * head), q[t,h,:] = codes[t,h,:] * q_scale[t,h] (a mode the caller declares;
+ * ix_quantize_queries makes them from bf16 queries).  With FP8 keys and d in
+ * {64, 128} the fused kernel then multiplies the codes on fp8 MFMA and reads
+ * the key cache in place; otherwise the codes are widened exactly to bf16.
+ * The scales factor out of the ReLU, so k_scale and q_scale must be >= 0 (as
+ * max|x|/448 scales are); a negative or NaN scale gives unspecified scores
+ * (memory accesses stay inside the buffers). */
 typedef struct ix_indexer_in {
   int32_t heads;    /* H, 1..64                                                */
   int32_t dim;      /* d, a multiple of 16 in 16..128                          */
   int32_t k_dtype;  /* ix_dtype of `k`                                         */
   int32_t path;     /* ix_indexer_path                                         */
-  const void* q;    /* bf16 [B][n_q][H][d]                                     */
+  const void* q;    /* [B][n_q][H][d]: bf16, or uint8 e4m3fn codes (q_dtype)   */
   const float* w;   /* fp32 [B][n_q][H]                                        */
   const void* k;    /* [B][kv_cap][d]: bf16, or uint8 e4m3fn codes             */
   const float* k_scale; /* fp32 [B][kv_cap] for FP8 keys; must be NULL for bf16 */
