@@ -478,8 +478,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_indexer_topk_kernel(FusedAr
   else key_bytes = reinterpret_cast<const unsigned char*>(a.keys + (int64_t)b * a.key_bstride);
   auto issue_tile = [&](int it, int slot) {
     const int s0 = it * kTileKeys;
-    const int64_t rows_left = a.kv_rows - s0;                    // >= 1: tiles start below the last key
-    const int tile_rows = rows_left < kTileKeys ? (int)rows_left : kTileKeys;
+    // the staged copy is padded by a tile, so its tiles load whole; the key
+    // cache read in place ends at kv_rows (>= 1 rows past s0: tiles start
+    // below the last key)
+    int tile_rows = kTileKeys;
+    if constexpr (Q8) {
+      const int64_t rows_left = a.kv_rows - s0;
+      if (rows_left < kTileKeys) tile_rows = (int)rows_left;
+    }
     unsigned char* tb = key_lds0 + slot * G::tile_bytes;
     const unsigned char* tile = key_bytes + (int64_t)s0 * G::row_bytes;
     const __amdgpu_buffer_rsrc_t kr =
