@@ -262,3 +262,33 @@ def test_projected_queries_through_the_fp8_indexer(ix):
     ov, worst = overlap(got, ref)
     print(f"overlap {ov:.6f} worst row {worst:.6f}")
     assert ov >= 0.999
+
+
+@pytest.mark.parametrize("kv_len", [70_001, 200_001])
+def test_decode_shape_long_rows(ix, kv_len):
+    """Decode-shaped calls (a few sequences, one new row each, long contexts):
+    the score kernel widens the codes and runs the top-k's wave-local stage;
+    positions bit for bit on integer inputs."""
+    w = BASE.with_(name=f"fp8q_decode_{kv_len}", batch=4, n_q=1, q_start=kv_len - 1, kv_len=kv_len, k=2048)
+    inputs = _inputs(w)
+    got = _run(ix, w, 0, inputs)
+    valid_idx_rows(got, w.q_start, w.k)
+    np.testing.assert_array_equal(got, _oracle(w, inputs))
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_sequences_of_different_lengths(ix, path):
+    """Per-sequence starts (ix_problem.seq_q_start) with fp8 queries: row t of
+    sequence b sits at starts[b] + t; positions bit for bit."""
+    starts = [0, 437, 1200]
+    w = BASE.with_(name="fp8q_varlen", batch=3, n_q=190, q_start=max(starts), kv_len=1390, k=300)
+    q, qs, wt, keys, scale = _inputs(w)
+    idx = torch.full((w.batch, w.n_q, w.k), -7, dtype=torch.int32, device="cuda")
+    print(f"[ix8 varlen] starts={starts} path={path}", flush=True)
+    ix.ix_indexer_topk(q, wt, keys, idx, k_scale=scale, q_start=w.q_start, kv_len=w.kv_len, path=path,
+                       seq_q_start=torch.tensor(starts, dtype=torch.int64, device="cuda"), q_scale=qs)
+    torch.cuda.synchronize()
+    kb, kd = key_bytes(keys)
+    ref = O.indexer_topk(host(q), host(wt), kb, kd, host(scale), np.array(starts), w.kv_len, w.k,
+                         q_scale=host(qs))
+    np.testing.assert_array_equal(host(idx), ref)
