@@ -262,8 +262,15 @@ int32_t run_indexer(const ix_problem* p, const ix_indexer_in* in, int32_t* idx, 
   return e == hipSuccess ? IX_OK : hip_fail(e);
 }
 
+// One attention layer.  chain == nullptr: its split partials (if any) are
+// merged by a kernel of their own right after it.  Otherwise *chain holds an
+// earlier layer's partials still to be merged (splits == 0: none): they are
+// merged in this launch's prologue when it runs four waves per (row, split),
+// else by their own kernel first; and this layer's partials are left in
+// *chain for a later launch (the caller flushes the last with
+// ix::launch_attn_combine).
 int32_t run_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, void* ws,
-                 hipStream_t s) {
+                 hipStream_t s, ix::CombineArgs* chain = nullptr) {
   ix::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(in->q);
   a.kv = static_cast<const uint16_t*>(in->kv);
@@ -287,8 +294,18 @@ int32_t run_attn(const ix_problem* p, const ix_attn_in* in, const int32_t* idx, 
     a.part_o = static_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(items * in->d_v * 4));
   }
-  hipError_t e = ix::launch_sparse_attn(a, in->d_qk, in->d_v, s);
-  return e == hipSuccess ? IX_OK : hip_fail(e);
+  hipError_t e = hipSuccess;
+  if (chain && chain->splits > 1) {
+    if (a.wpi > 1) a.prev = *chain;
+    else e = ix::launch_attn_combine(*chain, s);
+    chain->splits = 0;
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  const bool defer = chain && a.splits > 1;
+  e = ix::launch_sparse_attn(a, in->d_qk, in->d_v, s, defer);
+  if (e != hipSuccess) return hip_fail(e);
+  if (defer) *chain = ix::CombineArgs{a.part_o, a.part_ml, a.out, a.lse, a.rows, a.Hq, a.splits, in->d_v};
+  return IX_OK;
 }
 
 int32_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
@@ -299,16 +316,26 @@ int32_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
   return IX_OK;
 }
 
+// The group's attention layers keep their split partials in two alternating
+// halves of this size (a layer's partials are merged by the next layer's
+// launch, which writes its own into the other half).
+size_t group_attn_half(const ix_problem* p, int32_t n_layers, const ix_attn_in* attn) {
+  size_t half = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const size_t w = attn_ws(p, &attn[l]);
+    if (w > half) half = w;
+  }
+  return half;
+}
+
 size_t group_ws(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix_indexer_in* ixr,
                 const ix_attn_in* attn) {
-  size_t need = 0;
+  size_t need = 2 * group_attn_half(p, n_layers, attn);
   for (int l = 0; l < n_layers; ++l) {
     if ((f_mask >> l) & 1u) {
       const size_t w = indexer_ws(p, &ixr[l]);
       if (w > need) need = w;
     }
-    const size_t w = attn_ws(p, &attn[l]);
-    if (w > need) need = w;
   }
   return need;
 }
@@ -569,16 +596,28 @@ namespace {
 int32_t run_group(const ix_problem* p, int32_t n_layers, uint64_t f_mask, const ix_indexer_in* ixr,
                   const ix_attn_in* attn, int32_t* idx, void* ws, hipStream_t s) {
   const size_t slot = (size_t)p->batch * p->n_q * p->k;
+  const size_t half = group_attn_half(p, n_layers, attn);
   int32_t* cur = nullptr;
   int f = 0;
+  ix::CombineArgs pending{};           // the previous layer's partials, merged by the next launch
   for (int l = 0; l < n_layers; ++l) {
     if ((f_mask >> l) & 1u) {          // full layer: fresh positions into its own slot
+      if (pending.splits > 1) {        // the indexer's workspace overlaps the partials
+        hipError_t e = ix::launch_attn_combine(pending, s);
+        pending.splits = 0;
+        if (e != hipSuccess) return hip_fail(e);
+      }
       cur = idx + slot * f++;
       const int32_t st = run_indexer(p, &ixr[l], cur, ws, s);
       if (st != IX_OK) return st;
     }
-    const int32_t st = run_attn(p, &attn[l], cur, ws, s);   // shared layers reuse `cur` untouched
+    // shared layers reuse `cur` untouched
+    const int32_t st = run_attn(p, &attn[l], cur, static_cast<char*>(ws) + (l & 1) * half, s, &pending);
     if (st != IX_OK) return st;
+  }
+  if (pending.splits > 1) {
+    hipError_t e = ix::launch_attn_combine(pending, s);
+    if (e != hipSuccess) return hip_fail(e);
   }
   return IX_OK;
 }

@@ -127,6 +127,16 @@ hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int32_t* cou
                                 hipStream_t s);
 
 // Sparse gather attention.
+// Split partials of one attention launch that still have to be merged into
+// its output (splits > 1), or none (splits == 0).
+struct CombineArgs {
+  const float* part_o;    // [rows][splits][16][Dv]
+  const float* part_ml;   // [rows][splits][16][2]
+  uint16_t* out;          // [rows][Hq][Dv]
+  float* lse;             // [rows][Hq] or nullptr
+  int rows, Hq, splits, Dv;
+};
+
 struct AttnArgs {
   const uint16_t* q;      // [B][n_q][Hq][D]
   const uint16_t* kv;     // [B][cap][D]
@@ -140,8 +150,14 @@ struct AttnArgs {
   int rows, n_q, Hq, k, splits, slots_per_split;
   int wpi;                // waves per (row, split): 1, or 4 sharing the split's slots
   float scale_log2;       // sm_scale * log2(e)
+  CombineArgs prev;       // wpi == 4 only: an earlier launch's partials, merged in this
+                          // launch's prologue (prev.splits == 0: none)
 };
 bool attn_shape_supported(int d_qk, int d_v);
-hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s);
+// Launches the attention; with splits > 1 also the merge of its partials,
+// unless defer_combine (the caller then merges them later: in a following
+// wpi == 4 launch's prologue, or by launch_attn_combine).
+hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s, bool defer_combine = false);
+hipError_t launch_attn_combine(const CombineArgs& c, hipStream_t s);
 
 }  // namespace ix

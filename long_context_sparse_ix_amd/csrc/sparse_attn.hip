@@ -132,9 +132,81 @@ struct AttnLds {
   static constexpr int tiles = kWavesPerWG * wave_bytes;
   static constexpr int merge = 2 * MT * kWave * 16;
   static constexpr int stat_off = ((tiles > merge ? tiles : merge) + 15) / 16 * 16;
-  static constexpr int bytes = stat_off + 2 * kWavesPerWG * 16 * 4;
+  static constexpr int comb_off = stat_off + 2 * kWavesPerWG * 16 * 4;   // fused merge: [2][64] weights, [2][2] stats
+  static constexpr int bytes = comb_off + (2 * 64 + 4) * 4;
   static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
 };
+
+// Merge of split partials, per item (row, head): base-2 log-sum-exp weights
+// exp2(m_s - M) / L of the splits from one wave, then each of 128 threads
+// folds 4 consecutive value dims (Dv <= 512) over the splits in ascending
+// split order.  Used by the merge kernel and, for a launch chained behind
+// another, in the later launch's prologue; the same code gives both the same
+// bits.  The first kMergePre splits' partials are loaded before the weights
+// are known (split indices clamped to the last split; the weights of slots
+// past it are never used).
+constexpr int kMergePre = 8;
+
+__device__ __forceinline__ void merge_load(const CombineArgs& c, int item, int dv, f32x4 (&v)[kMergePre]) {
+  const int r = item / c.Hq, h = item % c.Hq;
+  const float* po = c.part_o + ((int64_t)r * c.splits * 16 + h) * c.Dv + min(dv, c.Dv - 4);
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u)
+    v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)min(u, c.splits - 1) * 16 * c.Dv);
+}
+
+// Lane s of the weight wave: split min(s, S-1)'s (m, l) (the lanes past the
+// last split are masked where the weights are formed, not here, so nothing
+// waits for these loads before it has to).
+__device__ __forceinline__ void merge_ml_load(const CombineArgs& c, int item, int lane, float& ms, float& ls) {
+  const int r = item / c.Hq, h = item % c.Hq;
+  const float* ml = c.part_ml + ((int64_t)r * c.splits * 16 + h) * 2;   // split s at + s*32
+  const int sl = min(lane, c.splits - 1);
+  ms = ml[(int64_t)sl * 32];
+  ls = ml[(int64_t)sl * 32 + 1];
+}
+
+// One whole wave: wgt[s] for s < S and stat = (M, L).
+__device__ __forceinline__ void merge_weights(float ms_raw, float ls_raw, int lane, int S, float* wgt, float* stat) {
+  const float ms = lane < S ? ms_raw : -INFINITY;
+  const float ls = lane < S ? ls_raw : 0.0f;
+  float M = ms;
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) M = fmaxf(M, __shfl_xor(M, dd));
+  const float e = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+  float L = ls * e;
+#pragma unroll
+  for (int dd = 32; dd >= 1; dd >>= 1) L += __shfl_xor(L, dd);
+  if (lane < S) wgt[lane] = L > 0.0f ? e / L : 0.0f;
+  if (lane == 0) {
+    stat[0] = M;
+    stat[1] = L;
+  }
+}
+
+__device__ __forceinline__ void merge_fold(const CombineArgs& c, int item, int dv, const f32x4 (&v)[kMergePre],
+                                           const float* wgt, const float* stat) {
+  const int r = item / c.Hq, h = item % c.Hq;
+  const int S = c.splits;
+  if (dv < c.Dv) {
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u)
+      if (u < S) acc += v[u] * wgt[u];
+    const float* po = c.part_o + ((int64_t)r * S * 16 + h) * c.Dv + dv;
+    for (int sp = kMergePre; sp < S; ++sp) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)sp * 16 * c.Dv) * wgt[sp];
+    const u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(c.out + ((int64_t)r * c.Hq + h) * c.Dv + dv) = o;
+  }
+  if (dv == 0 && c.lse)
+    c.lse[(int64_t)r * c.Hq + h] = stat[1] > 0.0f ? (stat[0] + log2f(stat[1])) * kLn2 : -INFINITY;
+}
+
+// Workgroup barrier that orders LDS only (s_barrier after this wave's LDS
+// operations), so loads in flight are not drained.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int KS, int MT, int WPI>
 __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(AttnArgs a) {
@@ -153,6 +225,24 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   const int b = r / a.n_q;
   unsigned char* const tile = smem + wave * L::wave_bytes;
 
+  // An earlier launch's partials merged here (whole workgroups, two items per
+  // pass, 128 threads each): the first pass's partials and split statistics
+  // are loaded ahead of everything else (every lane loads, no branch), so
+  // waiting for them waits for nothing of this launch; the merge itself runs
+  // once this launch's index words are requested, before its query slice and
+  // gathers (merging while the first gathers were in flight measured slower).
+  const CombineArgs mc = a.prev;          // by value (a reference into the kernel arguments costs a stack frame)
+  const int m_items = WPI > 1 && mc.splits > 1 ? mc.rows * mc.Hq : 0;
+  const int m_half = threadIdx.x >> 7, m_tid = threadIdx.x & 127;
+  f32x4 mv[kMergePre];
+  float m_ms = -INFINITY, m_ls = 0.0f;
+  if (m_items > 0) {
+    const int it0 = min(2 * (int)blockIdx.x + m_half, m_items - 1);
+    merge_load(mc, it0, 4 * m_tid, mv);
+    merge_ml_load(mc, it0, m_tid & (kWave - 1), m_ms, m_ls);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // Query slice as the B operand: head n16, elements [32ks + 8g, +8) -- the
   // MFMA's k-group g of step ks; the key operand is read the same way.
   // Lanes of heads past Hq load head 0's query (in bounds, finite): their
@@ -160,11 +250,6 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   // branch splits them.
   const bool hq_ok = n16 < a.Hq;
   bf16x8 qf[KS];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-  }
 
   int j0 = sp * a.slots_per_split;
   int j1 = min(a.k, j0 + a.slots_per_split);
@@ -176,9 +261,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   const int32_t* irow = a.idx + (int64_t)r * a.k;
   const uint16_t* kvb = a.kv + (int64_t)b * a.kv_bstride;
 
-  f32x4 oacc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{};
+  f32x4 oacc[MT];                         // zeroed after a chained merge (not live beside it)
   float m_run = -INFINITY, l_run = 0.0f;
 
   // Loads are unconditional: exec-masked load branches make the compiler's
@@ -348,8 +431,32 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   bf16x8 kA[G::NI], kB[G::NI];
   const int w0 = slot_word(j0), w1 = slot_word(j0 + 16);
   int r1 = slot_word(j0 + 32), r2 = slot_word(j0 + 48);
+  if (m_items > 0) {                     // the earlier launch's merge
+    float* mw = reinterpret_cast<float*>(smem + L::comb_off);     // [2][64] weights, then [2][2] stats
+    for (int base = 2 * (int)blockIdx.x; base < m_items; base += 2 * (int)gridDim.x) {
+      const int it = base + m_half;
+      const bool ok = it < m_items;
+      if (base != 2 * (int)blockIdx.x) {     // a later pass: the previous one's weights were read
+        lds_barrier();
+        const int itc = min(it, m_items - 1);
+        merge_load(mc, itc, 4 * m_tid, mv);
+        merge_ml_load(mc, itc, m_tid & (kWave - 1), m_ms, m_ls);
+      }
+      if (ok && m_tid < kWave) merge_weights(m_ms, m_ls, m_tid, mc.splits, mw + 64 * m_half, mw + 128 + 2 * m_half);
+      lds_barrier();
+      if (ok) merge_fold(mc, it, 4 * m_tid, mv, mw + 64 * m_half, mw + 128 + 2 * m_half);
+    }
+  }
+  {
+    const uint16_t* qrow = a.q + ((int64_t)r * a.Hq + (hq_ok ? n16 : 0)) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  }
   bool vA = fetch(j0, w0, kA);
   bool vB = fetch(j0 + 16, w1, kB);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{};
+
   if (j0 < j1) {
     uint32_t vm = park(kA, vA, tile);
     // Register-class hint: the query slice stays in AGPRs (an MFMA operand may
@@ -443,47 +550,21 @@ __global__ __launch_bounds__(kWavesPerWG * kWave, 1) void sparse_attn_kernel(Att
   }
 }
 
-// Merge the split partials of one (row, head): base-2 log-sum-exp weights
-// exp2(m_s - M) / L are computed once into LDS, then every thread folds four
-// consecutive value dims over the splits.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int Dv) {
+// Merge of one item (row, head) of a launch's split partials per workgroup.
+__global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs c) {
   __shared__ float wgt[64];
   __shared__ float stat[2];
   const int item = blockIdx.x;              // r * Hq + h
-  const int r = item / a.Hq, h = item % a.Hq;
-  const int S = a.splits;
-  const float* ml = a.part_ml + ((int64_t)r * S * 16 + h) * 2;     // split s at + s*32
+  const int dv = threadIdx.x * 4;
+  f32x4 v[kMergePre];
+  merge_load(c, item, dv, v);
   if (threadIdx.x < kWave) {
-    const int l = threadIdx.x;
-    const float ms = l < S ? ml[(int64_t)l * 32] : -INFINITY;
-    const float ls = l < S ? ml[(int64_t)l * 32 + 1] : 0.0f;
-    float M = ms;
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) M = fmaxf(M, __shfl_xor(M, dd));
-    const float e = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-    float L = ls * e;
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) L += __shfl_xor(L, dd);
-    if (l < S) wgt[l] = L > 0.0f ? e / L : 0.0f;
-    if (l == 0) {
-      stat[0] = M;
-      stat[1] = L;
-    }
+    float ms, ls;
+    merge_ml_load(c, item, threadIdx.x, ms, ls);
+    merge_weights(ms, ls, threadIdx.x, c.splits, wgt, stat);
   }
   __syncthreads();
-  const float* po = a.part_o + ((int64_t)r * S * 16 + h) * Dv;     // split s at + s*16*Dv
-  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * Dv;
-  for (int dv = threadIdx.x * 4; dv < Dv; dv += blockDim.x * 4) {
-    f32x4 acc = f32x4{};
-    for (int s = 0; s < S; ++s) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)s * 16 * Dv + dv);
-      acc += v * wgt[s];
-    }
-    const u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *reinterpret_cast<u32x2*>(orow + dv) = o;
-  }
-  if (threadIdx.x == 0 && a.lse)
-    a.lse[(int64_t)r * a.Hq + h] = stat[1] > 0.0f ? (stat[0] + log2f(stat[1])) * kLn2 : -INFINITY;
+  merge_fold(c, item, dv, v, wgt, stat);
 }
 
 template <int KS, int MT, int WPI>
@@ -499,13 +580,15 @@ hipError_t launch_attn_w(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int KS, int MT>
-hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s, bool defer_combine) {
   if (a.wpi != 1 && a.wpi != kWavesPerWG) return hipErrorInvalidValue;
   if (a.wpi > 1 && a.slots_per_split % (16 * kWavesPerWG) != 0) return hipErrorInvalidValue;
+  if (a.prev.splits > 1 && (a.wpi == 1 || a.prev.Dv > 512 || a.prev.Dv % 4 != 0 || a.prev.Hq > 16 ||
+                            a.prev.splits > 64))
+    return hipErrorInvalidValue;
   hipError_t e = a.wpi == 1 ? launch_attn_w<KS, MT, 1>(a, s) : launch_attn_w<KS, MT, kWavesPerWG>(a, s);
-  if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.rows * a.Hq)), dim3(128), 0, s, a, 16 * MT);
-  return hipGetLastError();
+  if (e != hipSuccess || a.splits == 1 || defer_combine) return e;
+  return launch_attn_combine(CombineArgs{a.part_o, a.part_ml, a.out, a.lse, a.rows, a.Hq, a.splits, 16 * MT}, s);
 }
 
 }  // namespace
@@ -515,12 +598,19 @@ bool attn_shape_supported(int d_qk, int d_v) {
          (d_qk == 64 && d_v == 64);
 }
 
-hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s) {
-  if (d_qk == 576 && d_v == 512) return launch_attn_t<18, 32>(a, s);
-  if (d_qk == 128 && d_v == 96) return launch_attn_t<4, 6>(a, s);
-  if (d_qk == 128 && d_v == 128) return launch_attn_t<4, 8>(a, s);
-  if (d_qk == 64 && d_v == 64) return launch_attn_t<2, 4>(a, s);
+hipError_t launch_sparse_attn(const AttnArgs& a, int d_qk, int d_v, hipStream_t s, bool defer_combine) {
+  if (d_qk == 576 && d_v == 512) return launch_attn_t<18, 32>(a, s, defer_combine);
+  if (d_qk == 128 && d_v == 96) return launch_attn_t<4, 6>(a, s, defer_combine);
+  if (d_qk == 128 && d_v == 128) return launch_attn_t<4, 8>(a, s, defer_combine);
+  if (d_qk == 64 && d_v == 64) return launch_attn_t<2, 4>(a, s, defer_combine);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_combine(const CombineArgs& c, hipStream_t s) {
+  if (c.splits <= 1) return hipSuccess;
+  if (c.Dv > 512 || c.Dv % 4 != 0 || c.Hq > 16 || c.splits > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(c.rows * c.Hq)), dim3(128), 0, s, c);
+  return hipGetLastError();
 }
 
 }  // namespace ix
