@@ -45,7 +45,8 @@
 //   * few rows (decode): the four waves of a workgroup share one (row, split),
 //     each taking a quarter of its slots, and merge their (o, m, l) through
 //     LDS; with several splits per row the merged partials go to the
-//     workspace and a combine kernel merges them.
+//     workspace and a merge kernel combines them, or, for a layer followed by
+//     another such launch in a layer group, that launch's prologue does.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
