@@ -16,8 +16,8 @@
 //     waits overlap the other's MFMAs); row blocks are issued longest-first so
 //     the causal triangle drains evenly;
 //   * keys stream HBM -> LDS with direct loads (buffer_load_dwordx4 ... lds,
-//     no VGPR staging) into a 4-slot ring of 64-key bf16 tiles shared by the 4
-//     rows, rows XOR-swizzled so B-operand reads are bank-conflict free; tiles
+//     no VGPR staging) into a 4-slot ring of 64-key tiles (bf16, or e4m3fn
+//     codes in the Q8 instance) shared by the 4 rows, rows XOR-swizzled so B-operand reads are bank-conflict free; tiles
 //     are consumed in pairs, one LDS-only barrier per pair;
 //   * each wave keeps its row's heads x d query slice in registers as the MFMA
 //     A operand (M = heads) and reads 32-key halves of a tile as the B operand
@@ -37,6 +37,14 @@
 //     an exact radix select;
 //   * at the end an exact radix select (score desc, position asc) picks the k
 //     winners and a stable pass writes their positions in ascending order.
+//
+// Queries declared as e4m3fn codes (one scale per row and head, IndexCache
+// notes, section 1: an FP8 indexer) run the Q8 instance when the keys are
+// e4m3fn too and d is 64 or 128: the tiles hold the cache's raw codes, read
+// in place (no staging copy), and v_mfma_f32_32x32x64_f8f6f4 multiplies codes
+// by codes; the query scale folds into the head weight and the key scale
+// multiplies the finished head sum.  Other fp8-query forms widen the codes
+// to bf16 in the prologue and run the bf16 instances.
 //
 // The same kernel with SELECT = false keeps only a running maximum per lane
 // instead of the candidate buffer: the row's best position (equal scores:
