@@ -162,3 +162,29 @@ def test_irregular_masks_against_oracle(ix, roles):
         assert torch.equal(solo, atl[l]["out"]), f"layer {l} did not attend over slot {expect_used[l]}"
         err = np.abs(atl[l]["out"].float().cpu().numpy()[:, rows] - ref["O"][l]).max()
         assert err <= 2e-2, (l, err)
+
+
+@pytest.mark.parametrize("roles", ["FSSS", "FSFSS", "FFSSF"])
+def test_chained_split_merges_equal_standalone_calls(ix, roles):
+    """Decode-shaped groups (few rows, so each attention launch splits the
+    slots and merges partials): inside the group a layer's partials are merged
+    by the next layer's launch, or by a merge kernel before a full layer's
+    indexer and after the last layer.  Every layer's output and lse must equal
+    a standalone ix_sparse_attn over the same slot, bit for bit; one layer
+    passes no lse buffer."""
+    w = synth.DECODE_B32.with_(name=f"decode_chain_{roles}", batch=6, q_start=5000, kv_len=5001,
+                               kv_cap=5001, roles=roles)
+    ixl, atl = _layers(w, roles)
+    atl[2]["lse"] = None
+    idx = _group(ix, w, roles, ixl, atl)
+    f_slot = -1
+    for l, r in enumerate(roles):
+        f_slot += r == "F"
+        out = torch.empty_like(atl[l]["out"])
+        lse = None if atl[l]["lse"] is None else torch.empty_like(atl[l]["lse"])
+        ix.ix_sparse_attn(atl[l]["q"], atl[l]["kv"], idx[f_slot], out, lse=lse, q_start=w.q_start,
+                          kv_len=w.kv_len)
+        torch.cuda.synchronize()
+        assert torch.equal(out, atl[l]["out"]), f"layer {l}"
+        if lse is not None:
+            assert torch.equal(lse, atl[l]["lse"]), f"layer {l} lse"
