@@ -188,3 +188,31 @@ def test_chained_split_merges_equal_standalone_calls(ix, roles):
         assert torch.equal(out, atl[l]["out"]), f"layer {l}"
         if lse is not None:
             assert torch.equal(lse, atl[l]["lse"]), f"layer {l} lse"
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+def test_forced_splits_on_many_rows_merge_by_kernel(ix, splits):
+    """Many rows (one wave per row and split) with the slots forced into
+    several splits: such launches cannot merge an earlier layer's partials in
+    their prologue, so the group merges each layer's with the merge kernel;
+    outputs and lse equal standalone calls with the same split count, bit
+    for bit."""
+    w = synth.TINY_L1K.with_(name=f"group_splits_{splits}", k=256)
+    roles = "FSSFS"
+    w = w.with_(roles=roles)
+    ixl, atl = _layers(w, roles)
+    mask = sum(1 << i for i, r in enumerate(roles) if r == "F")
+    idx = torch.full((roles.count("F"), w.batch, w.n_q, w.k), -7, dtype=torch.int32, device="cuda")
+    print(f"[group] {w.name} roles={roles} kv_splits={splits}", flush=True)
+    ix.ix_group_forward(ixl, atl, mask, idx, q_start=w.q_start, kv_len=w.kv_len, kv_splits=splits)
+    torch.cuda.synchronize()
+    f_slot = -1
+    for l, r in enumerate(roles):
+        f_slot += r == "F"
+        out = torch.empty_like(atl[l]["out"])
+        lse = torch.empty_like(atl[l]["lse"])
+        ix.ix_sparse_attn(atl[l]["q"], atl[l]["kv"], idx[f_slot], out, lse=lse, q_start=w.q_start,
+                          kv_len=w.kv_len, kv_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, atl[l]["out"]), f"layer {l}"
+        assert torch.equal(lse, atl[l]["lse"]), f"layer {l} lse"
