@@ -63,6 +63,7 @@ BASE = synth.L16K.with_(name="fp8q_exact", batch=2, n_q=301, q_start=700, kv_len
     ("fp8", 3, 128),      # fp8 MFMA form, one head tile
     ("fp8", 17, 64),
     ("fp8", 5, 32),       # widened form (no fp8 MFMA for d = 32)
+    ("fp8", 7, 16),       # widened form, the narrowest key
     ("bf16", 64, 128),    # widened form (bf16 keys)
 ])
 def test_exact_bit_exact(ix, path, key_dtype, heads, dim):
@@ -72,6 +73,19 @@ def test_exact_bit_exact(ix, path, key_dtype, heads, dim):
                    ix_dim=dim)
     inputs = _inputs(w)
     got = _run(ix, w, path, inputs)
+    valid_idx_rows(got, w.q_start, w.k)
+    np.testing.assert_array_equal(got, _oracle(w, inputs))
+
+
+@pytest.mark.parametrize("key_dtype", ["fp8", "bf16"])
+@pytest.mark.parametrize("heads,dim", [(64, 48), (40, 80), (33, 112)])
+def test_materialised_widths(ix, key_dtype, heads, dim):
+    """Widths the fused kernel does not take (the materialised path widens
+    the codes for every multiple of 16): positions bit for bit."""
+    w = BASE.with_(name=f"fp8q_width_{key_dtype}_{heads}x{dim}", batch=1, key_dtype=key_dtype, ix_heads=heads,
+                   ix_dim=dim)
+    inputs = _inputs(w)
+    got = _run(ix, w, 0, inputs)
     valid_idx_rows(got, w.q_start, w.k)
     np.testing.assert_array_equal(got, _oracle(w, inputs))
 
