@@ -622,8 +622,13 @@ __global__ __launch_bounds__(256) void tk_wave_local_kernel(ChunkArgs a) {
   const int pos0 = piece * kLocalSpan;
   const float* src = a.scores + (int64_t)row * a.ld;
   float v[kLocalNV];
+  if (pos0 + kLocalSpan <= n) {
 #pragma unroll
-  for (int j = 0; j < kLocalNV; ++j) v[j] = src[min(pos0 + kWave * j + l, n - 1)];
+    for (int j = 0; j < kLocalNV; ++j) v[j] = src[pos0 + kWave * j + l];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kLocalNV; ++j) v[j] = src[min(pos0 + kWave * j + l, n - 1)];
+  }
   const int cap = kLocalCap / P;
   __shared__ uint32_t hist[4][kLocalBins];
   const uint4 r = wave_keep_top<kLocalNV>(v, n - pos0, pos0, cap, hist[wave],
@@ -632,11 +637,11 @@ __global__ __launch_bounds__(256) void tk_wave_local_kernel(ChunkArgs a) {
 }
 
 // Per row: the pieces' kept entries (piece c at slots [c*cap, c*cap + kept_c)
-// of the candidate list, in position order).  Entries at or below the largest
-// dropped key D rank below some dropped entry; if at least k entries lie
-// above D, the row's k-th best is among them and every dropped entry ranks
-// below it, so the k-th best of the entries above D and a stable emission
-// give the row's top k.  Otherwise the whole-row select runs.
+// of the candidate list, in position order).  D, the largest of the pieces'
+// bounds, is at or above every dropped key; if at least k entries lie above
+// D, the row's k-th best is among them and every dropped entry ranks below
+// it, so the k-th best of the entries above D and a stable emission give the
+// row's top k.  Otherwise the whole-row select runs.
 // Thread t holds the 8 contiguous slots [8t, 8t + 8) in registers, so the
 // valid entries' list order is thread order and nothing is copied to LDS:
 //   A  every thread loads its slots and one piece's record at once; per-wave
@@ -708,27 +713,47 @@ __global__ __launch_bounds__(kFT) void tk_merge_kernel(ChunkArgs a, int32_t* __r
     gmax = max(gmax, q.w);
   }
   if ((int)m >= a.k) {
-    // B: slot s0 + u lies in piece c0 (or c0 + 1: cap >= 16 > 8 slots); for
-    // s < 2^13 and cap <= 2^13, floor(s / cap) = umulhi(s, floor((2^32 - 1) / cap) + 1)
+    // slot s0 + u lies in piece c0 (or c0 + 1: cap >= 16 > 8 slots); for
+    // s < 2^13 and cap <= 2^13, floor(s / cap) = umulhi(s, floor((2^32 - 1) / cap) + 1).
+    // This thread's slots [0, e0) hold piece c0's kept entries and [b1, e1)
+    // piece c0 + 1's; the key of every other slot becomes 0, which is below
+    // every score's key, so no later test sees it
     const uint32_t mul = 0xFFFFFFFFu / (uint32_t)cap + 1u;
     const int c0 = (int)__umulhi((uint32_t)s0, mul);
     const int j0 = s0 - c0 * cap;
     const int kept0 = c0 < P ? kept[c0] : 0, kept1 = c0 + 1 < P ? kept[c0 + 1] : 0;
+    const int e0 = min(max(kept0 - j0, 0), kMergeSlots);
+    const int b1 = min(cap - j0, kMergeSlots);
+    const int e1 = min(cap - j0 + kept1, kMergeSlots);
+    const uint32_t valid = ((1u << e0) - 1u) | (((1u << e1) - 1u) & ~((1u << b1) - 1u));
+#pragma unroll
+    for (int u = 0; u < kMergeSlots; ++u) x[u].x &= 0u - ((valid >> u) & 1u);
+    // B: entries above D into the value histogram over (D, largest kept]
     const float lo = key_value(max(dmax + 1u, gmin));
     const float inv = bin_scale(lo, key_value(gmax), kMergeBins);
-    uint32_t valid = 0u;
+    const float c = -lo * inv;
     int bn[kMergeSlots];
     int above = 0;
+    auto bin_of = [&](float f) { return min(kMergeBins - 1, max(0, (int)fmaf(f, inv, c))); };
+    if (dmax >= 0x80000000u) {          // every entry above D is a positive float: its value is key & 0x7fffffff
 #pragma unroll
-    for (int u = 0; u < kMergeSlots; ++u) {
-      const int j = j0 + u;
-      const bool ok = j < cap ? j < kept0 : j - cap < kept1;
-      valid |= ok ? 1u << u : 0u;
-      bn[u] = -1;
-      if (ok && x[u].x > dmax) {
-        bn[u] = vbin(key_value(x[u].x), lo, inv, kMergeBins);
-        ++above;
-        atomicAdd(&hist[bn[u]], 1u);
+      for (int u = 0; u < kMergeSlots; ++u) {
+        bn[u] = -1;
+        if (x[u].x > dmax) {
+          bn[u] = bin_of(__uint_as_float(x[u].x & 0x7fffffffu));
+          ++above;
+          atomicAdd(&hist[bn[u]], 1u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kMergeSlots; ++u) {
+        bn[u] = -1;
+        if (x[u].x > dmax) {
+          bn[u] = bin_of(key_value(x[u].x));
+          ++above;
+          atomicAdd(&hist[bn[u]], 1u);
+        }
       }
     }
     above = (int)wave_reduce((uint32_t)above, [](uint32_t p, uint32_t q) { return p + q; });
@@ -806,23 +831,21 @@ __global__ __launch_bounds__(kFT) void tk_merge_kernel(ChunkArgs a, int32_t* __r
         // F
         uint32_t gt = 0, eq = 0;
 #pragma unroll
-        for (int u = 0; u < kMergeSlots; ++u)
-          if ((valid >> u) & 1u) {
-            gt += x[u].x > v;
-            eq += x[u].x == v;
-          }
+        for (int u = 0; u < kMergeSlots; ++u) {
+          gt += x[u].x > v;
+          eq += x[u].x == v;
+        }
         const uint32_t ex = block_excl_scan1(gt | (eq << 16), wtot);
         int eq_rank = (int)(ex >> 16);
         int out = (int)(ex & 0xFFFFu) + min(eq_rank, need);
 #pragma unroll
-        for (int u = 0; u < kMergeSlots; ++u)
-          if ((valid >> u) & 1u) {
-            const uint32_t key = x[u].x;
-            if (key > v || (key == v && eq_rank++ < need)) {
-              if (out < a.k) dst[out] = (int)x[u].y;
-              ++out;
-            }
+        for (int u = 0; u < kMergeSlots; ++u) {
+          const uint32_t key = x[u].x;
+          if (key > v || (key == v && eq_rank++ < need)) {
+            if (out < a.k) dst[out] = (int)x[u].y;
+            ++out;
           }
+        }
         return;
       }
     }
