@@ -697,15 +697,15 @@ __global__ __launch_bounds__(kFT) void tk_merge_kernel(ChunkArgs a, int32_t* __r
   hist[tid] = 0u;
   if (tid == 0) sh_short = 0;
   if (tid < P) kept[tid] = (int)e.x;
-  {
+  const int n_rw = (P + kWave - 1) / kWave;     // waves holding records
+  if (wave < n_rw) {
     const uint32_t sum_w = wave_reduce(e.x, [](uint32_t p, uint32_t q) { return p + q; });
     const uint32_t dmax_w = wave_max(e.y), gmin_w = wave_min(e.z), gmax_w = wave_max(e.w);
     if (l == 0) wpart[wave] = make_uint4(sum_w, dmax_w, gmin_w, gmax_w);
   }
   __syncthreads();
   uint32_t m = 0, dmax = 0u, gmin = 0xFFFFFFFFu, gmax = 0u;
-#pragma unroll
-  for (int w = 0; w < kFT / kWave; ++w) {
+  for (int w = 0; w < n_rw; ++w) {
     const uint4 q = wpart[w];
     m += q.x;
     dmax = max(dmax, q.y);
