@@ -1,12 +1,12 @@
 """Row top-k over caller-provided fp32 scores (ix_topk_scores), on every
-select path: for few long rows the chunk-local keep + per-row merge (rows of
-up to 128 chunks of 8192 scores, with its whole-row fallback when a chunk
-dropped an entry that could rank among the k best, as on monotone ramps, or
-too few were kept) and the five-pass chunked select for longer rows (with its
-fallback when the k-th best sits in an over-full value bin); the
-single-workgroup select for many rows, unaligned row strides and rows short
-enough to keep every position.  Compared with the oracle's stable sort,
-element for element."""
+select path: for few long rows the wave-local keep over pieces of 1024
+positions + per-row merge (rows of up to 512 pieces, with its whole-row
+fallback when a piece dropped an entry that could rank among the k best, as
+on monotone ramps, or too few were kept) and the five-pass chunked select for
+longer rows (with its fallback when the k-th best sits in an over-full value
+bin); the single-workgroup select for many rows, unaligned row strides and
+rows short enough to keep every position.  Compared with the oracle's stable
+sort, element for element."""
 import numpy as np
 import pytest
 import torch
@@ -86,22 +86,46 @@ def test_chunked_monotone_ramps_fall_back(ix):
 
 
 def test_chunked_local_path_at_its_longest_rows(ix):
-    """128 chunks of 8192 (the longest rows of the local + merge passes):
-    each chunk keeps 64 entries."""
+    """512 pieces of 1024 (the longest rows of the keep + merge passes): each
+    piece keeps at most 16 entries."""
     g = torch.Generator(device="cuda").manual_seed(17)
-    L = 128 * 8192
+    L = 512 * 1024
     scores = torch.randn((2, 1, L), generator=g, device="cuda")
     _check(ix, scores, 2048, L - 1, L)
 
 
-def test_chunked_five_pass_path_past_1m(ix):
-    """Rows of more than 128 chunks use the range / histogram / select /
-    collect / finish passes."""
+def test_chunked_five_pass_path_past_512_pieces(ix):
+    """Rows of more than 512 pieces use the range / histogram / select /
+    collect / finish passes (one row just past the limit, one past 1M)."""
     g = torch.Generator(device="cuda").manual_seed(18)
-    L = 128 * 8192 + 5001
-    scores = torch.randn((2, 1, L), generator=g, device="cuda")
-    ties = torch.randint(-50, 50, (1, 1, L), generator=g, device="cuda").float()
-    _check(ix, torch.cat([scores, ties], dim=0), 2048, L - 1, L)
+    for L in (512 * 1024 + 1, 128 * 8192 + 5001):
+        scores = torch.randn((2, 1, L), generator=g, device="cuda")
+        ties = torch.randint(-50, 50, (1, 1, L), generator=g, device="cuda").float()
+        _check(ix, torch.cat([scores, ties], dim=0), 2048, L - 1, L)
+
+
+@pytest.mark.parametrize("L", [2049, 5000, 8192, 9000])
+def test_local_pieces_that_keep_everything(ix, L):
+    """Rows of at most 8 pieces give each piece at least 1024 slots, so a
+    full piece keeps all its scores (the row's k-th best is then found by the
+    merge alone); 9000 positions is the first row past that."""
+    g = torch.Generator(device="cuda").manual_seed(19)
+    scores = torch.randn((3, 1, L), generator=g, device="cuda")
+    _check(ix, scores, 2048, L - 1, L)
+
+
+def test_local_signed_zero_ties_through_the_merge(ix):
+    """Rare 2.0s, many zeros of both signs and negatives elsewhere: every
+    piece keeps its 2.0s and zeros, the row's k-th best is a zero, and the
+    merge keeps the earliest zeros of either sign (-0 and +0 rank equal)."""
+    g = torch.Generator(device="cuda").manual_seed(20)
+    L = 40_000
+    u = torch.rand((2, 1, L), generator=g, device="cuda")
+    s = torch.where(u < 0.001, torch.full_like(u, 2.0),
+                    torch.where(u < 0.05, torch.zeros_like(u),
+                                torch.where(u < 0.1, torch.full_like(u, -0.0), -1.0 - u)))
+    assert int((s == 2.0).sum()) < 2 * 256 and int((s == 0).sum()) > 2 * 256
+    _check(ix, s, 256, L - 1, L)
 
 
 def test_chunked_ragged_rows_with_short_prefix(ix):
