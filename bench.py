@@ -536,13 +536,15 @@ def run(args, pool):
                                             + (4 if w.key_dtype == "fp8" else 0)))
 
     # standalone row top-k over materialised fp32 rows at the decode shape
-    # (32 rows of 200,001 scores): HBM fraction on one read of the rows
+    # (32 rows of 200,001 scores): HBM fraction on one read of the rows.  A
+    # call is ~20 us of GPU work, so it is timed over 100 back-to-back calls
+    # (over a handful, the host's launch of each call shows in the figure)
     g = torch.Generator(device="cuda").manual_seed(0)
     dk = synth.DECODE_B32
     tk_scores = torch.randn((dk.batch, 1, dk.kv_len), generator=g, device="cuda")
     tk_idx = torch.empty((dk.batch, 1, dk.k), dtype=torch.int32, device="cuda")
     tk_ms = event_time(torch, lambda: ix.ix_topk_scores(tk_scores, tk_idx, q_start=dk.q_start, kv_len=dk.kv_len),
-                       max(args.kernel_reps, 10))
+                       max(args.kernel_reps, 100))
     tk_bytes = dk.batch * (4 * dk.kv_len + 4 * dk.k)
     del tk_scores
 
