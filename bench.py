@@ -8,13 +8,14 @@ arranged as two full+shared+shared+shared groups -- the indexer + streaming
 top-k on the 2 full layers and sparse attention on all 8.  Inputs are
 generated on the device before timing starts.  Prints one JSON line.
 
-    python bench.py --op indexer|argmax|attention|project [--fp8-queries] [--config ...] [--steps K] [--warmup W]
+    python bench.py --op indexer|argmax|attention|project|topk [--fp8-queries] [--config ...] [--steps K] [--warmup W]
 
 times one op of the workload's first layer alone (for profilers): the indexer
 with its streaming top-k, the same score stream with a running maximum
-instead of the top-k (ix_indexer_argmax), the sparse attention, or the
-indexer projection; --fp8-queries poses the indexer's queries as e4m3fn codes
-with a per-(row, head) scale.
+instead of the top-k (ix_indexer_argmax), the sparse attention, the
+indexer projection, or the row top-k alone over 32 rows of 200,001 fp32
+scores (ix_topk_scores); --fp8-queries poses the indexer's queries as e4m3fn
+codes with a per-(row, head) scale.
 
     python bench.py --write-traffic FETCH_DIR WRITE_DIR --traffic-op indexer|attention [--config ...]
 
@@ -436,8 +437,9 @@ def main(argv=None):
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
     ap.add_argument("--fp8-queries", action="store_true",
                     help="--op indexer/argmax: e4m3fn queries with a per-(row, head) scale")
-    ap.add_argument("--op", choices=["indexer", "argmax", "attention", "project"],
-                    help="time one op of the workload's first layer alone (warmup + steps launches), for profiling")
+    ap.add_argument("--op", choices=["indexer", "argmax", "attention", "project", "topk"],
+                    help="time one op of the workload's first layer alone (warmup + steps launches), for profiling; "
+                         "topk: ix_topk_scores on 32 rows x 200,001 fp32 scores, whatever the workload")
     args = ap.parse_args(argv)
     if args.write_traffic:
         write_traffic(args.traffic_op, CONFIGS[args.config], *args.write_traffic, args.traffic_command)
@@ -726,8 +728,9 @@ def project_leg(w, torch, synth, ix, reps):
 def bench_op(args, w, torch, synth, ix):
     """One op of the first layer, launched warmup + steps times: the indexer
     (+ fused top-k), the same score stream with a running maximum
-    (ix_indexer_argmax), or the sparse attention over the indexer's
-    positions."""
+    (ix_indexer_argmax), the sparse attention over the indexer's positions,
+    the indexer projection, or (topk) the standalone row top-k at the decode
+    shape."""
     dev = "cuda"
     if args.op == "project":
         x, wp = synth.projection_inputs(w, dev)
@@ -740,6 +743,21 @@ def bench_op(args, w, torch, synth, ix):
         ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
         print(json.dumps({"op": args.op, "workload": w.name, "launches": args.warmup + args.steps + 1,
                           "ms_per_launch": ms}), flush=True)
+        return 0
+    if args.op == "topk":
+        dk = synth.DECODE_B32
+        g = torch.Generator(device=dev).manual_seed(0)
+        scores = torch.randn((dk.batch, 1, dk.kv_len), generator=g, device=dev)
+        idx = torch.empty((dk.batch, 1, dk.k), dtype=torch.int32, device=dev)
+        fn = lambda: ix.ix_topk_scores(scores, idx, q_start=dk.q_start, kv_len=dk.kv_len)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = event_time(torch, fn, args.steps) if args.steps > 0 else None
+        print(json.dumps({"op": args.op, "workload": "32 rows x 200,001 fp32 scores, k=2048",
+                          "launches": args.warmup + args.steps + 1, "ms_per_launch": ms}), flush=True)
+        if args.copy_calibration:
+            copy_calibration(torch)
         return 0
     qs = None
     if args.fp8_queries:
