@@ -6,26 +6,27 @@
 // (score desc, position asc); emit them in ascending position order, then -1.
 //
 // Few long rows (decode: 32 rows of ~200K scores) cannot fill the chip with one
-// workgroup per row, so a row is cut into 8192-score chunks, each with its own
-// workgroup.  Rows of up to 128 chunks (about 1M scores) take two passes:
-//   L  local:  a chunk of a row with G chunks keeps at most cap = 8192 / G
-//              entries: a 1024-bin value histogram over the chunk's [min, max]
-//              gives the bin holding its (cap+1)-th best, and every entry in a
-//              higher bin is kept, in position order, at slots [g*cap, ...) of
-//              the row's candidate list.  The chunk records how many it kept
-//              and the largest order key it dropped;
-//   M  merge:  per row, the kept entries of all chunks (at most 8192, in
-//              position order) go to LDS and an exact radix select finds the
-//              k-th best v among them.  If v is above every dropped key, no
-//              dropped entry can rank among the k best, so the row's top k is
-//              the top k of the kept entries and a stable pass emits it.
-//              Otherwise (fewer than k kept, or a chunk dropped an entry at or
-//              above v: a ramp that puts the winners in one chunk, a flat row)
-//              the row is finished by a single-workgroup exact select over the
-//              whole row.
-// Random rows keep about 4x what each chunk contributes to the top k (k <=
-// 2048 of 8192 G slots), so the fallback is rare.  Longer rows run five
-// passes:
+// workgroup per row, so the work of a row is spread over many waves.  Rows of
+// up to 512 pieces of 1024 positions (524,288 scores) take two passes:
+//   K  keep:   one wave per piece (the score kernel's waves keep their own 640
+//              scores the same way, as their epilogue) keeps at most
+//              cap = 8192 / P of its scores, P the row's piece count: a
+//              256-bin value histogram in the wave's own LDS words gives the
+//              bin holding its (cap+1)-th best, and every score in a higher
+//              bin is kept, in position order, at slots [c*cap, ...) of the
+//              row's candidate list.  The piece records how many it kept, a
+//              bound D at or above every key it dropped, and its kept key
+//              range (topk_local.hpp);
+//   M  merge:  per row, one workgroup holds the whole candidate list in
+//              registers and selects the k best of the entries above the
+//              largest D; if at least k lie above it, no dropped score can
+//              rank among the k best, and a stable emission writes the row.
+//              Otherwise (a ramp that puts the winners in one piece, a flat
+//              row) the row is finished by a single-workgroup exact select
+//              over the whole row.
+// Random rows keep about 4x what each piece contributes to the top k (k <=
+// 2048 of 8192 slots), so the fallback is rare.  Longer rows run five passes
+// over chunks of 8192 scores, each with its own workgroup:
 //   R  range:   min / max of every chunk;
 //   H  hist:    a 1024-bin value-domain histogram of every chunk over the
 //               row's [min, max] (bins are monotone in the score);
