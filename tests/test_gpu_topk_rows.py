@@ -128,6 +128,18 @@ def test_local_signed_zero_ties_through_the_merge(ix):
     _check(ix, s, 256, L - 1, L)
 
 
+@pytest.mark.parametrize("k", [1, 7, 2047])
+def test_local_path_small_and_odd_k(ix, k):
+    """The keep + merge at k = 1 (the row's first maximum), a small odd k and
+    k = 2047, on normal rows and on integer rows where the k-th best is tied
+    many times over."""
+    g = torch.Generator(device="cuda").manual_seed(21 + k)
+    L = 100_003
+    normal = torch.randn((2, 1, L), generator=g, device="cuda")
+    ties = torch.randint(-40, 40, (2, 1, L), generator=g, device="cuda").float()
+    _check(ix, torch.cat([normal, ties], dim=0), k, L - 1, L)
+
+
 def test_chunked_ragged_rows_with_short_prefix(ix):
     """Rows 0.. of a prefill chunk: the first rows keep every position."""
     g = torch.Generator(device="cuda").manual_seed(15)
