@@ -28,14 +28,17 @@ def _rows(rng, n_rows, k, universe, sizes):
     return out
 
 
-def test_constructed_rows_with_known_overlap(ix):
+@pytest.mark.parametrize("k", [2048, 1, 3, 100, 1000, 1001, 2044])
+def test_constructed_rows_with_known_overlap(ix, k):
     """b shares a prescribed number of positions with a (the rest drawn from
-    outside a), with padded rows, empty rows and full rows."""
-    rng = np.random.default_rng(7)
-    B, n_q, k = 2, 150, 2048
+    outside a), with padded rows, empty rows and full rows; k = 2048, 2044
+    and 1000 take the kernel's 16-byte loads (2044 and 1000 with lanes past
+    the row's end), the others its 4-byte ones."""
+    rng = np.random.default_rng(7 + k)
+    B, n_q = 2, 150
     rows = B * n_q
     sizes = rng.integers(0, k + 1, size=rows)
-    sizes[:3] = [0, k, 1]
+    sizes[:3] = [0, k, min(1, k)]
     a = _rows(rng, rows, k, 100_000, sizes)
     b = np.full_like(a, -1)
     want = np.zeros(rows, dtype=np.int64)
